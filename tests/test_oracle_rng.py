@@ -1,0 +1,102 @@
+"""Pins of the oracle's counter-based generator (CPU only).
+
+The stochastic rounding draws r = fmix32(counter XOR key_k) * 2^-32 with key_k the low 32 bits
+of SplitMix64 output k+1 from the step seed.  Both generators are pinned to published
+known-answer values (tests/golden/rng_kat.json); the draw is then checked statistically.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "rng_kat.json")
+M32 = 0xFFFFFFFF
+
+
+def _rotl(x, r):
+    return ((x << r) | (x >> (32 - r))) & M32
+
+
+def _murmur3_x86_32(data: bytes, seed: int, fmix32) -> int:
+    """MurmurHash3_x86_32 body written here; only its finaliser comes from the oracle."""
+    c1, c2 = 0xCC9E2D51, 0x1B873593
+    h = seed
+    nb = len(data) // 4
+    for i in range(nb):
+        k = int.from_bytes(data[4 * i:4 * i + 4], "little")
+        k = _rotl((k * c1) & M32, 15) * c2 & M32
+        h = (_rotl(h ^ k, 13) * 5 + 0xE6546B64) & M32
+    tail = data[4 * nb:]
+    k = 0
+    if len(tail) >= 3:
+        k ^= tail[2] << 16
+    if len(tail) >= 2:
+        k ^= tail[1] << 8
+    if len(tail) >= 1:
+        k ^= tail[0]
+        h ^= _rotl((k * c1) & M32, 15) * c2 & M32
+    h ^= len(data)
+    return fmix32(h)
+
+
+def test_splitmix64_known_answers(orc):
+    kat = json.load(open(GOLDEN))["splitmix64"]
+    got = orc.splitmix64_outputs(kat["seed"], len(kat["outputs"]))
+    assert got == [int(v) for v in kat["outputs"]]
+
+
+def test_worker_key_is_splitmix_output(orc):
+    kat = json.load(open(GOLDEN))["splitmix64"]
+    for k, v in enumerate(kat["outputs"]):
+        assert orc.worker_key(kat["seed"], k) == int(v) & M32
+
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["murmur3_x86_32"])
+def test_fmix32_via_murmur3_known_answers(orc, case):
+    got = _murmur3_x86_32(case["data"].encode(), case["seed"], orc.fmix32)
+    assert got == int(case["hash"], 16)
+
+
+def test_uniform_is_exact_scaling(orc):
+    key = orc.worker_key(7, 3)
+    for c in (0, 1, 12345, M32):
+        assert orc.uniform(key, c) == orc.fmix32(c ^ key) / 2.0 ** 32
+
+
+def test_zero_draw_at_counter_equal_key(orc):
+    # fmix32(0) = 0, so the counter equal to the key draws r = 0 exactly
+    key = orc.worker_key(99, 0)
+    assert orc.uniform(key, key) == 0.0
+
+
+def test_hash_uniformity_chi_square(orc):
+    from scipy import stats
+    h = orc.hash_fill(orc.worker_key(1, 0), 0, 1 << 20)
+    counts = np.bincount(h >> 24, minlength=256)
+    chi2 = ((counts - counts.mean()) ** 2 / counts.mean()).sum()
+    assert stats.chi2.sf(chi2, 255) > 1e-4
+    # low byte too (the comparison uses all 32 bits)
+    counts = np.bincount(h & 0xFF, minlength=256)
+    chi2 = ((counts - counts.mean()) ** 2 / counts.mean()).sum()
+    assert stats.chi2.sf(chi2, 255) > 1e-4
+
+
+def test_hash_mean_variance_and_worker_independence(orc):
+    n = 1 << 20
+    r = [orc.hash_fill(orc.worker_key(5, k), 0, n) / 2.0 ** 32 for k in range(4)]
+    for x in r:
+        assert abs(x.mean() - 0.5) < 5 * np.sqrt(1 / 12 / n)
+        assert abs(x.var() - 1 / 12) < 5 * np.sqrt(1 / 180 / n)
+    for a in range(4):
+        for b in range(a + 1, 4):
+            c = np.corrcoef(r[a], r[b])[0, 1]
+            assert abs(c) < 5 / np.sqrt(n)
+    # consecutive counters of one worker are uncorrelated too
+    c = np.corrcoef(r[0][:-1], r[0][1:])[0, 1]
+    assert abs(c) < 5 / np.sqrt(n)
+
+
+def test_distinct_seeds_give_distinct_keys(orc):
+    keys = {orc.worker_key(s, k) for s in range(64) for k in range(16)}
+    assert len(keys) == 64 * 16
