@@ -1,0 +1,475 @@
+// gq_api.cpp -- host side of libgq.so: the C ABI declared in include/gq.h.
+//
+// Every call validates its arguments on the host first (nothing is enqueued on failure),
+// resolves the segment layout to a cached device tile table, derives the per-worker random
+// keys, and enqueues the kernels on the caller's stream.  No call synchronises except
+// gq_read_status and the rare scratch growth, which waits for the stream before freeing
+// the buffer it replaces.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "gq.h"
+#include "gq_internal.h"
+#include "gq_lq.h"
+
+#define GQ_EXPORT extern "C" __attribute__((visibility("default")))
+
+using gq::Tile;
+using gq::TileView;
+
+namespace {
+
+struct SegTable {
+  void *dev = nullptr;       // Tile[ntiles] followed by int64_t[nseg + 1]
+  std::vector<char> host;    // kept alive: the source of the stream-ordered upload
+  int64_t ntiles = 0;
+  int32_t nseg = 0;
+};
+
+}  // namespace
+
+struct gq_ctx {
+  int device = 0;
+  std::string err;
+  void *scratch = nullptr;
+  size_t scratch_bytes = 0;
+  unsigned *status = nullptr;       // device word: bit 0 = non-finite norm
+  unsigned *status_host = nullptr;  // pinned
+  std::map<std::vector<int64_t>, SegTable> segcache;
+  gq::LqState lq;
+};
+
+namespace {
+
+gq_status fail(gq_ctx *c, gq_status code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (c) c->err = buf;
+  return code;
+}
+
+gq_status hip_fail(gq_ctx *c, hipError_t e, const char *what) {
+  return fail(c, GQ_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): worker k's key is the low 32 bits of the
+// generator's output number k+1 when started from state `seed`.
+uint32_t worker_key(uint64_t seed, uint32_t worker) {
+  uint64_t state = seed;
+  uint64_t out = 0;
+  for (uint32_t i = 0; i <= worker; ++i) {
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    out = z ^ (z >> 31);
+  }
+  return static_cast<uint32_t>(out);
+}
+
+gq_status ensure_scratch(gq_ctx *c, size_t bytes, hipStream_t s) {
+  if (bytes <= c->scratch_bytes) return GQ_OK;
+  if (c->scratch) {
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+    (void)hipFree(c->scratch);
+    c->scratch = nullptr;
+    c->scratch_bytes = 0;
+  }
+  size_t want = bytes < (1u << 20) ? (1u << 20) : bytes + bytes / 4;
+  if (hipMalloc(&c->scratch, want) != hipSuccess) {
+    c->scratch = nullptr;
+    return fail(c, GQ_ENOMEM, "scratch allocation of %zu bytes failed", want);
+  }
+  c->scratch_bytes = want;
+  return GQ_OK;
+}
+
+// Validate the segment description and build the tile view (cached per layout).
+gq_status resolve_segments(gq_ctx *c, int64_t n, const int64_t *offsets, int32_t nseg,
+                           hipStream_t s, TileView *tv) {
+  if (n < 0) return fail(c, GQ_EINVAL, "n = %lld is negative", (long long)n);
+  if (nseg < 1) return fail(c, GQ_EINVAL, "nseg = %d must be >= 1", nseg);
+  tv->n = n;
+  tv->nseg = nseg;
+  if (offsets == nullptr) {
+    if (nseg != 1) return fail(c, GQ_EINVAL, "offsets = NULL needs nseg = 1");
+    tv->tiles = nullptr;
+    tv->seg_tile_start = nullptr;
+    tv->ntiles = (n + gq::kTile - 1) / gq::kTile;
+    return GQ_OK;
+  }
+  if (offsets[0] != 0) return fail(c, GQ_EINVAL, "offsets[0] = %lld, must be 0", (long long)offsets[0]);
+  if (offsets[nseg] != n)
+    return fail(c, GQ_EINVAL, "offsets[nseg] = %lld, must equal n = %lld",
+                (long long)offsets[nseg], (long long)n);
+  for (int32_t g = 0; g < nseg; ++g) {
+    if (offsets[g + 1] < offsets[g]) return fail(c, GQ_EINVAL, "offsets decrease at segment %d", g);
+    if (g > 0 && (offsets[g] % gq::kGroup) != 0)
+      return fail(c, GQ_EALIGN, "interior offset %d = %lld is not a multiple of 8", g,
+                  (long long)offsets[g]);
+  }
+  if (nseg == 1) {
+    tv->tiles = nullptr;
+    tv->seg_tile_start = nullptr;
+    tv->ntiles = (n + gq::kTile - 1) / gq::kTile;
+    return GQ_OK;
+  }
+  std::vector<int64_t> key(offsets, offsets + nseg + 1);
+  auto it = c->segcache.find(key);
+  if (it == c->segcache.end()) {
+    if (c->segcache.size() >= 64) {
+      hipError_t e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+      for (auto &kv : c->segcache) (void)hipFree(kv.second.dev);
+      c->segcache.clear();
+    }
+    SegTable t;
+    std::vector<Tile> tiles;
+    std::vector<int64_t> start(nseg + 1, 0);
+    for (int32_t g = 0; g < nseg; ++g) {
+      start[g] = (int64_t)tiles.size();
+      for (int64_t b = offsets[g]; b < offsets[g + 1]; b += gq::kTile) {
+        const int64_t rest = offsets[g + 1] - b;
+        tiles.push_back(Tile{b, (int32_t)(rest < gq::kTile ? rest : gq::kTile), g});
+      }
+    }
+    start[nseg] = (int64_t)tiles.size();
+    t.ntiles = (int64_t)tiles.size();
+    t.nseg = nseg;
+    const size_t tb = tiles.size() * sizeof(Tile), sb = start.size() * sizeof(int64_t);
+    t.host.resize(tb + sb);
+    if (tb) std::memcpy(t.host.data(), tiles.data(), tb);
+    std::memcpy(t.host.data() + tb, start.data(), sb);
+    if (hipMalloc(&t.dev, tb + sb) != hipSuccess)
+      return fail(c, GQ_ENOMEM, "segment table allocation failed");
+    hipError_t e = hipMemcpyAsync(t.dev, t.host.data(), tb + sb, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) {
+      (void)hipFree(t.dev);
+      return hip_fail(c, e, "segment table upload");
+    }
+    it = c->segcache.emplace(std::move(key), std::move(t)).first;
+  }
+  const SegTable &t = it->second;
+  tv->tiles = static_cast<const Tile *>(t.dev);
+  tv->seg_tile_start = reinterpret_cast<const int64_t *>(static_cast<const char *>(t.dev) +
+                                                         t.ntiles * sizeof(Tile));
+  tv->ntiles = t.ntiles;
+  return GQ_OK;
+}
+
+gq_status check_codec(gq_ctx *c, int32_t grid, int32_t levels, int32_t bits) {
+  if (grid != GQ_UNIFORM && grid != GQ_EXP) return fail(c, GQ_EINVAL, "grid = %d", grid);
+  if (bits != 4 && bits != 8) return fail(c, GQ_EINVAL, "bits = %d, must be 4 or 8", bits);
+  const int32_t maxlv = (1 << (bits - 1)) - 1;
+  if (levels < 1 || levels > maxlv)
+    return fail(c, GQ_EINVAL, "levels = %d outside [1, %d] for %d-bit codes", levels, maxlv, bits);
+  if (grid == GQ_EXP && levels > 30) return fail(c, GQ_EINVAL, "exponential levels = %d > 30", levels);
+  return GQ_OK;
+}
+
+int64_t max_lin(int32_t grid, int32_t levels) {
+  return grid == GQ_UNIFORM ? levels : (int64_t)1 << (levels - 1);
+}
+
+gq_status check_acc(gq_ctx *c, int32_t grid, int32_t levels, int32_t K, int32_t acc_bits) {
+  if (acc_bits != 16 && acc_bits != 32) return fail(c, GQ_EINVAL, "acc_bits = %d", acc_bits);
+  const int64_t lim = ((int64_t)1 << (acc_bits - 1)) - 1;
+  if ((int64_t)K * max_lin(grid, levels) > lim)
+    return fail(c, GQ_EOVERFLOW, "K * max level %lld = %lld does not fit int%d",
+                (long long)max_lin(grid, levels), (long long)K * max_lin(grid, levels), acc_bits);
+  return GQ_OK;
+}
+
+gq_status check_K(gq_ctx *c, int32_t K) {
+  if (K < 1 || K > gq::kMaxWorkers) return fail(c, GQ_EINVAL, "K = %d outside [1, 64]", K);
+  return GQ_OK;
+}
+
+gq_status check_dtype(gq_ctx *c, int32_t dt, const char *what) {
+  if (dt != GQ_F32 && dt != GQ_BF16) return fail(c, GQ_EINVAL, "%s = %d", what, dt);
+  return GQ_OK;
+}
+
+// Device buffers of an empty problem may be NULL (zero-size allocations have no address).
+gq_status check_ptr(gq_ctx *c, const void *p, const char *what, bool may_be_null = false) {
+  if (p == nullptr) return may_be_null ? GQ_OK : fail(c, GQ_EINVAL, "%s is NULL", what);
+  if (!aligned16(p)) return fail(c, GQ_EALIGN, "%s is not 16-byte aligned", what);
+  return GQ_OK;
+}
+
+gq_status check_counter(gq_ctx *c, int64_t n, uint32_t index_base) {
+  if ((uint64_t)n + index_base > ((uint64_t)1 << 32))
+    return fail(c, GQ_EINVAL, "n + index_base exceeds 2^32");
+  return GQ_OK;
+}
+
+double decode_denominator(int32_t grid, int32_t levels, int32_t K) {
+  return grid == GQ_UNIFORM ? (double)levels * (double)K : (double)K * std::ldexp(1.0, levels - 1);
+}
+
+#define TRY(x)                     \
+  do {                             \
+    gq_status st_ = (x);           \
+    if (st_ != GQ_OK) return st_;  \
+  } while (0)
+
+}  // namespace
+
+// ================================================================ ABI
+GQ_EXPORT const char *gq_version(void) { return "gq 0.1 (gfx950)"; }
+
+GQ_EXPORT gq_status gq_create(gq_ctx **out) {
+  if (!out) return GQ_EINVAL;
+  *out = nullptr;
+  gq_ctx *c = new (std::nothrow) gq_ctx();
+  if (!c) return GQ_ENOMEM;
+  if (hipGetDevice(&c->device) != hipSuccess || hipMalloc(&c->status, sizeof(unsigned)) != hipSuccess ||
+      hipHostMalloc(&c->status_host, sizeof(unsigned), hipHostMallocDefault) != hipSuccess ||
+      hipMemset(c->status, 0, sizeof(unsigned)) != hipSuccess) {
+    if (c->status) (void)hipFree(c->status);
+    if (c->status_host) (void)hipHostFree(c->status_host);
+    delete c;
+    return GQ_ENOMEM;
+  }
+  *out = c;
+  return GQ_OK;
+}
+
+GQ_EXPORT void gq_destroy(gq_ctx *c) {
+  if (!c) return;
+  (void)hipDeviceSynchronize();
+  if (c->scratch) (void)hipFree(c->scratch);
+  if (c->status) (void)hipFree(c->status);
+  if (c->status_host) (void)hipHostFree(c->status_host);
+  for (auto &kv : c->segcache) (void)hipFree(kv.second.dev);
+  gq::lq_release(c->lq);
+  delete c;
+}
+
+GQ_EXPORT const char *gq_last_error(const gq_ctx *c) { return c ? c->err.c_str() : "no context"; }
+
+GQ_EXPORT gq_status gq_read_status(gq_ctx *c, void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(c->status_host, c->status, sizeof(unsigned), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(c, e, "reading the status word");
+  const unsigned v = *c->status_host;
+  e = gq::launch_clear_u32(c->status, 1, s);
+  if (e != hipSuccess) return hip_fail(c, e, "clearing the status word");
+  if (v & 1u) return fail(c, GQ_ENONFINITE, "a global norm was not finite; its segment scale was set to 0");
+  return GQ_OK;
+}
+
+GQ_EXPORT gq_status gq_global_norm(gq_ctx *c, const void *const *grads, int32_t K, int32_t dtype,
+                                   int64_t n, const int64_t *offsets, int32_t nseg,
+                                   float *scale_out, double *norms_out, void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(check_K(c, K));
+  TRY(check_dtype(c, dtype, "dtype"));
+  if (!grads) return fail(c, GQ_EINVAL, "grads is NULL");
+  for (int k = 0; k < K; ++k) TRY(check_ptr(c, grads[k], "grads[k]", n == 0));
+  TRY(check_ptr(c, scale_out, "scale_out"));
+  if (norms_out) TRY(check_ptr(c, norms_out, "norms_out"));
+  TileView tv;
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  TRY(ensure_scratch(c, (size_t)K * (size_t)(tv.ntiles > 0 ? tv.ntiles : 1) * sizeof(double), s));
+  gq::NormArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int k = 0; k < K; ++k) a.grads[k] = grads[k];
+  a.partial = static_cast<double *>(c->scratch);
+  a.scale_out = scale_out;
+  a.norms_out = norms_out;
+  a.status = c->status;
+  a.tv = tv;
+  a.K = K;
+  hipError_t e = gq::launch_global_norm(a, dtype, s);
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "global norm launch");
+}
+
+GQ_EXPORT gq_status gq_quantize_pack(gq_ctx *c, const void *grad, int32_t dtype, int64_t n,
+                                     const int64_t *offsets, int32_t nseg, const float *scale,
+                                     int32_t grid, int32_t levels, int32_t bits, uint64_t seed,
+                                     uint32_t worker, uint32_t index_base, uint8_t *codes,
+                                     void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(check_dtype(c, dtype, "dtype"));
+  TRY(check_codec(c, grid, levels, bits));
+  TRY(check_ptr(c, grad, "grad", n == 0));
+  TRY(check_ptr(c, scale, "scale"));
+  TRY(check_ptr(c, codes, "codes", n == 0));
+  TRY(check_counter(c, n, index_base));
+  TileView tv;
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  gq::QuantArgs a;
+  a.grad = grad;
+  a.scale = scale;
+  a.codes = codes;
+  a.tv = tv;
+  a.levels = levels;
+  a.bits = bits;
+  a.key = worker_key(seed, worker);
+  a.index_base = index_base;
+  hipError_t e = gq::launch_quantize_pack(a, dtype, grid, s);
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "quantize launch");
+}
+
+GQ_EXPORT gq_status gq_accumulate_codes(gq_ctx *c, const uint8_t *const *codes, int32_t K, int64_t n,
+                                        int32_t grid, int32_t levels, int32_t bits,
+                                        int32_t acc_bits, void *sums, void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(check_K(c, K));
+  TRY(check_codec(c, grid, levels, bits));
+  TRY(check_acc(c, grid, levels, K, acc_bits));
+  if (n < 0) return fail(c, GQ_EINVAL, "n is negative");
+  if (!codes) return fail(c, GQ_EINVAL, "codes is NULL");
+  for (int k = 0; k < K; ++k) TRY(check_ptr(c, codes[k], "codes[k]", n == 0));
+  TRY(check_ptr(c, sums, "sums", n == 0));
+  gq::AccArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int k = 0; k < K; ++k) a.codes[k] = codes[k];
+  a.sums = sums;
+  a.n = n;
+  a.K = K;
+  a.bits = bits;
+  a.acc_bits = acc_bits;
+  hipError_t e = gq::launch_accumulate(a, grid, s);
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "accumulate launch");
+}
+
+GQ_EXPORT gq_status gq_dequantize(gq_ctx *c, const void *sums, int32_t acc_bits, int64_t n,
+                                  const int64_t *offsets, int32_t nseg, const float *scale,
+                                  int32_t grid, int32_t levels, int32_t K, int32_t out_dtype,
+                                  void *out, void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(check_K(c, K));
+  if (grid != GQ_UNIFORM && grid != GQ_EXP) return fail(c, GQ_EINVAL, "grid = %d", grid);
+  if (levels < 1 || levels > (grid == GQ_EXP ? 30 : 127))
+    return fail(c, GQ_EINVAL, "levels = %d", levels);
+  if (acc_bits != 16 && acc_bits != 32) return fail(c, GQ_EINVAL, "acc_bits = %d", acc_bits);
+  TRY(check_dtype(c, out_dtype, "out_dtype"));
+  TRY(check_ptr(c, sums, "sums", n == 0));
+  TRY(check_ptr(c, scale, "scale"));
+  TRY(check_ptr(c, out, "out", n == 0));
+  TileView tv;
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  gq::DequantArgs a;
+  a.sums = sums;
+  a.scale = scale;
+  a.out = out;
+  a.tv = tv;
+  a.acc_bits = acc_bits;
+  a.out_dtype = out_dtype;
+  a.denom = decode_denominator(grid, levels, K);
+  hipError_t e = gq::launch_dequantize(a, s);
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "dequantize launch");
+}
+
+GQ_EXPORT gq_status gq_fused_mean(gq_ctx *c, const void *const *grads, int32_t K, int32_t dtype,
+                                  int64_t n, const int64_t *offsets, int32_t nseg,
+                                  const float *scale, int32_t grid, int32_t levels, int32_t bits,
+                                  uint64_t seed, uint32_t index_base, int32_t acc_bits,
+                                  uint8_t *const *codes_or_null, void *sums_or_null,
+                                  int32_t out_dtype, void *out, void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(check_K(c, K));
+  TRY(check_dtype(c, dtype, "dtype"));
+  TRY(check_dtype(c, out_dtype, "out_dtype"));
+  TRY(check_codec(c, grid, levels, bits));
+  TRY(check_acc(c, grid, levels, K, acc_bits));
+  TRY(check_counter(c, n, index_base));
+  if (!grads) return fail(c, GQ_EINVAL, "grads is NULL");
+  for (int k = 0; k < K; ++k) TRY(check_ptr(c, grads[k], "grads[k]", n == 0));
+  if (codes_or_null)
+    for (int k = 0; k < K; ++k) TRY(check_ptr(c, codes_or_null[k], "codes[k]", n == 0));
+  if (sums_or_null) TRY(check_ptr(c, sums_or_null, "sums", n == 0));
+  TRY(check_ptr(c, scale, "scale"));
+  TRY(check_ptr(c, out, "out", n == 0));
+  TileView tv;
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  gq::FusedArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int k = 0; k < K; ++k) {
+    a.grads[k] = grads[k];
+    a.codes[k] = codes_or_null ? codes_or_null[k] : nullptr;
+    a.keys[k] = worker_key(seed, (uint32_t)k);
+  }
+  a.scale = scale;
+  a.sums = sums_or_null;
+  a.out = out;
+  a.tv = tv;
+  a.denom = decode_denominator(grid, levels, K);
+  a.K = K;
+  a.levels = levels;
+  a.bits = bits;
+  a.acc_bits = acc_bits;
+  a.out_dtype = out_dtype;
+  a.store_codes = codes_or_null ? 1 : 0;
+  a.index_base = index_base;
+  hipError_t e = gq::launch_fused(a, dtype, grid, s);
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "fused launch");
+}
+
+GQ_EXPORT gq_status gq_logquant(gq_ctx *c, const float *F, int64_t rows, int32_t r, double alpha,
+                                int32_t bits, int8_t *codes, float *colmax, float *F_hat_or_null,
+                                void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (rows < 0) return fail(c, GQ_EINVAL, "rows is negative");
+  if (r < 1 || r > gq::kLqMaxRank) return fail(c, GQ_EINVAL, "r = %d outside [1, %d]", r, gq::kLqMaxRank);
+  if (!(alpha > 0.0) || !std::isfinite(alpha)) return fail(c, GQ_EINVAL, "alpha must be positive and finite");
+  if (bits < 2 || bits > 8) return fail(c, GQ_EINVAL, "bits = %d outside [2, 8]", bits);
+  TRY(check_ptr(c, F, "F", rows == 0));
+  TRY(check_ptr(c, codes, "codes", rows == 0));
+  TRY(check_ptr(c, colmax, "colmax"));
+  if (F_hat_or_null) TRY(check_ptr(c, F_hat_or_null, "F_hat", rows == 0));
+  hipError_t e = gq::lq_logquant(c->lq, F, rows, r, alpha, bits, codes, colmax, F_hat_or_null, s);
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "logquant launch");
+}
+
+GQ_EXPORT gq_status gq_powersgd_logquant(gq_ctx *c, const float *G, float *E, float *Q, int64_t n,
+                                         int64_t m, int32_t r, double alpha, int32_t bits,
+                                         int8_t *p_codes, float *p_colmax, int8_t *q_codes,
+                                         float *q_colmax, float *p_hat_or_null,
+                                         float *p_pre_or_null, float *q_pre_or_null, void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n < 1 || m < 1) return fail(c, GQ_EINVAL, "n = %lld, m = %lld must be >= 1", (long long)n, (long long)m);
+  if (n > (1ll << 30) || m > (1ll << 30)) return fail(c, GQ_EINVAL, "n or m too large");
+  if (r < 1 || r > gq::kLqMaxRank) return fail(c, GQ_EINVAL, "r = %d outside [1, %d]", r, gq::kLqMaxRank);
+  if (!(alpha > 0.0) || !std::isfinite(alpha)) return fail(c, GQ_EINVAL, "alpha must be positive and finite");
+  if (bits < 2 || bits > 8) return fail(c, GQ_EINVAL, "bits = %d outside [2, 8]", bits);
+  TRY(check_ptr(c, G, "G"));
+  TRY(check_ptr(c, E, "E"));
+  TRY(check_ptr(c, Q, "Q"));
+  TRY(check_ptr(c, p_codes, "p_codes"));
+  TRY(check_ptr(c, p_colmax, "p_colmax"));
+  TRY(check_ptr(c, q_codes, "q_codes"));
+  TRY(check_ptr(c, q_colmax, "q_colmax"));
+  if (p_hat_or_null) TRY(check_ptr(c, p_hat_or_null, "p_hat"));
+  if (p_pre_or_null) TRY(check_ptr(c, p_pre_or_null, "p_pre"));
+  if (q_pre_or_null) TRY(check_ptr(c, q_pre_or_null, "q_pre"));
+  gq::LqStepArgs a{G, E, Q, n, m, r, alpha, bits, p_codes, p_colmax, q_codes, q_colmax,
+                   p_hat_or_null, p_pre_or_null, q_pre_or_null};
+  hipError_t e = gq::lq_step(c->lq, a, s);
+  if (e == hipErrorOutOfMemory) return fail(c, GQ_ENOMEM, "LQ scratch allocation failed");
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "powersgd_logquant launch");
+}

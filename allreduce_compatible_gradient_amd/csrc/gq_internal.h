@@ -1,0 +1,99 @@
+// gq_internal.h -- types shared by the host API (gq_api.cpp) and the gfx950 kernels (*.hip)
+// of libgq.so.  Nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gq {
+
+constexpr int kMaxWorkers = 64;
+constexpr int kGroup = 8;            // elements per thread step: one 32 B fp32 / 16 B bf16 load
+constexpr int kTile = 8192;          // elements per tile; a tile never crosses a segment
+constexpr int kBlock = 256;          // threads per block of the streaming kernels
+
+// One tile of a segmented buffer: elements [begin, begin + len) of segment `seg`.
+struct Tile {
+  int64_t begin;
+  int32_t len;
+  int32_t seg;
+};
+
+// How tiles map onto segments.  With tiles == nullptr there is one segment [0, n) cut into
+// kTile-element tiles; otherwise tiles[t] describes tile t and seg_tile_start[g] is the first
+// tile of segment g (nseg + 1 entries).
+struct TileView {
+  const Tile *tiles;
+  const int64_t *seg_tile_start;
+  int64_t ntiles;
+  int64_t n;
+  int32_t nseg;
+};
+
+struct NormArgs {
+  const void *grads[kMaxWorkers];
+  double *partial;        // K * ntiles
+  float *scale_out;       // nseg
+  double *norms_out;      // K * nseg or nullptr
+  unsigned *status;       // bit 0: a non-finite norm
+  TileView tv;
+  int32_t K;
+};
+
+struct QuantArgs {
+  const void *grad;
+  const float *scale;
+  uint8_t *codes;
+  TileView tv;
+  int32_t levels;
+  int32_t bits;
+  uint32_t key;
+  uint32_t index_base;
+};
+
+struct AccArgs {
+  const uint8_t *codes[kMaxWorkers];
+  void *sums;
+  int64_t n;
+  int32_t K;
+  int32_t bits;
+  int32_t acc_bits;
+};
+
+struct DequantArgs {
+  const void *sums;
+  const float *scale;
+  void *out;
+  TileView tv;
+  int32_t acc_bits;
+  int32_t out_dtype;
+  double denom;           // D: s*K (uniform) or K*2^(E-1) (exponential)
+};
+
+struct FusedArgs {
+  const void *grads[kMaxWorkers];
+  uint8_t *codes[kMaxWorkers];   // all nullptr unless codes are materialised
+  uint32_t keys[kMaxWorkers];
+  const float *scale;
+  void *sums;                    // nullptr unless sums are materialised
+  void *out;
+  TileView tv;
+  double denom;
+  int32_t K;
+  int32_t levels;
+  int32_t bits;
+  int32_t acc_bits;
+  int32_t out_dtype;
+  int32_t store_codes;
+  uint32_t index_base;
+};
+
+// Kernel launchers (gq_stream.hip).  Each returns the launch error, if any.
+hipError_t launch_global_norm(const NormArgs &a, int dtype, hipStream_t s);
+hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, hipStream_t s);
+hipError_t launch_accumulate(const AccArgs &a, int grid, hipStream_t s);
+hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
+hipError_t launch_fused(const FusedArgs &a, int dtype, int grid, hipStream_t s);
+hipError_t launch_clear_u32(unsigned *p, int count, hipStream_t s);
+
+}  // namespace gq

@@ -144,6 +144,33 @@ def get(name: str, n: Optional[int] = None) -> Workload:
     raise KeyError(name)
 
 
+def reduced(name: str) -> Workload:
+    """Oracle-sized variant of a workload: same distribution, segment structure and codec,
+    a few million elements per worker, a ragged end where the layout allows one."""
+    if name == "flat-1M-f32-K4-uniform31":
+        return get(name)
+    if name == "resnet50-161t-f32-K8-exp7":
+        full = get(name)
+        sizes = full.tensor_sizes[:60]
+        w = dataclasses.replace(full, name=name + "-first60", n=int(sum(sizes)),
+                                offsets=offsets_from_sizes(sizes), tensor_sizes=sizes)
+        return w
+    if name == "gpt2s-148t-bf16-K16-uniform7":
+        full = get(name)
+        tensors, total = [], 0
+        for s in full.tensor_sizes:          # reverse registration order
+            tensors.append(s)
+            total += s
+            if total >= 3_000_000:
+                break
+        buckets = ddp_buckets(tensors[::-1], 1 << 19)
+        return dataclasses.replace(full, name=name + "-tail3M", n=int(total),
+                                   offsets=offsets_from_sizes(buckets), tensor_sizes=tensors)
+    if name == "flat-1.3G-f32-K8-uniform127":
+        return get(name, n=(1 << 22) + 13)
+    raise KeyError(name)
+
+
 GLOBAL_QSGD_WORKLOADS = ("flat-1M-f32-K4-uniform31", "resnet50-161t-f32-K8-exp7",
                          "gpt2s-148t-bf16-K16-uniform7", "flat-1.3G-f32-K8-uniform127")
 LQ_SHAPES = ((4096, 4096), (4096, 11008))

@@ -453,6 +453,7 @@ void orc_powersgd_logquant(const float *G, float *E, float *Q, int64_t n, int64_
     float *Qn = (float *)malloc((size_t)(m * r) * sizeof(float));
     float *Ph = (float *)malloc((size_t)(n * r) * sizeof(float));
     float *Qh = (float *)malloc((size_t)(m * r) * sizeof(float));
+    double *Qacc = (double *)malloc((size_t)(m * r) * sizeof(double));
     int64_t i, j;
     int32_t c;
 
@@ -470,14 +471,16 @@ void orc_powersgd_logquant(const float *G, float *E, float *Q, int64_t n, int64_
         }
     orc_mgs(P, n, r);
 
-    /* Q = M^T P */
-    for (j = 0; j < m; ++j)
-        for (c = 0; c < r; ++c) {
-            double acc = 0.0;
-            for (i = 0; i < n; ++i)
-                acc += (double)E[i * m + j] * (double)P[i * r + c];
-            Qn[j * r + c] = (float)acc;
-        }
+    /* Q = M^T P: every Q[j][c] sums over i = 0..n-1 in order (rows outermost so that M is
+     * read along its rows) */
+    for (j = 0; j < m * r; ++j)
+        Qacc[j] = 0.0;
+    for (i = 0; i < n; ++i)
+        for (j = 0; j < m; ++j)
+            for (c = 0; c < r; ++c)
+                Qacc[j * r + c] += (double)E[i * m + j] * (double)P[i * r + c];
+    for (j = 0; j < m * r; ++j)
+        Qn[j] = (float)Qacc[j];
     if (P_pre)
         memcpy(P_pre, P, (size_t)(n * r) * sizeof(float));
     if (Q_pre)
@@ -501,4 +504,5 @@ void orc_powersgd_logquant(const float *G, float *E, float *Q, int64_t n, int64_
     free(Qn);
     free(Ph);
     free(Qh);
+    free(Qacc);
 }

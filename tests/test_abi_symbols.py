@@ -1,0 +1,67 @@
+"""The C-ABI library loads and exports every function include/gq.h declares (CPU only: no
+compute call is made without a GPU), and the oracle and the product share no code."""
+import ctypes
+import os
+import re
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gq.h")
+PKG = os.path.join(ROOT, "allreduce_compatible_gradient_amd")
+LIB = os.path.join(PKG, "libgq.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gq_[a-z_]+)\s*\(", text)))
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        from allreduce_compatible_gradient_amd import build
+        build.build()
+
+
+def test_header_declares_the_path():
+    names = _declared()
+    for want in ("gq_global_norm", "gq_quantize_pack", "gq_accumulate_codes", "gq_dequantize",
+                 "gq_fused_mean", "gq_logquant", "gq_powersgd_logquant", "gq_create",
+                 "gq_destroy", "gq_last_error", "gq_read_status", "gq_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    _ensure_built()
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_exports_nothing_else():
+    _ensure_built()
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = sorted({line.split()[-1] for line in out.splitlines()
+                       if line.split()[1:2] == ["T"] and line.split()[-1].startswith("gq_")})
+    assert exported == _declared()
+
+
+def test_version_string_is_callable_without_gpu():
+    _ensure_built()
+    lib = ctypes.CDLL(LIB)
+    lib.gq_version.restype = ctypes.c_char_p
+    assert lib.gq_version().decode().startswith("gq ")
+
+
+def test_oracle_and_product_share_no_code():
+    csrc = os.path.join(PKG, "csrc")
+    for f in os.listdir(csrc):
+        txt = open(os.path.join(csrc, f)).read()
+        assert "oracle" not in txt.lower(), f
+    for f in ("gq_oracle.c", "gq_oracle.h", "oracle.py"):
+        txt = open(os.path.join(ROOT, "oracle", f)).read()
+        assert "allreduce_compatible_gradient_amd" not in txt and "gq.h" not in txt, f
+    for f in os.listdir(PKG):
+        if f.endswith(".py"):
+            txt = open(os.path.join(PKG, f)).read()
+            assert "import oracle" not in txt and "from oracle" not in txt, f

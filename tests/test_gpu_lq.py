@@ -1,0 +1,159 @@
+"""GPU parity of the LQ-SGD step against the CPU oracle.
+
+The log quantiser alone (gq_logquant) must be bit-exact: same codes, column maxima and decoded
+values on the same input factor, including inputs on either side of every bin boundary.
+The full step compares within tolerance (the products and the orthonormalisation sum in a
+different order): relative Frobenius error <= 2e-3 on Phat, Qhat, Ghat = Phat Qhat^T and E;
+1e-5 on the unquantised factors.  Each step starts both sides from the oracle's state.
+"""
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+import torch
+
+from allreduce_compatible_gradient_amd import workloads as W
+from tests.gpu_helpers import dev, first_diff, gq, host, say
+
+pytestmark = pytest.mark.gpu
+getcontext().prec = 60
+ALPHA, BITS = W.LQ_ALPHA, W.LQ_BITS
+
+
+@pytest.fixture(scope="module")
+def orc():
+    from oracle import oracle
+    oracle.lib()
+    return oracle
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+@pytest.mark.parametrize("rows,r", [(1, 1), (37, 3), (4096, 7), (11008, 8), (5000, 1)])
+def test_logquant_bit_exact(orc, rows, r):
+    say("logquant", rows, r)
+    g = gq()
+    rng = np.random.default_rng(rows * 10 + r)
+    F = (rng.standard_normal((rows, r)) * 10.0 ** rng.uniform(-3, 3, r)).astype(np.float32)
+    if r > 1:
+        F[:, 1] = 0.0  # a zero column
+    for bits in (8, 4):
+        codes, cmax, Fh = orc.logquant(F, ALPHA, bits)
+        gc, gm, gh = g.logquant(dev(F), ALPHA, bits)
+        assert np.array_equal(host(gc), codes), first_diff(host(gc), codes)
+        assert np.array_equal(host(gm), cmax)
+        assert np.array_equal(host(gh), Fh), first_diff(host(gh), Fh)
+
+
+def test_logquant_at_bin_boundaries(orc):
+    """Values just below and just above every bin boundary (boundaries from 60-digit decimal
+    arithmetic) land in the same bins on both sides."""
+    g = gq()
+    L = 127
+    vals = [1.0]
+    a = Decimal(ALPHA)
+    for k in range(L):
+        b = ((1 + a) ** (Decimal(2 * k + 1) / Decimal(2 * L)) - 1) / a
+        f = np.float32(float(b))
+        while Decimal(float(f)) >= b:
+            f = np.nextafter(f, np.float32(-1))
+        vals += [f, np.nextafter(f, np.float32(2))]
+    F = np.array(vals, np.float32).reshape(-1, 1)
+    say("logquant boundaries", F.shape)
+    codes, cmax, Fh = orc.logquant(F, ALPHA, 8)
+    gc, gm, gh = g.logquant(dev(F), ALPHA, 8)
+    assert np.array_equal(host(gc), codes), first_diff(host(gc), codes)
+    assert np.array_equal(host(gh), Fh)
+    assert codes[1::2, 0].tolist() == list(range(L))
+    assert codes[2::2, 0].tolist() == list(range(1, L + 1))
+
+
+def _step_both(orc, G, E, Q):
+    g = gq()
+    ref = orc.powersgd_logquant(G, E, Q, ALPHA, BITS)
+    Ed, Qd = dev(E), dev(Q)
+    out = g.powersgd_logquant(dev(G), Ed, Qd, ALPHA, BITS, want_pre=True)
+    return ref, out, host(Ed), host(Qd)
+
+
+def _check_step(ref, out, E_gpu, Q_gpu, tol=2e-3):
+    P_pre = host(out["p_pre"])
+    Q_pre = host(out["q_pre"])
+    assert _rel(P_pre, ref["P_pre"]) < 1e-5
+    assert _rel(Q_pre, ref["Q_pre"]) < 1e-5
+    r = P_pre.shape[1]
+    assert np.abs(P_pre.T.astype(np.float64) @ P_pre - np.eye(r)).max() < 1e-5
+    ph = host(out["p_hat"])
+    assert _rel(ph, ref["p_hat"]) < tol
+    assert _rel(Q_gpu, ref["Q"]) < tol
+    Ghat = ph.astype(np.float64) @ Q_gpu.astype(np.float64).T
+    Gref = ref["p_hat"].astype(np.float64) @ ref["Q"].astype(np.float64).T
+    assert _rel(Ghat, Gref) < tol
+    assert _rel(E_gpu, ref["E"]) < tol
+    # column maxima to fp32 rounding of the unquantised factors
+    np.testing.assert_allclose(host(out["p_colmax"]), ref["p_colmax"], rtol=1e-5)
+    np.testing.assert_allclose(host(out["q_colmax"]), ref["q_colmax"], rtol=1e-5)
+    # codes: identical except for entries whose unquantised value sits within rounding of a
+    # bin boundary
+    for key in ("p_codes", "q_codes"):
+        gc = host(out[key]).astype(np.int32)
+        rc = ref[key].astype(np.int32)
+        assert np.abs(gc - rc).max() <= 1
+        assert np.mean(gc != rc) < 1e-3
+
+
+@pytest.mark.parametrize("n,m,r", [(300, 200, 1), (300, 200, 4), (257, 301, 7), (64, 40, 8),
+                                   (1000, 999, 3)])
+def test_step_small(orc, n, m, r):
+    say("lq step small", n, m, r)
+    rng = np.random.default_rng(n + m + r)
+    E = np.zeros((n, m), np.float32)
+    Q = rng.standard_normal((m, r)).astype(np.float32)
+    for t in range(3):
+        G = (rng.standard_normal((n, m)) * 1e-3
+             + np.outer(rng.standard_normal(n), rng.standard_normal(m)) * 1e-3).astype(np.float32)
+        ref, out, Eg, Qg = _step_both(orc, G, E, Q)
+        _check_step(ref, out, Eg, Qg)
+        E, Q = ref["E"], ref["Q"]
+
+
+def test_step_invariants_on_gpu():
+    """E_new + Phat Qhat^T = G + E_old to fp32 rounding; Q leaves as the decoded factor."""
+    g = gq()
+    say("lq invariants")
+    n, m, r = 512, 384, 4
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    G = torch.randn(n, m, device="cuda", generator=gen)
+    E = torch.randn(n, m, device="cuda", generator=gen) * 0.1
+    Q = torch.randn(m, r, device="cuda", generator=gen)
+    M = (G + E).double()
+    out = g.powersgd_logquant(G, E, Q, ALPHA, BITS, want_pre=True)
+    Ghat = out["p_hat"].double() @ Q.double().T
+    assert (E.double() + Ghat - M).abs().max().item() < 1e-6 * M.abs().max().item()
+    codes, cmax, qh = g.logquant(out["q_pre"], ALPHA, BITS)
+    assert torch.equal(qh, Q)
+    assert torch.equal(codes, out["q_codes"])
+    # payload: r(n+m) one-byte codes plus 2r fp32 maxima
+    assert out["p_codes"].numel() + out["q_codes"].numel() == r * (n + m)
+
+
+@pytest.mark.parametrize("shape", W.LQ_SHAPES)
+@pytest.mark.parametrize("r", W.LQ_RANKS)
+def test_step_full_shapes(orc, shape, r):
+    """The LQ-SGD workload: noise (std 1e-3) + rank-8 signal, error feedback over 3 steps with
+    a fresh gradient per step; each step starts both sides from the oracle's state."""
+    n, m = shape
+    say("lq step full", n, m, r)
+    E = np.zeros((n, m), np.float32)
+    Q = None
+    for t in range(3):
+        Gt, Q0 = W.lq_problem(n, m, r, t, "cpu")
+        if Q is None:
+            Q = Q0.numpy()
+        ref, out, Eg, Qg = _step_both(orc, Gt.numpy(), E, Q)
+        _check_step(ref, out, Eg, Qg)
+        E, Q = ref["E"], ref["Q"]
