@@ -1,0 +1,295 @@
+"""Benchmark of the allreduce-compatible quantisation hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-rows]
+
+One step = the whole Global-QSGD path over one batch of K worker gradients resident in HBM:
+the shared global norm (gq_global_norm) and the fused quantise -> pack -> integer sum ->
+decode pass (gq_fused_mean), on the 1.3e9-element fp32 bucket with K = 8 workers (uniform
+grid s = 127, int16 sums, fp32 mean).  ``value`` is gradient bytes quantised and aggregated
+per second (K * n * 4 bytes per step).  ``roofline`` reports the dominant kernel (the fused
+pass) against the 8 TB/s HBM peak with its algorithmic bytes (K*n*4 in + n*4 out) and its
+average duration from HIP events recorded on the launch stream.  ``rows`` times each step of
+the path on its own (and the exponential-grid, bf16 and LQ-SGD workloads) for the same
+roofline.  ``cpu_baseline`` times the plain CPU oracle on the first 2^26 elements of every
+worker of the same data.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "flat-1.3G-f32-K8-uniform127"
+METRIC = "gradient GB/s quantized+aggregated over K workers; % of HBM roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_mean_flat-1.3G-f32-K8.traffic.json")
+STREAM_SRC = os.path.join(ROOT, "allreduce_compatible_gradient_amd", "csrc", "gq_stream.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(STREAM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(algo_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
+    the kernel source as it is now; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every gq call launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def time_calls(torch, fn, iters, warmup=1):
+    for _ in range(warmup):
+        fn()
+    t = Timer(torch)
+    for _ in range(iters):
+        e = t.start()
+        fn()
+        t.stop(e)
+    return t.mean_ms()
+
+
+def rows_breakdown(torch, gq, W, grads, S, w, args):
+    """Each step of the path timed on its own, with its algorithmic bytes."""
+    rows = {}
+    n, K = w.n, w.K
+    it = 3
+
+    def row(name, ms, nbytes, note):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rows[name] = {"ms": round(ms, 4), "algo_bytes": int(nbytes), "GBps": round(gbs, 1),
+                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "what": note}
+        log("row %-28s %9.3f ms %8.1f GB/s (%.1f%% of HBM)" % (name, ms, gbs,
+                                                                100 * gbs / HBM_PEAK_GBS))
+
+    # per-worker quantise + pack, accumulate, dequantize, parity-mode fused on the same bucket
+    codes = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(K)]
+    ms = time_calls(torch, lambda: gq.quantize_pack(grads[0], S, w.grid, w.levels, w.bits, 1, 0,
+                                                    codes=codes[0]), it)
+    row("quantize_pack_1.3G_s127_int8", ms, n * 4 + n, "one worker: fp32 in, int8 codes out")
+    for k in range(1, K):
+        gq.quantize_pack(grads[k], S, w.grid, w.levels, w.bits, 1, k, codes=codes[k])
+    sums = torch.empty(n, dtype=torch.int16, device="cuda")
+    ms = time_calls(torch, lambda: gq.accumulate_codes(codes, n, w.grid, w.levels, w.bits, 16,
+                                                       sums=sums), it)
+    row("accumulate_K8_int8_to_int16", ms, K * n + 2 * n, "K int8 code streams in, int16 out")
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    ms = time_calls(torch, lambda: gq.dequantize(sums, S, w.grid, w.levels, K, 0, out=out), it)
+    row("dequantize_int16_to_f32", ms, 2 * n + 4 * n, "int16 sums in, fp32 mean out")
+    ms = time_calls(torch, lambda: gq.fused_mean(grads, S, w.grid, w.levels, w.bits, 1, 16, 0,
+                                                 codes=codes, sums=sums, out=out), it)
+    row("fused_parity_mode_codes_sums", ms, K * n * 4 + 4 * n + K * n + 2 * n,
+        "fused pass that also writes every worker's codes and the int16 sums")
+    del codes, sums, out
+    torch.cuda.empty_cache()
+
+    # exponential grid, 161 ResNet-50 segments
+    w2 = W.get("resnet50-161t-f32-K8-exp7")
+    g2 = W.gradients(w2, "cuda")
+    S2, _ = gq.global_norm(g2, w2.offsets)
+    o2 = torch.empty(w2.n, dtype=torch.float32, device="cuda")
+    c2 = torch.empty((w2.n + 1) // 2, dtype=torch.uint8, device="cuda")
+    ms = time_calls(torch, lambda: gq.global_norm(g2, w2.offsets, scale_out=S2), 5)
+    row("norm_resnet50_161seg_K8", ms, w2.K * w2.n * 4, "K fp32 buffers in")
+    ms = time_calls(torch, lambda: gq.quantize_pack(g2[0], S2, w2.grid, w2.levels, w2.bits, 1, 0,
+                                                    offsets=w2.offsets, codes=c2), 5)
+    row("quantize_pack_resnet50_exp7_int4", ms, w2.n * 4 + (w2.n + 1) // 2,
+        "one worker, exponential grid, 4-bit codes")
+    ms = time_calls(torch, lambda: gq.fused_mean(g2, S2, w2.grid, w2.levels, w2.bits, 1, 16, 0,
+                                                 offsets=w2.offsets, out=o2), 5)
+    row("fused_resnet50_exp7_K8", ms, w2.K * w2.n * 4 + w2.n * 4, "fused pass, 161 segments")
+    del g2, o2, c2
+    torch.cuda.empty_cache()
+
+    # bf16, 9 GPT-2 buckets, K = 16
+    w3 = W.get("gpt2s-148t-bf16-K16-uniform7")
+    g3 = W.gradients(w3, "cuda")
+    S3, _ = gq.global_norm(g3, w3.offsets)
+    o3 = torch.empty(w3.n, dtype=torch.bfloat16, device="cuda")
+    ms = time_calls(torch, lambda: gq.global_norm(g3, w3.offsets, scale_out=S3), 3)
+    row("norm_gpt2_bf16_K16", ms, w3.K * w3.n * 2, "K bf16 buffers in")
+    ms = time_calls(torch, lambda: gq.fused_mean(g3, S3, w3.grid, w3.levels, w3.bits, 1, 16, 1,
+                                                 offsets=w3.offsets, out=o3), 3)
+    row("fused_gpt2_bf16_s7_K16", ms, w3.K * w3.n * 2 + w3.n * 2, "fused pass, bf16 in and out")
+    del g3, o3
+    torch.cuda.empty_cache()
+
+    # LQ-SGD step on the largest shape
+    for (n5, m5) in W.LQ_SHAPES:
+        for r5 in (1, 7):
+            G, Q0 = W.lq_problem(n5, m5, r5, 0, "cuda")
+            E = torch.zeros_like(G)
+            Q = Q0.clone()
+            o5 = {}
+            ms = time_calls(torch, lambda: gq.powersgd_logquant(G, E, Q, W.LQ_ALPHA, W.LQ_BITS,
+                                                                out=o5), 5)
+            row("lq_step_%dx%d_r%d" % (n5, m5, r5), ms, 6 * n5 * m5 * 4,
+                "G read, E read+write, E read, E read+write")
+            del G, E, Q
+    torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_baseline(grads, w, sample):
+    """The oracle, as it stands (one thread), on the first `sample` elements of each worker."""
+    import numpy as np
+    from oracle import oracle as orc
+    xs = [g[:sample].cpu().numpy() for g in grads]
+    t0 = time.perf_counter()
+    res = orc.allreduce_mean(xs, w.grid, w.levels, w.bits, w.acc_bits, 1)
+    dt = time.perf_counter() - t0
+    assert res["mean"].size == sample
+    gbs = w.K * sample * 4 / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": "first %d elements of each of the %d workers of %s (%.2f GB of gradient): "
+                      "global norm, quantise, pack, integer sum and decode, single thread"
+                      % (sample, w.K, w.name, w.K * sample * 4 / 1e9)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 26)
+    ap.add_argument("--profile-once", action="store_true",
+                    help="for rocprofv3 counter runs: one 1 GiB torch copy (a plain copy kernel of "
+                         "known size, to calibrate FETCH_SIZE/WRITE_SIZE) then one step, no JSON")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the K data-parallel workers are simulated as K buffers "
+              "on it, and runs on more than one GPU are not part of this build (asked for %d)"
+              % max(args.gpus, int(os.environ.get("WORLD_SIZE", "1"))), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from allreduce_compatible_gradient_amd import build as B
+    if not os.path.exists(B.LIB):
+        B.build()
+    from allreduce_compatible_gradient_amd import gq
+    from allreduce_compatible_gradient_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    w = W.get(WORKLOAD)
+    log("generating %s: K=%d n=%d (%.1f GB) on the GPU" % (w.name, w.K, w.n, w.grad_bytes() / 1e9))
+    grads = W.gradients(w, "cuda")
+    S = torch.empty(1, dtype=torch.float32, device="cuda")
+    out = torch.empty(w.n, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        gq.global_norm(grads, scale_out=S)
+        gq.fused_mean(grads, S, w.grid, w.levels, w.bits, 1, w.acc_bits, 0, out=out)
+
+    if args.profile_once:
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        step()
+        torch.cuda.synchronize()
+        log("profile-once done: copy of %d bytes, then global_norm + fused_mean" % (4 << 28))
+        return
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    norm_t, fused_t = Timer(torch), Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e0 = norm_t.start()
+        gq.global_norm(grads, scale_out=S)
+        norm_t.stop(e0)
+        e1 = fused_t.start()
+        gq.fused_mean(grads, S, w.grid, w.levels, w.bits, 1, w.acc_bits, 0, out=out)
+        fused_t.stop(e1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    grad_bytes = w.grad_bytes()
+    value = grad_bytes / (wall / args.steps) / 1e9
+    norm_ms, fused_ms = norm_t.mean_ms(), fused_t.mean_ms()
+    fused_bytes = grad_bytes + w.n * 4
+    step_min_bytes = 2 * grad_bytes + w.n * 4
+    achieved = fused_bytes / (fused_ms * 1e-3) / 1e9
+    log("step %.3f ms: norm %.3f ms (%.0f GB/s), fused %.3f ms (%.0f GB/s = %.1f%% of HBM)"
+        % (ms_step, norm_ms, grad_bytes / norm_ms / 1e6, fused_ms, achieved,
+           100 * achieved / HBM_PEAK_GBS))
+    roof_step_ms = step_min_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "K": w.K, "n_per_worker": w.n, "grid": "uniform",
+                   "levels": w.levels, "code_bits": w.bits, "acc_bits": w.acc_bits,
+                   "step": "global norm + fused quantise/pack/sum/decode"},
+        "hbm_roofline_frac": round(roof_step_ms / ms_step, 4),
+        "roofline": {"bound": "hbm", "kernel": "k_fused<K=8,f32,uniform>",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(fused_bytes),
+                     "algo_bytes_per_launch": fused_bytes, "avg_launch_ms": round(fused_ms, 4)},
+        "kernels": {"global_norm_ms": round(norm_ms, 4), "fused_mean_ms": round(fused_ms, 4),
+                    "global_norm_GBps": round(grad_bytes / norm_ms / 1e6, 1)},
+    }
+    if not args.no_rows:
+        result["rows"] = rows_breakdown(torch, gq, W, grads, S, w, args)
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on %d elements per worker" % args.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline(grads, w, args.cpu_sample)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
