@@ -42,7 +42,7 @@ struct gq_ctx {
   size_t scratch_bytes = 0;
   unsigned *status = nullptr;       // device word: bit 0 = non-finite norm
   unsigned *status_host = nullptr;  // pinned
-  std::map<std::vector<int64_t>, SegTable> segcache;
+  std::map<std::pair<std::vector<int64_t>, int>, SegTable> segcache;  // (offsets, tile size)
   gq::LqState lq;
 };
 
@@ -79,6 +79,10 @@ uint32_t worker_key(uint64_t seed, uint32_t worker) {
   return static_cast<uint32_t>(out);
 }
 
+// The key's share of the first step of MurmurHash3's fmix32 (h ^= h >> 16 distributes over
+// the XOR of counter and key), so the kernels mix the counter once for all workers.
+uint32_t key_mix(uint32_t key) { return key ^ (key >> 16); }
+
 gq_status ensure_scratch(gq_ctx *c, size_t bytes, hipStream_t s) {
   if (bytes <= c->scratch_bytes) return GQ_OK;
   if (c->scratch) {
@@ -99,7 +103,7 @@ gq_status ensure_scratch(gq_ctx *c, size_t bytes, hipStream_t s) {
 
 // Validate the segment description and build the tile view (cached per layout).
 gq_status resolve_segments(gq_ctx *c, int64_t n, const int64_t *offsets, int32_t nseg,
-                           hipStream_t s, TileView *tv) {
+                           hipStream_t s, TileView *tv, int tile = gq::kTile) {
   if (n < 0) return fail(c, GQ_EINVAL, "n = %lld is negative", (long long)n);
   if (nseg < 1) return fail(c, GQ_EINVAL, "nseg = %d must be >= 1", nseg);
   tv->n = n;
@@ -108,7 +112,7 @@ gq_status resolve_segments(gq_ctx *c, int64_t n, const int64_t *offsets, int32_t
     if (nseg != 1) return fail(c, GQ_EINVAL, "offsets = NULL needs nseg = 1");
     tv->tiles = nullptr;
     tv->seg_tile_start = nullptr;
-    tv->ntiles = (n + gq::kTile - 1) / gq::kTile;
+    tv->ntiles = (n + tile - 1) / tile;
     return GQ_OK;
   }
   if (offsets[0] != 0) return fail(c, GQ_EINVAL, "offsets[0] = %lld, must be 0", (long long)offsets[0]);
@@ -124,10 +128,10 @@ gq_status resolve_segments(gq_ctx *c, int64_t n, const int64_t *offsets, int32_t
   if (nseg == 1) {
     tv->tiles = nullptr;
     tv->seg_tile_start = nullptr;
-    tv->ntiles = (n + gq::kTile - 1) / gq::kTile;
+    tv->ntiles = (n + tile - 1) / tile;
     return GQ_OK;
   }
-  std::vector<int64_t> key(offsets, offsets + nseg + 1);
+  auto key = std::make_pair(std::vector<int64_t>(offsets, offsets + nseg + 1), tile);
   auto it = c->segcache.find(key);
   if (it == c->segcache.end()) {
     if (c->segcache.size() >= 64) {
@@ -141,9 +145,9 @@ gq_status resolve_segments(gq_ctx *c, int64_t n, const int64_t *offsets, int32_t
     std::vector<int64_t> start(nseg + 1, 0);
     for (int32_t g = 0; g < nseg; ++g) {
       start[g] = (int64_t)tiles.size();
-      for (int64_t b = offsets[g]; b < offsets[g + 1]; b += gq::kTile) {
+      for (int64_t b = offsets[g]; b < offsets[g + 1]; b += tile) {
         const int64_t rest = offsets[g + 1] - b;
-        tiles.push_back(Tile{b, (int32_t)(rest < gq::kTile ? rest : gq::kTile), g});
+        tiles.push_back(Tile{b, (int32_t)(rest < tile ? rest : tile), g});
       }
     }
     start[nseg] = (int64_t)tiles.size();
@@ -286,12 +290,14 @@ GQ_EXPORT gq_status gq_global_norm(gq_ctx *c, const void *const *grads, int32_t 
   TRY(check_ptr(c, scale_out, "scale_out"));
   if (norms_out) TRY(check_ptr(c, norms_out, "norms_out"));
   TileView tv;
-  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
-  TRY(ensure_scratch(c, (size_t)K * (size_t)(tv.ntiles > 0 ? tv.ntiles : 1) * sizeof(double), s));
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, gq::kNormTile));
+  const size_t npart = (size_t)K * (size_t)tv.ntiles;
+  TRY(ensure_scratch(c, (npart + (size_t)K * nseg) * sizeof(double), s));
   gq::NormArgs a;
   std::memset(&a, 0, sizeof a);
   for (int k = 0; k < K; ++k) a.grads[k] = grads[k];
   a.partial = static_cast<double *>(c->scratch);
+  a.norms = a.partial + npart;
   a.scale_out = scale_out;
   a.norms_out = norms_out;
   a.status = c->status;
@@ -323,7 +329,7 @@ GQ_EXPORT gq_status gq_quantize_pack(gq_ctx *c, const void *grad, int32_t dtype,
   a.tv = tv;
   a.levels = levels;
   a.bits = bits;
-  a.key = worker_key(seed, worker);
+  a.key_mix = key_mix(worker_key(seed, worker));
   a.index_base = index_base;
   hipError_t e = gq::launch_quantize_pack(a, dtype, grid, s);
   return e == hipSuccess ? GQ_OK : hip_fail(c, e, "quantize launch");
@@ -410,7 +416,7 @@ GQ_EXPORT gq_status gq_fused_mean(gq_ctx *c, const void *const *grads, int32_t K
   for (int k = 0; k < K; ++k) {
     a.grads[k] = grads[k];
     a.codes[k] = codes_or_null ? codes_or_null[k] : nullptr;
-    a.keys[k] = worker_key(seed, (uint32_t)k);
+    a.key_mix[k] = key_mix(worker_key(seed, (uint32_t)k));
   }
   a.scale = scale;
   a.sums = sums_or_null;

@@ -10,7 +10,10 @@ namespace gq {
 constexpr int kMaxWorkers = 64;
 constexpr int kGroup = 8;            // elements per thread step: one 32 B fp32 / 16 B bf16 load
 constexpr int kTile = 8192;          // elements per tile; a tile never crosses a segment
+constexpr int kNormTile = 65536;     // elements per tile of the norm pass (one fp64 partial each)
 constexpr int kBlock = 256;          // threads per block of the streaming kernels
+constexpr int kStreamGrid = 4096;    // resident blocks of the element-wise streaming kernels
+constexpr int kNormGrid = 2048;      // blocks per worker of the norm pass
 
 // One tile of a segmented buffer: elements [begin, begin + len) of segment `seg`.
 struct Tile {
@@ -33,6 +36,7 @@ struct TileView {
 struct NormArgs {
   const void *grads[kMaxWorkers];
   double *partial;        // K * ntiles
+  double *norms;          // K * nseg (scratch)
   float *scale_out;       // nseg
   double *norms_out;      // K * nseg or nullptr
   unsigned *status;       // bit 0: a non-finite norm
@@ -47,7 +51,7 @@ struct QuantArgs {
   TileView tv;
   int32_t levels;
   int32_t bits;
-  uint32_t key;
+  uint32_t key_mix;       // key ^ (key >> 16): the key's share of fmix32's first step
   uint32_t index_base;
 };
 
@@ -73,7 +77,7 @@ struct DequantArgs {
 struct FusedArgs {
   const void *grads[kMaxWorkers];
   uint8_t *codes[kMaxWorkers];   // all nullptr unless codes are materialised
-  uint32_t keys[kMaxWorkers];
+  uint32_t key_mix[kMaxWorkers];  // key ^ (key >> 16) per worker
   const float *scale;
   void *sums;                    // nullptr unless sums are materialised
   void *out;

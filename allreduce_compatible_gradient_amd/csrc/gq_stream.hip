@@ -6,20 +6,23 @@
 // summed (Allreduce); the mean is decoded once.  Uniform grid: QSGD family ("Unbiased
 // Single-scale and Multi-scale Quantizers", abstract).  Exponential grid: "NUQSGD", abstract.
 //
-// Design for CDNA4: every kernel is an HBM stream.  A thread owns groups of 8 consecutive
-// elements (one 32 B fp32 or 16 B bf16 load, issued non-temporal so the 256 MB Infinity Cache
-// is not polluted by data that is never re-read); a 256-thread block walks 8192-element tiles
-// with a grid-stride loop, so 2048 resident blocks cover all 256 CUs whatever the size.  Tiles
-// never cross segments, so the per-segment scale is one scalar load per tile.  Codes are
-// packed in registers (8 int8 -> one 8 B store, 8 nibbles -> one 4 B store).  No MFMA: there
-// is no contraction on this path.  Reductions are fixed-order (no float atomics), so results
-// are bit-stable from run to run.
+// Design for CDNA4.  Every kernel is an HBM stream, so the design is about how a wave touches
+// memory.  A wave walks 512-element chunks; lane L owns NP "parts" of P consecutive elements,
+// part j at chunk offset j*64*P + L*P, so every load and store instruction of the wave covers
+// one contiguous block (1 KB of fp32, 256 B of int8 codes, ...): whole cache lines, never the
+// half-line writes a 32-byte-per-lane layout produces.  Gradient loads are non-temporal (they
+// are read once; keeping them out of the 256 MB Infinity Cache lets a pure read stream run at
+// ~7 TB/s on MI355X).  A 256-thread block walks tiles with a grid-stride loop, so a fixed grid
+// covers all 256 CUs whatever the size; tiles never cross segments, so the per-segment scale
+// is one scalar load per tile.  Codes are packed in registers.  No MFMA: there is no
+// contraction here.  Reductions are fixed-order (no float atomics): results are bit-stable.
 //
 // Arithmetic contract (each step is one IEEE operation, so any conforming implementation of
 // the same definition gets the same bits; compiled with -ffp-contract=off and IEEE fp32
-// denormals): u = |x| * inv is one fp32 multiply; floor, fraction and the scaling of
-// the fraction by 2^32 are exact; the draw r = h * 2^-32 satisfies r < p exactly when
-// h < ceil(p * 2^32), which is the integer comparison used here.
+// denormals): u = |x| * inv is one fp32 multiply; floor, fraction and the scaling of the
+// fraction by 2^32 are exact; the draw r = h * 2^-32 satisfies r < p exactly when
+// h < ceil(p * 2^32), which is the integer comparison used here.  Uniform sums are carried
+// in fp32, which is exact because |sum| <= 64 * 127 < 2^24.
 #include <float.h>
 #include <math.h>
 
@@ -32,11 +35,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kMaxGrid = 2048;
+constexpr int kChunk = 512;  // elements per wave iteration
 
-// MurmurHash3's 32-bit finaliser (Appleby, public domain).
-__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
-  h ^= h >> 16;
+// ---------------------------------------------------------------- random numbers
+// MurmurHash3's 32-bit finaliser (Appleby, public domain) applied to (counter XOR key).  Its
+// first step h ^= h >> 16 distributes over XOR, so it is split: mix16(counter) once per element
+// (shared by all workers) and mix16(key) once per worker, on the host.
+__device__ __forceinline__ uint32_t mix16(uint32_t v) { return v ^ (v >> 16); }
+
+__device__ __forceinline__ uint32_t fmix32_tail(uint32_t h) {
   h *= 0x85EBCA6Bu;
   h ^= h >> 13;
   h *= 0xC2B2AE35u;
@@ -44,12 +51,13 @@ __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
   return h;
 }
 
-__device__ __forceinline__ void tile_of(const TileView &tv, int64_t t, int64_t &begin,
-                                        int &len, int &seg) {
+// ---------------------------------------------------------------- tiles and lane map
+__device__ __forceinline__ void tile_of(const TileView &tv, int64_t t, int tile_elems,
+                                        int64_t &begin, int &len, int &seg) {
   if (tv.tiles == nullptr) {
-    begin = t * kTile;
+    begin = t * tile_elems;
     const int64_t rest = tv.n - begin;
-    len = rest < kTile ? (int)rest : kTile;
+    len = rest < tile_elems ? (int)rest : tile_elems;
     seg = 0;
   } else {
     const Tile tl = tv.tiles[t];
@@ -64,8 +72,200 @@ __device__ __forceinline__ int64_t seg_first_tile(const TileView &tv, int g) {
   return tv.seg_tile_start[g];
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
-  return __uint_as_float(bits16 << 16);
+// Offset within the tile of part j of this lane in chunk ci.
+template <int P>
+__device__ __forceinline__ int part_offset(int ci, int j, int lane) {
+  return ci * kChunk + j * 64 * P + lane * P;
+}
+
+// ---------------------------------------------------------------- element loads / stores
+// A part is P elements starting at element e0 (a multiple of P); cnt of them exist (cnt == P
+// except in the last part of a buffer whose length is not a multiple of 8).
+template <int DT, int P>
+__device__ __forceinline__ void load_part(const void *base, int64_t e0, int cnt, float (&x)[P]) {
+  if (cnt == P) {
+    if constexpr (DT == 0) {
+      const f32x4 *p = reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + e0);
+#pragma unroll
+      for (int q = 0; q < P / 4; ++q) {
+        const f32x4 v = __builtin_nontemporal_load(p + q);
+        x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+      }
+    } else if constexpr (P == 8) {
+      const u32x4 v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + e0));
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+      const u32x2 v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(base) + e0));
+      const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      if (e < cnt) {
+        if constexpr (DT == 0)
+          x[e] = static_cast<const float *>(base)[e0 + e];
+        else
+          x[e] = __uint_as_float((uint32_t)static_cast<const uint16_t *>(base)[e0 + e] << 16);
+      } else {
+        x[e] = 0.0f;
+      }
+    }
+  }
+}
+
+// Codes: c[e] holds the code field (bits wide) of element e0 + e.
+template <int P>
+__device__ __forceinline__ void store_codes(uint8_t *codes, int64_t e0, int cnt, int bits,
+                                            const uint32_t (&c)[P]) {
+  if (bits == 8) {
+    uint32_t w[P / 4];
+#pragma unroll
+    for (int i = 0; i < P / 4; ++i)
+      w[i] = c[4 * i] | (c[4 * i + 1] << 8) | (c[4 * i + 2] << 16) | (c[4 * i + 3] << 24);
+    if (cnt == P) {
+      if constexpr (P == 4) {
+        __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t *>(codes + e0));
+      } else {
+        u32x2 v = {w[0], w[1]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(codes + e0));
+      }
+    } else {
+      for (int e = 0; e < cnt; ++e) codes[e0 + e] = (uint8_t)c[e];
+    }
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < P; ++e) w |= c[e] << (4 * e);
+    if (cnt == P) {
+      if constexpr (P == 4)
+        __builtin_nontemporal_store((uint16_t)w, reinterpret_cast<uint16_t *>(codes + e0 / 2));
+      else
+        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t *>(codes + e0 / 2));
+    } else {
+      for (int b = 0; b < (cnt + 1) / 2; ++b) codes[e0 / 2 + b] = (uint8_t)(w >> (8 * b));
+    }
+  }
+}
+
+template <int P>
+__device__ __forceinline__ void load_codes(const uint8_t *codes, int64_t e0, int cnt, int bits,
+                                           uint32_t (&c)[P]) {
+  if (bits == 8) {
+    uint32_t w[P / 4];
+    if (cnt == P) {
+      if constexpr (P == 4) {
+        w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(codes + e0));
+      } else {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(codes + e0));
+        w[0] = v.x;
+        w[1] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < P / 4; ++i) w[i] = 0;
+      for (int e = 0; e < cnt; ++e) w[e / 4] |= (uint32_t)codes[e0 + e] << (8 * (e % 4));
+    }
+#pragma unroll
+    for (int e = 0; e < P; ++e) c[e] = (w[e / 4] >> (8 * (e % 4))) & 0xFFu;
+  } else {
+    uint32_t w = 0;
+    if (cnt == P) {
+      if constexpr (P == 4)
+        w = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(codes + e0 / 2));
+      else
+        w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(codes + e0 / 2));
+    } else {
+      for (int b = 0; b < (cnt + 1) / 2; ++b) w |= (uint32_t)codes[e0 / 2 + b] << (8 * b);
+      w &= (1u << (4 * cnt)) - 1u;
+    }
+#pragma unroll
+    for (int e = 0; e < P; ++e) c[e] = (w >> (4 * e)) & 0xFu;
+  }
+}
+
+template <int P>
+__device__ __forceinline__ void store_sums(void *sums, int acc_bits, int64_t e0, int cnt,
+                                           const int32_t (&a)[P]) {
+  if (acc_bits == 16) {
+    int16_t *s = static_cast<int16_t *>(sums) + e0;
+    if (cnt == P) {
+      uint32_t w[P / 2];
+#pragma unroll
+      for (int i = 0; i < P / 2; ++i)
+        w[i] = ((uint32_t)a[2 * i] & 0xFFFFu) | ((uint32_t)a[2 * i + 1] << 16);
+      if constexpr (P == 4) {
+        u32x2 v = {w[0], w[1]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(s));
+      } else {
+        u32x4 v = {w[0], w[1], w[2], w[3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(s));
+      }
+    } else {
+      for (int e = 0; e < cnt; ++e) s[e] = (int16_t)a[e];
+    }
+  } else {
+    int32_t *s = static_cast<int32_t *>(sums) + e0;
+    if (cnt == P) {
+#pragma unroll
+      for (int q = 0; q < P / 4; ++q) {
+        u32x4 v = {(uint32_t)a[4 * q], (uint32_t)a[4 * q + 1], (uint32_t)a[4 * q + 2],
+                   (uint32_t)a[4 * q + 3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(s) + q);
+      }
+    } else {
+      for (int e = 0; e < cnt; ++e) s[e] = a[e];
+    }
+  }
+}
+
+template <int P>
+__device__ __forceinline__ void load_sums(const void *sums, int acc_bits, int64_t e0, int cnt,
+                                          int32_t (&a)[P]) {
+  if (acc_bits == 16) {
+    const int16_t *s = static_cast<const int16_t *>(sums) + e0;
+    if (cnt == P) {
+      uint32_t w[P / 2];
+      if constexpr (P == 4) {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(s));
+        w[0] = v.x;
+        w[1] = v.y;
+      } else {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(s));
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+      }
+#pragma unroll
+      for (int i = 0; i < P / 2; ++i) {
+        a[2 * i] = ((int32_t)(w[i] << 16)) >> 16;
+        a[2 * i + 1] = ((int32_t)w[i]) >> 16;
+      }
+    } else {
+      for (int e = 0; e < P; ++e) a[e] = e < cnt ? s[e] : 0;
+    }
+  } else {
+    const int32_t *s = static_cast<const int32_t *>(sums) + e0;
+    if (cnt == P) {
+#pragma unroll
+      for (int q = 0; q < P / 4; ++q) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(s) + q);
+        a[4 * q] = (int32_t)v.x; a[4 * q + 1] = (int32_t)v.y;
+        a[4 * q + 2] = (int32_t)v.z; a[4 * q + 3] = (int32_t)v.w;
+      }
+    } else {
+      for (int e = 0; e < P; ++e) a[e] = e < cnt ? s[e] : 0;
+    }
+  }
 }
 
 // Round-to-nearest-even fp32 -> bf16 (NaN stays a quiet NaN).
@@ -75,49 +275,38 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float v) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Eight consecutive elements starting at e0 (a multiple of 8).
-template <int DT>
-__device__ __forceinline__ void load8(const void *base, int64_t e0, float (&x)[8]) {
-  if constexpr (DT == 0) {
-    const f32x4 *p = reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + e0);
-    const f32x4 a = __builtin_nontemporal_load(p);
-    const f32x4 b = __builtin_nontemporal_load(p + 1);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  } else {
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + e0);
-    const u32x4 v = __builtin_nontemporal_load(p);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+template <int P>
+__device__ __forceinline__ void store_mean(void *out, int out_dtype, int64_t e0, int cnt,
+                                           const float (&v)[P]) {
+  if (out_dtype == 0) {
+    float *o = static_cast<float *>(out) + e0;
+    if (cnt == P) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  }
-}
-
-// The last group of a buffer whose length is not a multiple of 8: cnt < 8 elements, rest 0.
-template <int DT>
-__device__ __forceinline__ void load_tail(const void *base, int64_t e0, int cnt, float (&x)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if (e < cnt) {
-      if constexpr (DT == 0)
-        x[e] = static_cast<const float *>(base)[e0 + e];
-      else
-        x[e] = bf16_to_f32(static_cast<const uint16_t *>(base)[e0 + e]);
+      for (int q = 0; q < P / 4; ++q) {
+        f32x4 w = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(o) + q);
+      }
     } else {
-      x[e] = 0.0f;
+      for (int e = 0; e < cnt; ++e) o[e] = v[e];
+    }
+  } else {
+    uint16_t *o = static_cast<uint16_t *>(out) + e0;
+    uint32_t b[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) b[e] = f32_to_bf16(v[e]);
+    if (cnt == P) {
+      if constexpr (P == 4) {
+        u32x2 w = {b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(o));
+      } else {
+        u32x4 w = {b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
+                   b[6] | (b[7] << 16)};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(o));
+      }
+    } else {
+      for (int e = 0; e < cnt; ++e) o[e] = (uint16_t)b[e];
     }
   }
-}
-
-template <int DT>
-__device__ __forceinline__ void load_group(const void *base, int64_t e0, int cnt, float (&x)[8]) {
-  if (cnt == 8)
-    load8<DT>(base, e0, x);
-  else
-    load_tail<DT>(base, e0, cnt, x);
 }
 
 // ---------------------------------------------------------------- per-segment constants
@@ -145,215 +334,58 @@ __device__ __forceinline__ float seg_decode(float S, double denom) {
 }
 
 // ---------------------------------------------------------------- element quantisers
-// Uniform grid: signed level in [-s, s].
-__device__ __forceinline__ int32_t quant_uniform(float x, float inv, float sf, uint32_t h) {
+// Uniform grid.  Returns the level magnitude m in [0, s] as a float (exact small integer);
+// the signed level is copysign(m, x).
+__device__ __forceinline__ float quant_uniform_mag(float x, float inv, float sf, uint32_t h) {
   const float u = fminf(fabsf(x) * inv, sf);  // NaN -> s
   const float fl = floorf(u);
   const float p = u - fl;                     // exact
   const uint32_t c = (uint32_t)ceilf(p * 4294967296.0f);
-  const int32_t m = (int32_t)fl + (h < c ? 1 : 0);
-  return x < 0.0f ? -m : m;
+  return h < c ? ceilf(u) : fl;               // p > 0 whenever h < c, so ceil(u) = fl + 1
 }
 
-// Exponential grid: signed index sign*j, j in [0, E]; level j > 0 is 2^(j-E).
-__device__ __forceinline__ int32_t quant_exp(float x, float inv, int E, float two_em1,
-                                             uint32_t h) {
+// Exponential grid: index j in [0, E] of the level (level j > 0 is 2^(j-E)).
+__device__ __forceinline__ uint32_t quant_exp_index(float x, float inv, int E, float two_em1,
+                                                    uint32_t h) {
   const float u = fminf(fabsf(x) * inv, 1.0f);
   const uint32_t b = __float_as_uint(u);
   const int e = (int)(b >> 23) - 127;  // binade of u (u normal when e >= 1 - E)
-  int j;
+  uint32_t j;
   float p;
   if (e < 1 - E) {
     j = 0;
     p = u * two_em1;                   // (u - 0) / 2^(1-E), exact
   } else {
-    j = E + e;
+    j = (uint32_t)(E + e);
     p = __uint_as_float((b & 0x7FFFFFu) | 0x3F800000u) - 1.0f;  // u / 2^e - 1, exact
   }
   const uint32_t c = (uint32_t)ceilf(p * 4294967296.0f);
-  j += (h < c) ? 1 : 0;
-  return (x < 0.0f && j > 0) ? -j : j;
+  return j + (h < c ? 1u : 0u);
+}
+
+// Code field of a uniform level (signed, two's complement in `bits`).
+__device__ __forceinline__ uint32_t uniform_code(float m, float x, int bits) {
+  return (uint32_t)(int32_t)copysignf(m, x) & ((1u << bits) - 1u);
+}
+
+// Code field of an exponential index: sign bit above j (zero has no sign).
+__device__ __forceinline__ uint32_t exp_code(uint32_t j, float x, int bits) {
+  return ((x < 0.0f && j > 0) ? (1u << (bits - 1)) : 0u) | j;
+}
+
+// Signed integer value on the common grid of an exponential index: sign * 2^(j-1), 0 for j = 0.
+__device__ __forceinline__ int32_t exp_lin(uint32_t j, bool neg) {
+  const int32_t v = (int32_t)((1u << j) >> 1);
+  return neg ? -v : v;
 }
 
 template <int GRID>
-__device__ __forceinline__ int32_t quant_one(float x, const SegQ &q, int levels, float sf,
-                                             float two_em1, uint32_t h) {
-  if constexpr (GRID == 0)
-    return quant_uniform(x, q.inv, sf, h);
-  else
-    return quant_exp(x, q.inv, levels, two_em1, h);
-}
-
-// Integer value on the common grid: the level (uniform) or sign * 2^(j-1) (exponential).
-template <int GRID>
-__device__ __forceinline__ int32_t lin_of(int32_t q) {
-  if constexpr (GRID == 0) {
-    return q;
-  } else {
-    const uint32_t j = (uint32_t)(q < 0 ? -q : q);
-    const int32_t v = (int32_t)((1u << j) >> 1);
-    return q < 0 ? -v : v;
-  }
-}
-
-// Code bits of a signed level (bits wide, not yet positioned).
-template <int GRID>
-__device__ __forceinline__ uint32_t code_bits(int32_t q, int bits) {
-  if constexpr (GRID == 0) {
-    return (uint32_t)q & ((1u << bits) - 1u);
-  } else {
-    const uint32_t j = (uint32_t)(q < 0 ? -q : q);
-    return (q < 0 ? (1u << (bits - 1)) : 0u) | j;
-  }
-}
-
-// Signed level from code bits.
-template <int GRID>
-__device__ __forceinline__ int32_t level_of_code(uint32_t c, int bits) {
+__device__ __forceinline__ int32_t lin_of_code(uint32_t c, int bits) {
   if constexpr (GRID == 0) {
     return ((int32_t)(c << (32 - bits))) >> (32 - bits);
   } else {
-    const int32_t j = (int32_t)(c & ((1u << (bits - 1)) - 1u));
-    return (c >> (bits - 1)) & 1u ? -j : j;
-  }
-}
-
-// Store 8 codes of bits width for elements e0..e0+cnt-1.
-__device__ __forceinline__ void store_codes(uint8_t *codes, int64_t e0, int cnt, int bits,
-                                            const uint32_t (&c)[8]) {
-  if (bits == 8) {
-    const uint32_t lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    const uint32_t hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-    if (cnt == 8) {
-      u32x2 v = {lo, hi};
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(codes + e0));
-    } else {
-      for (int e = 0; e < cnt; ++e) codes[e0 + e] = (uint8_t)c[e];
-    }
-  } else {
-    uint32_t w = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w |= c[e] << (4 * e);
-    if (cnt == 8) {
-      __builtin_nontemporal_store(w, reinterpret_cast<uint32_t *>(codes + e0 / 2));
-    } else {
-      for (int b = 0; b < (cnt + 1) / 2; ++b) codes[e0 / 2 + b] = (uint8_t)(w >> (8 * b));
-    }
-  }
-}
-
-// Load the 8 code fields of elements e0..e0+7 (missing tail fields read as 0).
-__device__ __forceinline__ void load_codes(const uint8_t *codes, int64_t e0, int cnt, int bits,
-                                           uint32_t (&c)[8]) {
-  if (bits == 8) {
-    uint32_t lo = 0, hi = 0;
-    if (cnt == 8) {
-      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(codes + e0));
-      lo = v.x;
-      hi = v.y;
-    } else {
-      for (int e = 0; e < cnt; ++e) {
-        const uint32_t b = codes[e0 + e];
-        if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      c[e] = (lo >> (8 * e)) & 0xFFu;
-      c[e + 4] = (hi >> (8 * e)) & 0xFFu;
-    }
-  } else {
-    uint32_t w = 0;
-    if (cnt == 8) {
-      w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(codes + e0 / 2));
-    } else {
-      for (int b = 0; b < (cnt + 1) / 2; ++b) w |= (uint32_t)codes[e0 / 2 + b] << (8 * b);
-      w &= cnt >= 8 ? 0xFFFFFFFFu : ((1u << (4 * cnt)) - 1u);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = (w >> (4 * e)) & 0xFu;
-  }
-}
-
-__device__ __forceinline__ void store_sums(void *sums, int acc_bits, int64_t e0, int cnt,
-                                           const int32_t (&acc)[8]) {
-  if (acc_bits == 16) {
-    int16_t *s = static_cast<int16_t *>(sums) + e0;
-    if (cnt == 8) {
-      u32x4 v;
-      v.x = ((uint32_t)acc[0] & 0xFFFFu) | ((uint32_t)acc[1] << 16);
-      v.y = ((uint32_t)acc[2] & 0xFFFFu) | ((uint32_t)acc[3] << 16);
-      v.z = ((uint32_t)acc[4] & 0xFFFFu) | ((uint32_t)acc[5] << 16);
-      v.w = ((uint32_t)acc[6] & 0xFFFFu) | ((uint32_t)acc[7] << 16);
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(s));
-    } else {
-      for (int e = 0; e < cnt; ++e) s[e] = (int16_t)acc[e];
-    }
-  } else {
-    int32_t *s = static_cast<int32_t *>(sums) + e0;
-    if (cnt == 8) {
-      u32x4 a = {(uint32_t)acc[0], (uint32_t)acc[1], (uint32_t)acc[2], (uint32_t)acc[3]};
-      u32x4 b = {(uint32_t)acc[4], (uint32_t)acc[5], (uint32_t)acc[6], (uint32_t)acc[7]};
-      __builtin_nontemporal_store(a, reinterpret_cast<u32x4 *>(s));
-      __builtin_nontemporal_store(b, reinterpret_cast<u32x4 *>(s) + 1);
-    } else {
-      for (int e = 0; e < cnt; ++e) s[e] = acc[e];
-    }
-  }
-}
-
-__device__ __forceinline__ void load_sums(const void *sums, int acc_bits, int64_t e0, int cnt,
-                                          int32_t (&acc)[8]) {
-  if (acc_bits == 16) {
-    const int16_t *s = static_cast<const int16_t *>(sums) + e0;
-    if (cnt == 8) {
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(s));
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = ((int32_t)(w[i] << 16)) >> 16;
-        acc[2 * i + 1] = ((int32_t)w[i]) >> 16;
-      }
-    } else {
-      for (int e = 0; e < 8; ++e) acc[e] = e < cnt ? s[e] : 0;
-    }
-  } else {
-    const int32_t *s = static_cast<const int32_t *>(sums) + e0;
-    if (cnt == 8) {
-      const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(s));
-      const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(s) + 1);
-      acc[0] = (int32_t)a.x; acc[1] = (int32_t)a.y; acc[2] = (int32_t)a.z; acc[3] = (int32_t)a.w;
-      acc[4] = (int32_t)b.x; acc[5] = (int32_t)b.y; acc[6] = (int32_t)b.z; acc[7] = (int32_t)b.w;
-    } else {
-      for (int e = 0; e < 8; ++e) acc[e] = e < cnt ? s[e] : 0;
-    }
-  }
-}
-
-__device__ __forceinline__ void store_mean(void *out, int out_dtype, int64_t e0, int cnt,
-                                           const float (&v)[8]) {
-  if (out_dtype == 0) {
-    float *o = static_cast<float *>(out) + e0;
-    if (cnt == 8) {
-      f32x4 a = {v[0], v[1], v[2], v[3]};
-      f32x4 b = {v[4], v[5], v[6], v[7]};
-      __builtin_nontemporal_store(a, reinterpret_cast<f32x4 *>(o));
-      __builtin_nontemporal_store(b, reinterpret_cast<f32x4 *>(o) + 1);
-    } else {
-      for (int e = 0; e < cnt; ++e) o[e] = v[e];
-    }
-  } else {
-    uint16_t *o = static_cast<uint16_t *>(out) + e0;
-    uint32_t b[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) b[e] = f32_to_bf16(v[e]);
-    if (cnt == 8) {
-      u32x4 w = {b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
-                 b[6] | (b[7] << 16)};
-      __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(o));
-    } else {
-      for (int e = 0; e < cnt; ++e) o[e] = (uint16_t)b[e];
-    }
+    const uint32_t j = c & ((1u << (bits - 1)) - 1u);
+    return exp_lin(j, ((c >> (bits - 1)) & 1u) != 0);
   }
 }
 
@@ -376,197 +408,308 @@ __device__ __forceinline__ double block_sum(double v, double *lds) {
   return t;
 }
 
-// ================================================================ kernels
-// Per (worker, tile) fp64 sum of squares.  Grid: (tiles, K).
+// ================================================================ global norm
+// Per (worker, norm tile) fp64 sum of squares.  Grid: (tiles, K).
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_norm_partial(NormArgs a) {
+  constexpr int P = DT == 0 ? 4 : 8;
+  constexpr int NP = kChunk / (64 * P);
   __shared__ double lds[kBlock / 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int k = blockIdx.y;
   const void *src = a.grads[k];
   for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, begin, len, seg);
-    const int ng = (len + 7) >> 3;
+    tile_of(a.tv, t, kNormTile, begin, len, seg);
+    const int nch = (len + kChunk - 1) / kChunk;
     double acc = 0.0;
-    for (int gi = threadIdx.x; gi < ng; gi += kBlock) {
-      float x[8];
-      load_group<DT>(src, begin + 8 * (int64_t)gi, min(8, len - 8 * gi), x);
+    for (int ci = wv; ci < nch; ci += kBlock / 64) {
+      float x[NP][P];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double v = (double)x[e];
-        acc = __fma_rn(v, v, acc);  // v*v is exact in fp64, so this is the plain sum
+      for (int j = 0; j < NP; ++j) {
+        const int o = part_offset<P>(ci, j, lane);
+        const int cnt = min(P, len - o);
+        if (cnt > 0) {
+          load_part<DT, P>(src, begin + o, cnt, x[j]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < P; ++e) x[j][e] = 0.0f;
+        }
       }
+#pragma unroll
+      for (int j = 0; j < NP; ++j)
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          const double v = (double)x[j][e];
+          acc = __fma_rn(v, v, acc);  // v*v is exact in fp64, so this is the plain sum
+        }
     }
     const double tot = block_sum(acc, lds);
     if (threadIdx.x == 0) a.partial[(int64_t)k * a.tv.ntiles + t] = tot;
   }
 }
 
-// One block per segment: fixed-order sum of the tile partials, sqrt, max over workers.
-__global__ __launch_bounds__(kBlock) void k_norm_finalize(NormArgs a) {
+// One block per (segment, worker): fixed-order sum of the tile partials, sqrt.
+__global__ __launch_bounds__(kBlock) void k_norm_segments(NormArgs a) {
   __shared__ double lds[kBlock / 64];
-  const int g = blockIdx.x;
+  const int g = blockIdx.x, k = blockIdx.y;
   const int64_t t0 = seg_first_tile(a.tv, g), t1 = seg_first_tile(a.tv, g + 1);
+  const double *part = a.partial + (int64_t)k * a.tv.ntiles;
+  double acc = 0.0;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += kBlock) acc += part[t];
+  const double nrm = sqrt(block_sum(acc, lds));
+  if (threadIdx.x == 0) a.norms[(int64_t)k * a.tv.nseg + g] = nrm;
+}
+
+// One thread per segment: S_g = fp32(max_k norm), 0 (and a status flag) if not finite.
+__global__ void k_norm_scale(NormArgs a) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= a.tv.nseg) return;
   double best = 0.0;
   bool bad = false;
   for (int k = 0; k < a.K; ++k) {
-    double acc = 0.0;
-    const double *part = a.partial + (int64_t)k * a.tv.ntiles;
-    for (int64_t t = t0 + threadIdx.x; t < t1; t += kBlock) acc += part[t];
-    const double nrm = sqrt(block_sum(acc, lds));
-    if (a.norms_out && threadIdx.x == 0) a.norms_out[(int64_t)k * a.tv.nseg + g] = nrm;
+    const double nrm = a.norms[(int64_t)k * a.tv.nseg + g];
+    if (a.norms_out) a.norms_out[(int64_t)k * a.tv.nseg + g] = nrm;
     if (!isfinite(nrm))
       bad = true;
     else if (nrm > best)
       best = nrm;
   }
-  if (threadIdx.x == 0) {
-    float S = (float)best;
-    if (bad || !isfinite(S)) {
-      S = 0.0f;
-      atomicOr(a.status, 1u);
-    }
-    a.scale_out[g] = S;
+  float S = (float)best;
+  if (bad || !isfinite(S)) {
+    S = 0.0f;
+    atomicOr(a.status, 1u);
   }
+  a.scale_out[g] = S;
 }
 
-// Quantise one worker's buffer and pack the codes.
+// ================================================================ quantise + pack (one worker)
 template <int DT, int GRID>
 __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
+  constexpr int P = DT == 0 ? 4 : 8;
+  constexpr int NP = kChunk / (64 * P);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float sf = (float)a.levels;
   const float two_em1 = ldexpf(1.0f, a.levels - 1);
   for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, begin, len, seg);
+    tile_of(a.tv, t, kTile, begin, len, seg);
     const SegQ q = seg_quant<GRID>(a.scale[seg], a.levels);
-    const int ng = (len + 7) >> 3;
-    for (int gi = threadIdx.x; gi < ng; gi += kBlock) {
-      const int64_t e0 = begin + 8 * (int64_t)gi;
-      const int cnt = min(8, len - 8 * gi);
-      uint32_t c[8];
-      if (q.valid) {
-        float x[8];
-        load_group<DT>(a.grad, e0, cnt, x);
-        const uint32_t ctr = a.index_base + (uint32_t)e0;
+    const int nch = (len + kChunk - 1) / kChunk;
+    for (int ci = wv; ci < nch; ci += kBlock / 64) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t h = fmix32((ctr + e) ^ a.key);
-          c[e] = code_bits<GRID>(quant_one<GRID>(x[e], q, a.levels, sf, two_em1, h), a.bits);
+      for (int j = 0; j < NP; ++j) {
+        const int o = part_offset<P>(ci, j, lane);
+        const int cnt = min(P, len - o);
+        if (cnt <= 0) continue;
+        const int64_t e0 = begin + o;
+        uint32_t c[P];
+        if (q.valid) {
+          float x[P];
+          load_part<DT, P>(a.grad, e0, cnt, x);
+          const uint32_t ctr = a.index_base + (uint32_t)e0;
+#pragma unroll
+          for (int e = 0; e < P; ++e) {
+            const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+            if constexpr (GRID == 0)
+              c[e] = uniform_code(quant_uniform_mag(x[e], q.inv, sf, h), x[e], a.bits);
+            else
+              c[e] = exp_code(quant_exp_index(x[e], q.inv, a.levels, two_em1, h), x[e], a.bits);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < P; ++e) c[e] = 0;
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) c[e] = 0;
+        store_codes<P>(a.codes, e0, cnt, a.bits, c);
       }
-      store_codes(a.codes, e0, cnt, a.bits, c);
     }
   }
 }
 
-// sums_i = sum_k lin(code_{k,i}).
-template <int GRID>
+// ================================================================ integer sum of codes
+// sums_i = sum_k lin(code_{k,i}).  P = 8 for int16 sums (16 B stores), 4 for int32.
+template <int GRID, int P>
 __global__ __launch_bounds__(kBlock) void k_accumulate(AccArgs a) {
-  const int64_t ng = (a.n + 7) >> 3;
-  for (int64_t gi = (int64_t)blockIdx.x * kBlock + threadIdx.x; gi < ng;
-       gi += (int64_t)gridDim.x * kBlock) {
-    const int64_t e0 = 8 * gi;
-    const int cnt = (int)min((int64_t)8, a.n - e0);
-    int32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int k = 0; k < a.K; ++k) {
-      uint32_t c[8];
-      load_codes(a.codes[k], e0, cnt, a.bits, c);
+  constexpr int NP = kChunk / (64 * P);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const TileView tv{nullptr, nullptr, (a.n + kTile - 1) / kTile, a.n, 1};
+  for (int64_t t = blockIdx.x; t < tv.ntiles; t += gridDim.x) {
+    int64_t begin;
+    int len, seg;
+    tile_of(tv, t, kTile, begin, len, seg);
+    const int nch = (len + kChunk - 1) / kChunk;
+    for (int ci = wv; ci < nch; ci += kBlock / 64) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += lin_of<GRID>(level_of_code<GRID>(c[e], a.bits));
+      for (int j = 0; j < NP; ++j) {
+        const int o = part_offset<P>(ci, j, lane);
+        const int cnt = min(P, len - o);
+        if (cnt <= 0) continue;
+        const int64_t e0 = begin + o;
+        int32_t acc[P];
+#pragma unroll
+        for (int e = 0; e < P; ++e) acc[e] = 0;
+        for (int k = 0; k < a.K; ++k) {
+          uint32_t c[P];
+          load_codes<P>(a.codes[k], e0, cnt, a.bits, c);
+#pragma unroll
+          for (int e = 0; e < P; ++e) acc[e] += lin_of_code<GRID>(c[e], a.bits);
+        }
+        store_sums<P>(a.sums, a.acc_bits, e0, cnt, acc);
+      }
     }
-    store_sums(a.sums, a.acc_bits, e0, cnt, acc);
   }
 }
 
-// mean_i = fp32(sums_i) * f_g.
+// ================================================================ decode of the mean
+template <int P>
 __global__ __launch_bounds__(kBlock) void k_dequantize(DequantArgs a) {
+  constexpr int NP = kChunk / (64 * P);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, begin, len, seg);
+    tile_of(a.tv, t, kTile, begin, len, seg);
     const float f = seg_decode(a.scale[seg], a.denom);
-    const int ng = (len + 7) >> 3;
-    for (int gi = threadIdx.x; gi < ng; gi += kBlock) {
-      const int64_t e0 = begin + 8 * (int64_t)gi;
-      const int cnt = min(8, len - 8 * gi);
-      int32_t acc[8];
-      load_sums(a.sums, a.acc_bits, e0, cnt, acc);
-      float v[8];
+    const int nch = (len + kChunk - 1) / kChunk;
+    for (int ci = wv; ci < nch; ci += kBlock / 64) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (float)acc[e] * f;
-      store_mean(a.out, a.out_dtype, e0, cnt, v);
+      for (int j = 0; j < NP; ++j) {
+        const int o = part_offset<P>(ci, j, lane);
+        const int cnt = min(P, len - o);
+        if (cnt <= 0) continue;
+        const int64_t e0 = begin + o;
+        int32_t s[P];
+        load_sums<P>(a.sums, a.acc_bits, e0, cnt, s);
+        float v[P];
+#pragma unroll
+        for (int e = 0; e < P; ++e) v[e] = (float)s[e] * f;
+        store_mean<P>(a.out, a.out_dtype, e0, cnt, v);
+      }
     }
   }
 }
 
-// Fused pass: for each element, K quantisations in registers, integer sum, one decode.
-// KT > 0 fixes K at compile time (loads of all workers are issued before any arithmetic);
-// KT = 0 loops over a runtime K.
-template <int KT, int DT, int GRID>
-__global__ __launch_bounds__(kBlock) void k_fused(FusedArgs a) {
+// ================================================================ fused pass
+// For each element: the K workers' quantisations in registers, their integer sum, one decode.
+// Workers are processed in batches of KB whose loads are all issued before any arithmetic.
+// KT > 0 fixes K at compile time; KT = 0 loops over a runtime K.
+template <int DT, int GRID, int P, int NP, int KB, bool STORE>
+__device__ __forceinline__ void fused_batch(const FusedArgs &a, int k0, int kn,
+                                            const int64_t (&e0)[NP], const int (&cnt)[NP],
+                                            const uint32_t (&am)[NP][P], const SegQ &q,
+                                            float sf, float two_em1,
+                                            float (&accf)[NP][P], int32_t (&acci)[NP][P]) {
+  float x[KB][NP][P];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    if (kb < kn)
+#pragma unroll
+      for (int j = 0; j < NP; ++j)
+        if (cnt[j] > 0) load_part<DT, P>(a.grads[k0 + kb], e0[j], cnt[j], x[kb][j]);
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    if (kb >= kn) break;
+    const uint32_t km = a.key_mix[k0 + kb];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      uint32_t c[P];
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        const float xv = x[kb][j][e];
+        const uint32_t h = fmix32_tail(am[j][e] ^ km);
+        if constexpr (GRID == 0) {
+          const float m = quant_uniform_mag(xv, q.inv, sf, h);
+          accf[j][e] += copysignf(m, xv);
+          if constexpr (STORE) c[e] = uniform_code(m, xv, a.bits);
+        } else {
+          const uint32_t jj = quant_exp_index(xv, q.inv, a.levels, two_em1, h);
+          acci[j][e] += exp_lin(jj, xv < 0.0f);
+          if constexpr (STORE) c[e] = exp_code(jj, xv, a.bits);
+        }
+      }
+      if constexpr (STORE)
+        if (cnt[j] > 0) store_codes<P>(a.codes[k0 + kb], e0[j], cnt[j], a.bits, c);
+    }
+  }
+}
+
+// The uniform fast path fits in 128 VGPRs (4 waves per SIMD, enough loads in flight per CU
+// to cover HBM latency); the exponential grid and the code-storing variant keep more values
+// live and get 256 (2 waves per SIMD) rather than spilling.
+template <int KT, int DT, int GRID, bool STORE>
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu((GRID == 0 && !STORE) ? 4 : 2, 8)))
+void k_fused(FusedArgs a) {
+  constexpr int P = DT == 0 ? 4 : 8;
+  constexpr int NP = kChunk / (64 * P);
+  constexpr int KB = KT == 16 ? 8 : (KT > 0 ? KT : 4);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int K = KT > 0 ? KT : a.K;
   const float sf = (float)a.levels;
   const float two_em1 = ldexpf(1.0f, a.levels - 1);
-  const bool store_codes_ = a.store_codes != 0;
   for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, begin, len, seg);
+    tile_of(a.tv, t, kTile, begin, len, seg);
     const float S = a.scale[seg];
     const SegQ q = seg_quant<GRID>(S, a.levels);
     const float f = seg_decode(S, a.denom);
-    const int ng = (len + 7) >> 3;
-    for (int gi = threadIdx.x; gi < ng; gi += kBlock) {
-      const int64_t e0 = begin + 8 * (int64_t)gi;
-      const int cnt = min(8, len - 8 * gi);
-      int32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (q.valid) {
-        const uint32_t ctr = a.index_base + (uint32_t)e0;
-        if constexpr (KT > 0) {
-          float x[KT][8];
+    const int nch = (len + kChunk - 1) / kChunk;
+    for (int ci = wv; ci < nch; ci += kBlock / 64) {
+      int64_t e0[NP];
+      int cnt[NP];
+      uint32_t am[NP][P];
+      float accf[NP][P];
+      int32_t acci[NP][P];
 #pragma unroll
-          for (int k = 0; k < KT; ++k) load_group<DT>(a.grads[k], e0, cnt, x[k]);
+      for (int j = 0; j < NP; ++j) {
+        const int o = part_offset<P>(ci, j, lane);
+        cnt[j] = min(P, len - o);
+        e0[j] = begin + o;
+        const uint32_t ctr = a.index_base + (uint32_t)e0[j];
 #pragma unroll
-          for (int k = 0; k < KT; ++k) {
-            uint32_t c[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t h = fmix32((ctr + e) ^ a.keys[k]);
-              const int32_t lv = quant_one<GRID>(x[k][e], q, a.levels, sf, two_em1, h);
-              acc[e] += lin_of<GRID>(lv);
-              c[e] = code_bits<GRID>(lv, a.bits);
-            }
-            if (store_codes_) store_codes(a.codes[k], e0, cnt, a.bits, c);
-          }
-        } else {
-          for (int k = 0; k < K; ++k) {
-            float x[8];
-            load_group<DT>(a.grads[k], e0, cnt, x);
-            uint32_t c[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t h = fmix32((ctr + e) ^ a.keys[k]);
-              const int32_t lv = quant_one<GRID>(x[e], q, a.levels, sf, two_em1, h);
-              acc[e] += lin_of<GRID>(lv);
-              c[e] = code_bits<GRID>(lv, a.bits);
-            }
-            if (store_codes_) store_codes(a.codes[k], e0, cnt, a.bits, c);
-          }
+        for (int e = 0; e < P; ++e) {
+          am[j][e] = mix16(ctr + e);
+          accf[j][e] = 0.0f;
+          acci[j][e] = 0;
         }
-      } else if (store_codes_) {
-        const uint32_t z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int k = 0; k < K; ++k) store_codes(a.codes[k], e0, cnt, a.bits, z);
       }
-      if (a.sums) store_sums(a.sums, a.acc_bits, e0, cnt, acc);
-      float v[8];
+      if (q.valid) {
+        if constexpr (KT > 0) {
+#pragma unroll 1
+          for (int k0 = 0; k0 < KT; k0 += KB)
+            fused_batch<DT, GRID, P, NP, KB, STORE>(a, k0, KB, e0, cnt, am, q, sf, two_em1,
+                                                    accf, acci);
+        } else {
+#pragma unroll 1
+          for (int k0 = 0; k0 < K; k0 += KB)
+            fused_batch<DT, GRID, P, NP, KB, STORE>(a, k0, min(KB, K - k0), e0, cnt, am, q,
+                                                    sf, two_em1, accf, acci);
+        }
+      } else if (STORE) {
+        const uint32_t z[P] = {};
+        for (int k = 0; k < K; ++k)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (float)acc[e] * f;
-      store_mean(a.out, a.out_dtype, e0, cnt, v);
+          for (int j = 0; j < NP; ++j)
+            if (cnt[j] > 0) store_codes<P>(a.codes[k], e0[j], cnt[j], a.bits, z);
+      }
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        if (cnt[j] <= 0) continue;
+        int32_t s[P];
+        float v[P];
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          // uniform sums are carried exactly in fp32; exponential sums in int32
+          const float sumf = GRID == 0 ? accf[j][e] : (float)acci[j][e];
+          s[e] = GRID == 0 ? (int32_t)accf[j][e] : acci[j][e];
+          v[e] = sumf * f;
+        }
+        if (a.sums) store_sums<P>(a.sums, a.acc_bits, e0[j], cnt[j], s);
+        store_mean<P>(a.out, a.out_dtype, e0[j], cnt[j], v);
+      }
     }
   }
 }
@@ -576,8 +719,8 @@ __global__ void k_clear_u32(unsigned *p, int count) {
   if (i < count) p[i] = 0u;
 }
 
-int grid_for(int64_t work) {
-  return (int)(work < kMaxGrid ? (work > 0 ? work : 1) : kMaxGrid);
+int grid_for(int64_t work, int cap) {
+  return (int)(work < cap ? (work > 0 ? work : 1) : cap);
 }
 
 }  // namespace
@@ -585,20 +728,22 @@ int grid_for(int64_t work) {
 // ================================================================ launchers
 hipError_t launch_global_norm(const NormArgs &a, int dtype, hipStream_t s) {
   if (a.tv.ntiles > 0) {
-    dim3 grid(grid_for(a.tv.ntiles), a.K);
+    dim3 grid(grid_for(a.tv.ntiles, kNormGrid), a.K);
     if (dtype == 0)
       hipLaunchKernelGGL(k_norm_partial<0>, grid, dim3(kBlock), 0, s, a);
     else
       hipLaunchKernelGGL(k_norm_partial<1>, grid, dim3(kBlock), 0, s, a);
   }
-  if (a.tv.nseg > 0)
-    hipLaunchKernelGGL(k_norm_finalize, dim3(a.tv.nseg), dim3(kBlock), 0, s, a);
+  if (a.tv.nseg > 0) {
+    hipLaunchKernelGGL(k_norm_segments, dim3(a.tv.nseg, a.K), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_norm_scale, dim3((a.tv.nseg + 255) / 256), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, hipStream_t s) {
   if (a.tv.ntiles == 0) return hipSuccess;
-  dim3 g(grid_for(a.tv.ntiles));
+  dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
   if (dtype == 0 && grid == 0) hipLaunchKernelGGL((k_quantize_pack<0, 0>), g, dim3(kBlock), 0, s, a);
   if (dtype == 0 && grid == 1) hipLaunchKernelGGL((k_quantize_pack<0, 1>), g, dim3(kBlock), 0, s, a);
   if (dtype == 1 && grid == 0) hipLaunchKernelGGL((k_quantize_pack<1, 0>), g, dim3(kBlock), 0, s, a);
@@ -607,41 +752,57 @@ hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, hipStre
 }
 
 hipError_t launch_accumulate(const AccArgs &a, int grid, hipStream_t s) {
-  const int64_t ng = (a.n + 7) / 8;
-  if (ng == 0) return hipSuccess;
-  dim3 g(grid_for((ng + kBlock - 1) / kBlock));
-  if (grid == 0)
-    hipLaunchKernelGGL(k_accumulate<0>, g, dim3(kBlock), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_accumulate<1>, g, dim3(kBlock), 0, s, a);
+  const int64_t ntiles = (a.n + kTile - 1) / kTile;
+  if (ntiles == 0) return hipSuccess;
+  dim3 g(grid_for(ntiles, kStreamGrid));
+  if (a.acc_bits == 16) {
+    if (grid == 0) hipLaunchKernelGGL((k_accumulate<0, 8>), g, dim3(kBlock), 0, s, a);
+    else hipLaunchKernelGGL((k_accumulate<1, 8>), g, dim3(kBlock), 0, s, a);
+  } else {
+    if (grid == 0) hipLaunchKernelGGL((k_accumulate<0, 4>), g, dim3(kBlock), 0, s, a);
+    else hipLaunchKernelGGL((k_accumulate<1, 4>), g, dim3(kBlock), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s) {
   if (a.tv.ntiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_dequantize, dim3(grid_for(a.tv.ntiles)), dim3(kBlock), 0, s, a);
+  dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+  // 16-byte accesses on both sides: int16 -> bf16 with 8 elements per part, else 4
+  if (a.acc_bits == 16 && a.out_dtype == 1)
+    hipLaunchKernelGGL(k_dequantize<8>, g, dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_dequantize<4>, g, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
-template <int DT, int GRID>
+template <int DT, int GRID, bool STORE>
 static void launch_fused_k(const FusedArgs &a, dim3 g, hipStream_t s) {
   switch (a.K) {
-    case 1: hipLaunchKernelGGL((k_fused<1, DT, GRID>), g, dim3(kBlock), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_fused<2, DT, GRID>), g, dim3(kBlock), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_fused<4, DT, GRID>), g, dim3(kBlock), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((k_fused<8, DT, GRID>), g, dim3(kBlock), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((k_fused<16, DT, GRID>), g, dim3(kBlock), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_fused<0, DT, GRID>), g, dim3(kBlock), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_fused<1, DT, GRID, STORE>), g, dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_fused<2, DT, GRID, STORE>), g, dim3(kBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_fused<4, DT, GRID, STORE>), g, dim3(kBlock), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_fused<8, DT, GRID, STORE>), g, dim3(kBlock), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_fused<16, DT, GRID, STORE>), g, dim3(kBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_fused<0, DT, GRID, STORE>), g, dim3(kBlock), 0, s, a); break;
   }
+}
+
+template <bool STORE>
+static void launch_fused_s(const FusedArgs &a, int dtype, int grid, dim3 g, hipStream_t s) {
+  if (dtype == 0 && grid == 0) launch_fused_k<0, 0, STORE>(a, g, s);
+  if (dtype == 0 && grid == 1) launch_fused_k<0, 1, STORE>(a, g, s);
+  if (dtype == 1 && grid == 0) launch_fused_k<1, 0, STORE>(a, g, s);
+  if (dtype == 1 && grid == 1) launch_fused_k<1, 1, STORE>(a, g, s);
 }
 
 hipError_t launch_fused(const FusedArgs &a, int dtype, int grid, hipStream_t s) {
   if (a.tv.ntiles == 0) return hipSuccess;
-  dim3 g(grid_for(a.tv.ntiles));
-  if (dtype == 0 && grid == 0) launch_fused_k<0, 0>(a, g, s);
-  if (dtype == 0 && grid == 1) launch_fused_k<0, 1>(a, g, s);
-  if (dtype == 1 && grid == 0) launch_fused_k<1, 0>(a, g, s);
-  if (dtype == 1 && grid == 1) launch_fused_k<1, 1>(a, g, s);
+  dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+  if (a.store_codes)
+    launch_fused_s<true>(a, dtype, grid, g, s);
+  else
+    launch_fused_s<false>(a, dtype, grid, g, s);
   return hipGetLastError();
 }
 
