@@ -8,16 +8,20 @@
 //
 // Design for CDNA4.  The step is HBM-bound: at rank r <= 8 the products do at most 2r flops
 // per 4-byte element, far below the MFMA ridge, so they stay on the vector ALUs with fp32 FMA
-// and the work is organised around the passes over the n x m matrix:
-//   pass 1  E <- G + E and P = E Q          (read G, E; write E)      k_lq_ef_mq
-//   pass 2  Q' = E^T P                      (read E)                  k_lq_mtp (+ k_lq_qsum)
-//   pass 3  E <- E - Phat Q'hat^T           (read E; write E)         k_lq_ef_update
-// Row passes give each block 4 rows so every Q value loaded from L2 is used 4 times; the
-// column pass gives each 512-thread block 256 rows x (64*VEC) columns and reduces its 8 waves
-// in LDS, so the per-chunk partials stay a few percent of the pass.  The orthonormalisation
-// (a single workgroup) is two rounds of Cholesky-QR in fp64 (the r x r Gram matrix in one
-// reduction, Gram-Schmidt on it by one thread, then P <- P T): in exact arithmetic this is
-// the Gram-Schmidt Q factor, and the second round restores orthogonality to fp64 accuracy.
+// and the work is organised around the three passes over the n x m matrix:
+//   pass 1  E <- G + E and P = E Q              (read G, E; write E)   k_lq_ef_mq
+//   pass 2  Q' = E^T Pt                         (read E)               k_lq_mtp + k_lq_qsum
+//   pass 3  E <- E - Phat Q'hat^T               (read E; write E)      k_lq_ef_update
+// Row passes give each block 4 rows so every Q value fetched (from L2: Q is at most
+// m x 8 fp32) is used 4 times; Q is read in its own row-major layout (a thread's 4 columns
+// are 4r consecutive floats), so no transposed copy is made.  The column pass gives each
+// 512-thread block 128 rows x (64*VEC) columns and reduces its 8 waves in LDS, so the
+// per-chunk partials stay a few percent of the pass.
+// Orthonormalisation: pass 1 also emits each block's r x r Gram contribution (products of the
+// fp32 P values, exact in fp64); k_lq_solve sums them in a fixed order and runs Cholesky-QR
+// twice in r x r space -- T1 from G, then T2 from T1^T G T1, which measures and removes the
+// error of the first factorisation -- and applies T = T1 T2 to P.  In exact arithmetic P T is
+// the Gram-Schmidt Q factor of P (columns in order; a column with no remaining norm is zero).
 // The log quantiser encodes with a table of the L bin boundaries rounded up to fp32 (so
 // "y >= boundary" is decided exactly) and decodes with a table of the L+1 Eq. 6 levels.
 #include <float.h>
@@ -33,21 +37,11 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRowsA = 4;     // rows per block in the row passes
+constexpr int kRowsA = 4;      // rows per block in the row passes
 constexpr int kBlockA = 256;
-constexpr int kRowsC = 256;   // rows per chunk in the column pass
+constexpr int kRowsC = 128;    // rows per chunk in the column pass
 constexpr int kWavesC = 8;
-constexpr int kBlockOrth = 1024;
-
-template <int VEC>
-__device__ __forceinline__ void ldv(const float *p, float (&v)[VEC]) {
-  if constexpr (VEC == 4) {
-    const f32x4 t = *reinterpret_cast<const f32x4 *>(p);
-    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-  } else {
-    v[0] = *p;
-  }
-}
+constexpr int kBlockSolve = 256;
 
 template <int VEC>
 __device__ __forceinline__ void ldv_nt(const float *p, float (&v)[VEC]) {
@@ -69,6 +63,28 @@ __device__ __forceinline__ void stv(float *p, const float (&v)[VEC]) {
   }
 }
 
+// q[c][v] = Q[(j + v) * RANK + c]: the VEC rows of the row-major m x RANK factor that this
+// thread's VEC columns need (4*RANK consecutive floats when VEC = 4; j is a multiple of 4).
+template <int RANK, int VEC>
+__device__ __forceinline__ void load_q_rows(const float *Q, int64_t j, float (&q)[RANK][VEC]) {
+  if constexpr (VEC == 4) {
+    float f[4 * RANK];
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(Q + j * RANK);
+#pragma unroll
+    for (int i = 0; i < RANK; ++i) {
+      const f32x4 t = p[i];
+      f[4 * i] = t.x; f[4 * i + 1] = t.y; f[4 * i + 2] = t.z; f[4 * i + 3] = t.w;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int c = 0; c < RANK; ++c) q[c][v] = f[v * RANK + c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < RANK; ++c) q[c][0] = Q[j * RANK + c];
+  }
+}
+
 __device__ __forceinline__ float wave_sum_f(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -87,24 +103,29 @@ __device__ __forceinline__ float wave_max_f(float v) {
   return v;
 }
 
-// Qt (r x m) <- Q (m x r).
-__global__ void k_lq_transpose(const float *Q, float *Qt, int64_t m, int r) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < m * r) {
-    const int64_t j = i / r;
-    const int c = (int)(i % r);
-    Qt[(int64_t)c * m + j] = Q[i];
+// Index (a, b), a <= b, of packed upper-triangle entry t of a RANK x RANK matrix.
+template <int RANK>
+__device__ __forceinline__ void tri_index(int t, int &a, int &b) {
+  a = 0;
+  while (t >= RANK - a) {
+    t -= RANK - a;
+    ++a;
   }
+  b = a + t;
 }
 
-// Pass 1: E <- G + E (the gradient with the previous error fed back) and P = E Q.
+// Pass 1: E <- G + E (the gradient with the previous error fed back), P = E Q, and the block's
+// share of the Gram matrix P^T P (packed upper triangle, fp64).
 template <int RANK, int VEC>
 __global__ __launch_bounds__(kBlockA) void k_lq_ef_mq(const float *__restrict__ G,
                                                       float *__restrict__ E,
-                                                      const float *__restrict__ Qt,
-                                                      float *__restrict__ P, int64_t n,
+                                                      const float *__restrict__ Q,
+                                                      float *__restrict__ P,
+                                                      double *__restrict__ gpart, int64_t n,
                                                       int64_t m) {
+  constexpr int NG = RANK * (RANK + 1) / 2;
   __shared__ float red[kBlockA / 64][kRowsA * RANK];
+  __shared__ float pv[kRowsA * RANK];
   const int64_t row0 = (int64_t)blockIdx.x * kRowsA;
   float acc[kRowsA][RANK];
 #pragma unroll
@@ -113,8 +134,7 @@ __global__ __launch_bounds__(kBlockA) void k_lq_ef_mq(const float *__restrict__ 
     for (int c = 0; c < RANK; ++c) acc[rr][c] = 0.0f;
   for (int64_t j = (int64_t)threadIdx.x * VEC; j < m; j += (int64_t)kBlockA * VEC) {
     float q[RANK][VEC];
-#pragma unroll
-    for (int c = 0; c < RANK; ++c) ldv<VEC>(Qt + (int64_t)c * m + j, q[c]);
+    load_q_rows<RANK, VEC>(Q, j, q);
 #pragma unroll
     for (int rr = 0; rr < kRowsA; ++rr) {
       const int64_t row = row0 + rr;
@@ -144,112 +164,153 @@ __global__ __launch_bounds__(kBlockA) void k_lq_ef_mq(const float *__restrict__ 
   if (threadIdx.x < kRowsA * RANK) {
     const int t = threadIdx.x;
     const int64_t row = row0 + t / RANK;
-    if (row < n) {
-      float s = 0.0f;
-      for (int i = 0; i < kBlockA / 64; ++i) s += red[i][t];
-      P[row * RANK + t % RANK] = s;
-    }
+    float s = 0.0f;
+    for (int i = 0; i < kBlockA / 64; ++i) s += red[i][t];
+    if (row >= n) s = 0.0f;
+    pv[t] = s;
+    if (row < n) P[row * RANK + t % RANK] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < NG) {
+    int a, b;
+    tri_index<RANK>(threadIdx.x, a, b);
+    double g = 0.0;
+#pragma unroll
+    for (int rr = 0; rr < kRowsA; ++rr) g += (double)pv[rr * RANK + a] * (double)pv[rr * RANK + b];
+    gpart[(int64_t)blockIdx.x * NG + threadIdx.x] = g;
   }
 }
 
-// Orthonormalise the columns of P (n x RANK): two rounds of Cholesky-QR in fp64 on one
-// workgroup.  Each round forms the Gram matrix, runs modified Gram-Schmidt on it (one thread,
-// RANK x RANK) to get the upper-triangular T with P T orthonormal, and applies T.  A column
-// whose remaining norm is not positive becomes zero.
+// Upper-triangular T with (P T)^T (P T) = I given G = P^T P: Gram-Schmidt carried out on G
+// (column c: remove its components along the previous orthonormal columns, then normalise;
+// a column with no remaining norm becomes zero).  RANK x RANK, in registers.
 template <int RANK>
-__global__ __launch_bounds__(kBlockOrth) void k_lq_orth(const float *P, double *W, float *Pt,
-                                                        float *p_pre, int64_t n) {
+__device__ __forceinline__ void gram_schmidt_T(const double (&G)[RANK][RANK],
+                                               double (&T)[RANK][RANK]) {
+#pragma unroll
+  for (int a = 0; a < RANK; ++a)
+#pragma unroll
+    for (int b = 0; b < RANK; ++b) T[a][b] = 0.0;
+#pragma unroll
+  for (int c = 0; c < RANK; ++c) {
+    double wv[RANK];
+#pragma unroll
+    for (int a = 0; a < RANK; ++a) wv[a] = a == c ? 1.0 : 0.0;
+#pragma unroll
+    for (int j = 0; j < c; ++j) {
+      double d = 0.0;  // (P T_j)^T (P wv) = T_j^T G wv
+#pragma unroll
+      for (int a = 0; a <= j; ++a) {
+        double gw = 0.0;
+#pragma unroll
+        for (int b = 0; b <= c; ++b) gw += G[a][b] * wv[b];
+        d += T[a][j] * gw;
+      }
+#pragma unroll
+      for (int a = 0; a <= j; ++a) wv[a] -= d * T[a][j];
+    }
+    double nrm2 = 0.0;
+#pragma unroll
+    for (int a = 0; a <= c; ++a) {
+      double gw = 0.0;
+#pragma unroll
+      for (int b = 0; b <= c; ++b) gw += G[a][b] * wv[b];
+      nrm2 += wv[a] * gw;
+    }
+    const double inv = nrm2 > 0.0 ? 1.0 / sqrt(nrm2) : 0.0;
+#pragma unroll
+    for (int a = 0; a <= c; ++a) T[a][c] = wv[a] * inv;
+  }
+}
+
+// Orthonormalise P: fixed-order sum of the block Gram partials, two Cholesky-QR rounds in
+// r x r space (one thread), then Pt = fp32(P T) with fp64 products.
+template <int RANK>
+__global__ __launch_bounds__(kBlockSolve) void k_lq_solve(const float *__restrict__ P,
+                                                          const double *__restrict__ gpart,
+                                                          int64_t nblocks, float *__restrict__ Pt,
+                                                          float *__restrict__ p_pre, int64_t n) {
   constexpr int NG = RANK * (RANK + 1) / 2;
-  __shared__ double red[kBlockOrth / 64][NG];
-  __shared__ double Gm[RANK][RANK];
-  __shared__ double T[RANK][RANK];
+  __shared__ double red[kBlockSolve / 64][NG];
+  __shared__ double Gs[RANK][RANK];
+  __shared__ double Ts[RANK][RANK];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int64_t i = tid; i < n * RANK; i += kBlockOrth) W[i] = (double)P[i];
+  double g[NG];
+#pragma unroll
+  for (int t = 0; t < NG; ++t) g[t] = 0.0;
+  for (int64_t b = tid; b < nblocks; b += kBlockSolve)
+#pragma unroll
+    for (int t = 0; t < NG; ++t) g[t] += gpart[b * NG + t];
+#pragma unroll
+  for (int t = 0; t < NG; ++t) {
+    const double s = wave_sum_d(g[t]);
+    if (lane == 0) red[w][t] = s;
+  }
   __syncthreads();
-  for (int round = 0; round < 2; ++round) {
-    double g[NG];
+  if (tid < NG) {
+    double s = 0.0;
+    for (int i = 0; i < kBlockSolve / 64; ++i) s += red[i][tid];
+    int a, b;
+    tri_index<RANK>(tid, a, b);
+    Gs[a][b] = s;
+    Gs[b][a] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double G[RANK][RANK], T1[RANK][RANK], T2[RANK][RANK];
 #pragma unroll
-    for (int t = 0; t < NG; ++t) g[t] = 0.0;
-    for (int64_t i = tid; i < n; i += kBlockOrth) {
-      double v[RANK];
+    for (int a = 0; a < RANK; ++a)
 #pragma unroll
-      for (int c = 0; c < RANK; ++c) v[c] = W[i * RANK + c];
-      int t = 0;
+      for (int b = 0; b < RANK; ++b) G[a][b] = Gs[a][b];
+    gram_schmidt_T<RANK>(G, T1);
+    // G <- T1^T G T1 (the Gram matrix of P T1), with T2 as scratch for G T1
 #pragma unroll
-      for (int a = 0; a < RANK; ++a)
-#pragma unroll
-        for (int b = a; b < RANK; ++b) g[t++] += v[a] * v[b];
-    }
-#pragma unroll
-    for (int t = 0; t < NG; ++t) {
-      const double s = wave_sum_d(g[t]);
-      if (lane == 0) red[w][t] = s;
-    }
-    __syncthreads();
-    if (tid < NG) {
-      double s = 0.0;
-      for (int i = 0; i < kBlockOrth / 64; ++i) s += red[i][tid];
-      int a = 0, t = tid;
-      while (t >= RANK - a) {
-        t -= RANK - a;
-        ++a;
-      }
-      const int b = a + t;
-      Gm[a][b] = s;
-      Gm[b][a] = s;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      for (int c = 0; c < RANK; ++c)
-        for (int a = 0; a < RANK; ++a) T[a][c] = 0.0;
-      for (int c = 0; c < RANK; ++c) {
-        double wv[RANK];
-        for (int a = 0; a < RANK; ++a) wv[a] = a == c ? 1.0 : 0.0;
-        for (int j = 0; j < c; ++j) {
-          // d = (P T_j)^T (P wv) = T_j^T G wv
-          double d = 0.0;
-          for (int a = 0; a <= j; ++a) {
-            double gw = 0.0;
-            for (int b = 0; b < RANK; ++b) gw += Gm[a][b] * wv[b];
-            d += T[a][j] * gw;
-          }
-          for (int a = 0; a <= j; ++a) wv[a] -= d * T[a][j];
-        }
-        double nrm2 = 0.0;
-        for (int a = 0; a < RANK; ++a) {
-          double gw = 0.0;
-          for (int b = 0; b < RANK; ++b) gw += Gm[a][b] * wv[b];
-          nrm2 += wv[a] * gw;
-        }
-        const double inv = nrm2 > 0.0 ? 1.0 / sqrt(nrm2) : 0.0;
-        for (int a = 0; a < RANK; ++a) T[a][c] = wv[a] * inv;
-      }
-    }
-    __syncthreads();
-    for (int64_t i = tid; i < n; i += kBlockOrth) {
-      double v[RANK], o[RANK];
-#pragma unroll
-      for (int c = 0; c < RANK; ++c) v[c] = W[i * RANK + c];
+    for (int a = 0; a < RANK; ++a)
 #pragma unroll
       for (int c = 0; c < RANK; ++c) {
         double s = 0.0;
 #pragma unroll
-        for (int a = 0; a <= c; ++a) s += v[a] * T[a][c];
-        o[c] = s;
+        for (int b = 0; b <= c; ++b) s += G[a][b] * T1[b][c];
+        T2[a][c] = s;
       }
 #pragma unroll
-      for (int c = 0; c < RANK; ++c) W[i * RANK + c] = o[c];
-    }
-    __syncthreads();
+    for (int a = 0; a < RANK; ++a)
+#pragma unroll
+      for (int c = 0; c < RANK; ++c) {
+        double s = 0.0;
+#pragma unroll
+        for (int b = 0; b <= a; ++b) s += T1[b][a] * T2[b][c];
+        G[a][c] = s;
+      }
+    gram_schmidt_T<RANK>(G, T2);
+#pragma unroll
+    for (int a = 0; a < RANK; ++a)
+#pragma unroll
+      for (int c = 0; c < RANK; ++c) {
+        double s = 0.0;
+#pragma unroll
+        for (int k = a; k <= c; ++k) s += T1[a][k] * T2[k][c];
+        Ts[a][c] = s;
+      }
   }
-  for (int64_t i = tid; i < n * RANK; i += kBlockOrth) {
-    const float v = (float)W[i];
-    Pt[i] = v;
-    if (p_pre) p_pre[i] = v;
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += kBlockSolve) {
+    double v[RANK];
+#pragma unroll
+    for (int c = 0; c < RANK; ++c) v[c] = (double)P[i * RANK + c];
+#pragma unroll
+    for (int c = 0; c < RANK; ++c) {
+      double s = 0.0;
+#pragma unroll
+      for (int a = 0; a <= c; ++a) s += v[a] * Ts[a][c];
+      const float o = (float)s;
+      Pt[i * RANK + c] = o;
+      if (p_pre) p_pre[i * RANK + c] = o;
+    }
   }
 }
 
-// Pass 2 (partials): part[chunk][j][c] = sum over the chunk's rows of E[row][j] * P[row][c].
+// Pass 2 (partials): part[chunk][j][c] = sum over the chunk's rows of E[row][j] * Pt[row][c].
 template <int RANK, int VEC>
 __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict__ M,
                                                          const float *__restrict__ Pt,
@@ -315,7 +376,6 @@ struct ColJob {
   float *colmax;         // r
   float *Fhat;           // rows x r or nullptr
   float *Fhat2;          // rows x r or nullptr (second copy)
-  float *Fhat_t;         // r x rows or nullptr (transposed copy)
 };
 
 // One block per column: max magnitude, then Eq. 5 encode by the boundary table and Eq. 6
@@ -359,15 +419,14 @@ __global__ __launch_bounds__(1024) void k_lq_quant_cols(ColJob j0, ColJob j1, in
     const float fh = x < 0.0f ? -v : v;
     if (J.Fhat) J.Fhat[i * J.r + c] = fh;
     if (J.Fhat2) J.Fhat2[i * J.r + c] = fh;
-    if (J.Fhat_t) J.Fhat_t[(int64_t)c * J.rows + i] = fh;
   }
 }
 
-// Pass 3: E <- E - Phat Qhat^T.
+// Pass 3: E <- E - Phat Qhat^T (Qhat row-major m x RANK).
 template <int RANK, int VEC>
 __global__ __launch_bounds__(kBlockA) void k_lq_ef_update(float *__restrict__ E,
                                                           const float *__restrict__ Ph,
-                                                          const float *__restrict__ Qht,
+                                                          const float *__restrict__ Qh,
                                                           int64_t n, int64_t m) {
   const int64_t row0 = (int64_t)blockIdx.x * kRowsA;
   float p[kRowsA][RANK];
@@ -377,8 +436,7 @@ __global__ __launch_bounds__(kBlockA) void k_lq_ef_update(float *__restrict__ E,
     for (int c = 0; c < RANK; ++c) p[rr][c] = row0 + rr < n ? Ph[(row0 + rr) * RANK + c] : 0.0f;
   for (int64_t j = (int64_t)threadIdx.x * VEC; j < m; j += (int64_t)kBlockA * VEC) {
     float q[RANK][VEC];
-#pragma unroll
-    for (int c = 0; c < RANK; ++c) ldv<VEC>(Qht + (int64_t)c * m + j, q[c]);
+    load_q_rows<RANK, VEC>(Qh, j, q);
 #pragma unroll
     for (int rr = 0; rr < kRowsA; ++rr) {
       const int64_t row = row0 + rr;
@@ -451,37 +509,40 @@ hipError_t tables(LqState &st, double alpha, int bits, hipStream_t s, const LqTa
   return hipSuccess;
 }
 
+struct StepBufs {
+  float *P, *Pt, *part, *Qn, *Ph;
+  double *gpart;
+  int nchunks;
+  int64_t nblocks;
+};
+
 template <int RANK, int VEC>
-void launch_step(const LqStepArgs &a, float *Qt, float *P, double *W, float *Pt, float *part,
-                 int nchunks, float *Qn, float *Ph, float *Qht, const LqTables &tab,
-                 hipStream_t s) {
+void launch_step(const LqStepArgs &a, const StepBufs &b, const LqTables &tab, hipStream_t s) {
   const int64_t n = a.n, m = a.m;
-  hipLaunchKernelGGL(k_lq_transpose, dim3((unsigned)((m * RANK + 255) / 256)), dim3(256), 0, s,
-                     a.Q, Qt, m, RANK);
-  hipLaunchKernelGGL((k_lq_ef_mq<RANK, VEC>), dim3((unsigned)((n + kRowsA - 1) / kRowsA)),
-                     dim3(kBlockA), 0, s, a.G, a.E, Qt, P, n, m);
-  hipLaunchKernelGGL((k_lq_orth<RANK>), dim3(1), dim3(kBlockOrth), 0, s, P, W, Pt, a.p_pre, n);
+  hipLaunchKernelGGL((k_lq_ef_mq<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA), 0, s,
+                     a.G, a.E, a.Q, b.P, b.gpart, n, m);
+  hipLaunchKernelGGL((k_lq_solve<RANK>), dim3(1), dim3(kBlockSolve), 0, s, b.P, b.gpart,
+                     b.nblocks, b.Pt, a.p_pre, n);
   hipLaunchKernelGGL((k_lq_mtp<RANK, VEC>),
-                     dim3((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)nchunks),
-                     dim3(kWavesC * 64), 0, s, a.E, Pt, part, n, m);
-  hipLaunchKernelGGL(k_lq_qsum, dim3((unsigned)((m * RANK + 255) / 256)), dim3(256), 0, s, part,
-                     Qn, a.q_pre, m * RANK, nchunks);
-  ColJob jp{Pt, n, RANK, a.p_codes, a.p_colmax, Ph, a.p_hat, nullptr};
-  ColJob jq{Qn, m, RANK, a.q_codes, a.q_colmax, a.Q, nullptr, Qht};
+                     dim3((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)b.nchunks),
+                     dim3(kWavesC * 64), 0, s, a.E, b.Pt, b.part, n, m);
+  hipLaunchKernelGGL(k_lq_qsum, dim3((unsigned)((m * RANK + 255) / 256)), dim3(256), 0, s,
+                     b.part, b.Qn, a.q_pre, m * RANK, b.nchunks);
+  ColJob jp{b.Pt, n, RANK, a.p_codes, a.p_colmax, b.Ph, a.p_hat};
+  ColJob jq{b.Qn, m, RANK, a.q_codes, a.q_colmax, a.Q, nullptr};
   hipLaunchKernelGGL(k_lq_quant_cols, dim3(2 * RANK), dim3(1024), 0, s, jp, jq, RANK, tab.dev,
                      tab.L);
-  hipLaunchKernelGGL((k_lq_ef_update<RANK, VEC>), dim3((unsigned)((n + kRowsA - 1) / kRowsA)),
-                     dim3(kBlockA), 0, s, a.E, Ph, Qht, n, m);
+  hipLaunchKernelGGL((k_lq_ef_update<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA), 0,
+                     s, a.E, b.Ph, a.Q, n, m);
 }
 
 template <int RANK>
-void launch_step_v(const LqStepArgs &a, bool vec4, float *Qt, float *P, double *W, float *Pt,
-                   float *part, int nchunks, float *Qn, float *Ph, float *Qht,
-                   const LqTables &tab, hipStream_t s) {
+void launch_step_v(const LqStepArgs &a, bool vec4, const StepBufs &b, const LqTables &tab,
+                   hipStream_t s) {
   if (vec4)
-    launch_step<RANK, 4>(a, Qt, P, W, Pt, part, nchunks, Qn, Ph, Qht, tab, s);
+    launch_step<RANK, 4>(a, b, tab, s);
   else
-    launch_step<RANK, 1>(a, Qt, P, W, Pt, part, nchunks, Qn, Ph, Qht, tab, s);
+    launch_step<RANK, 1>(a, b, tab, s);
 }
 
 }  // namespace
@@ -491,7 +552,7 @@ hipError_t lq_logquant(LqState &st, const float *F, int64_t rows, int r, double 
   const LqTables *tab = nullptr;
   hipError_t e = tables(st, alpha, bits, s, &tab);
   if (e != hipSuccess) return e;
-  ColJob j{F, rows, r, codes, colmax, Fhat, nullptr, nullptr};
+  ColJob j{F, rows, r, codes, colmax, Fhat, nullptr};
   hipLaunchKernelGGL(k_lq_quant_cols, dim3(r), dim3(1024), 0, s, j, j, r, tab->dev, tab->L);
   return hipGetLastError();
 }
@@ -501,37 +562,36 @@ hipError_t lq_step(LqState &st, const LqStepArgs &a, hipStream_t s) {
   hipError_t e = tables(st, a.alpha, a.bits, s, &tab);
   if (e != hipSuccess) return e;
   const int64_t n = a.n, m = a.m, r = a.r;
-  const int nchunks = (int)((n + kRowsC - 1) / kRowsC);
+  StepBufs b;
+  b.nchunks = (int)((n + kRowsC - 1) / kRowsC);
+  b.nblocks = (n + kRowsA - 1) / kRowsA;
+  const int64_t ng = r * (r + 1) / 2;
   size_t off = 0;
-  const size_t oQt = off; off += align256(sizeof(float) * r * m);
   const size_t oP = off; off += align256(sizeof(float) * n * r);
-  const size_t oW = off; off += align256(sizeof(double) * n * r);
+  const size_t oG = off; off += align256(sizeof(double) * b.nblocks * ng);
   const size_t oPt = off; off += align256(sizeof(float) * n * r);
-  const size_t oPart = off; off += align256(sizeof(float) * (size_t)nchunks * m * r);
+  const size_t oPart = off; off += align256(sizeof(float) * (size_t)b.nchunks * m * r);
   const size_t oQn = off; off += align256(sizeof(float) * m * r);
   const size_t oPh = off; off += align256(sizeof(float) * n * r);
-  const size_t oQht = off; off += align256(sizeof(float) * r * m);
   e = ensure(st, off, s);
   if (e != hipSuccess) return e;
   char *base = static_cast<char *>(st.scratch);
-  float *Qt = reinterpret_cast<float *>(base + oQt);
-  float *P = reinterpret_cast<float *>(base + oP);
-  double *W = reinterpret_cast<double *>(base + oW);
-  float *Pt = reinterpret_cast<float *>(base + oPt);
-  float *part = reinterpret_cast<float *>(base + oPart);
-  float *Qn = reinterpret_cast<float *>(base + oQn);
-  float *Ph = reinterpret_cast<float *>(base + oPh);
-  float *Qht = reinterpret_cast<float *>(base + oQht);
+  b.P = reinterpret_cast<float *>(base + oP);
+  b.gpart = reinterpret_cast<double *>(base + oG);
+  b.Pt = reinterpret_cast<float *>(base + oPt);
+  b.part = reinterpret_cast<float *>(base + oPart);
+  b.Qn = reinterpret_cast<float *>(base + oQn);
+  b.Ph = reinterpret_cast<float *>(base + oPh);
   const bool vec4 = (m % 4) == 0;
   switch (a.r) {
-    case 1: launch_step_v<1>(a, vec4, Qt, P, W, Pt, part, nchunks, Qn, Ph, Qht, *tab, s); break;
-    case 2: launch_step_v<2>(a, vec4, Qt, P, W, Pt, part, nchunks, Qn, Ph, Qht, *tab, s); break;
-    case 3: launch_step_v<3>(a, vec4, Qt, P, W, Pt, part, nchunks, Qn, Ph, Qht, *tab, s); break;
-    case 4: launch_step_v<4>(a, vec4, Qt, P, W, Pt, part, nchunks, Qn, Ph, Qht, *tab, s); break;
-    case 5: launch_step_v<5>(a, vec4, Qt, P, W, Pt, part, nchunks, Qn, Ph, Qht, *tab, s); break;
-    case 6: launch_step_v<6>(a, vec4, Qt, P, W, Pt, part, nchunks, Qn, Ph, Qht, *tab, s); break;
-    case 7: launch_step_v<7>(a, vec4, Qt, P, W, Pt, part, nchunks, Qn, Ph, Qht, *tab, s); break;
-    case 8: launch_step_v<8>(a, vec4, Qt, P, W, Pt, part, nchunks, Qn, Ph, Qht, *tab, s); break;
+    case 1: launch_step_v<1>(a, vec4, b, *tab, s); break;
+    case 2: launch_step_v<2>(a, vec4, b, *tab, s); break;
+    case 3: launch_step_v<3>(a, vec4, b, *tab, s); break;
+    case 4: launch_step_v<4>(a, vec4, b, *tab, s); break;
+    case 5: launch_step_v<5>(a, vec4, b, *tab, s); break;
+    case 6: launch_step_v<6>(a, vec4, b, *tab, s); break;
+    case 7: launch_step_v<7>(a, vec4, b, *tab, s); break;
+    case 8: launch_step_v<8>(a, vec4, b, *tab, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
