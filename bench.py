@@ -167,6 +167,31 @@ def rows_breakdown(torch, gq, W, grads, S, w, args):
     return rows
 
 
+def measure_ceilings(torch, grads, out):
+    """Bandwidth of a plain stream with the fused pass's memory pattern and with the norm
+    pass's (libgq_ceiling.so): K fp32 reads + 1 fp32 write, and K fp32 reads."""
+    import ctypes as C
+    from allreduce_compatible_gradient_amd import build as B
+    lib = C.CDLL(B.CEILING_LIB)
+    lib.gqc_stream.restype = C.c_int
+    lib.gqc_stream.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_void_p,
+                               C.c_void_p]
+    K, n = len(grads), grads[0].numel()
+    srcs = (C.c_void_p * K)(*[g.data_ptr() for g in grads])
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for name, o, nbytes in (("read_K%d_write1" % K, out.data_ptr(), (K + 1) * (n // 512) * 2048),
+                            ("read_K%d" % K, None, K * (n // 512) * 2048)):
+        def run():
+            assert lib.gqc_stream(srcs, K, n, o, sink.data_ptr(), stream) == 0
+        ms = time_calls(torch, run, 5)
+        res[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        log("ceiling %-22s %8.1f GB/s (%.1f%% of HBM)" % (name, res[name],
+                                                          100 * res[name] / HBM_PEAK_GBS))
+    return res
+
+
 def cpu_baseline(grads, w, sample):
     """The oracle, as it stands (one thread), on the first `sample` elements of each worker."""
     import numpy as np
@@ -283,6 +308,11 @@ def main():
         "kernels": {"global_norm_ms": round(norm_ms, 4), "fused_mean_ms": round(fused_ms, 4),
                     "global_norm_GBps": round(grad_bytes / norm_ms / 1e6, 1)},
     }
+    ceil = measure_ceilings(torch, grads, out)
+    result["measured_ceilings_GBps"] = ceil
+    result["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceil["read_K8_write1"], 4)
+    result["kernels"]["global_norm_frac_of_measured_ceiling"] = round(
+        grad_bytes / norm_ms / 1e6 / ceil["read_K8"], 4)
     if not args.no_rows:
         result["rows"] = rows_breakdown(torch, gq, W, grads, S, w, args)
     if not args.no_cpu_baseline:
