@@ -13,17 +13,21 @@
 //   pass 2  Q' = E^T Pt                         (read E)               k_lq_mtp + k_lq_qsum
 //   pass 3  E <- E - Phat Q'hat^T               (read E; write E)      k_lq_ef_update
 // Row passes give each block 4 rows so every Q value fetched (from L2: Q is at most
-// m x 8 fp32) is used 4 times; Q is read in its own row-major layout (a thread's 4 columns
-// are 4r consecutive floats), so no transposed copy is made.  The column pass gives each
+// m x 8 fp32) is used 4 times, and issue all of a column group's row loads before the first
+// store; Q is read in its own row-major layout (a thread's 4 columns are 4r consecutive
+// floats), so no transposed copy is made.  The column pass gives each
 // 512-thread block 128 rows x (64*VEC) columns and reduces its 8 waves in LDS, so the
 // per-chunk partials stay a few percent of the pass.
 // Orthonormalisation: pass 1 also emits each block's r x r Gram contribution (products of the
 // fp32 P values, exact in fp64); k_lq_solve sums them in a fixed order and runs Cholesky-QR
 // twice in r x r space -- T1 from G, then T2 from T1^T G T1, which measures and removes the
-// error of the first factorisation -- and applies T = T1 T2 to P.  In exact arithmetic P T is
-// the Gram-Schmidt Q factor of P (columns in order; a column with no remaining norm is zero).
-// The log quantiser encodes with a table of the L bin boundaries rounded up to fp32 (so
-// "y >= boundary" is decided exactly) and decodes with a table of the L+1 Eq. 6 levels.
+// error of the first factorisation -- and the column pass forms Pt = P T1 T2 tile by tile.  In exact
+// arithmetic P T is the Gram-Schmidt Q factor of P (columns in order; a column with no
+// remaining norm is zero).  The kernels that produce Pt and Q' also take their column maxima
+// (integer atomicMax on the bit patterns of |v|: exact and order-independent), so the log
+// quantiser runs element by element: it encodes with a table of the L bin boundaries rounded
+// up to fp32 (so "y >= boundary" is decided exactly) and decodes with a table of the L+1
+// Eq. 6 levels.
 #include <float.h>
 #include <math.h>
 
@@ -40,8 +44,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRowsA = 4;      // rows per block in the row passes
 constexpr int kBlockA = 256;
 constexpr int kRowsC = 128;    // rows per chunk in the column pass
-constexpr int kWavesC = 8;
-constexpr int kBlockSolve = 256;
+constexpr int kWavesC = 8;     // kRowsC / kWavesC rows per wave, all loaded at once
+// threads of the one-block solve: 16 waves, 8 at rank 8 (so that its r x r work fits in
+// registers)
+template <int RANK>
+constexpr int solve_block() { return RANK > 7 ? 512 : 1024; }
 
 template <int VEC>
 __device__ __forceinline__ void ldv_nt(const float *p, float (&v)[VEC]) {
@@ -115,7 +122,8 @@ __device__ __forceinline__ void tri_index(int t, int &a, int &b) {
 }
 
 // Pass 1: E <- G + E (the gradient with the previous error fed back), P = E Q, and the block's
-// share of the Gram matrix P^T P (packed upper triangle, fp64).
+// share of the Gram matrix P^T P (packed upper triangle, fp64, stored entry-major so that the
+// solve reads each entry's partials contiguously).
 template <int RANK, int VEC>
 __global__ __launch_bounds__(kBlockA) void k_lq_ef_mq(const float *__restrict__ G,
                                                       float *__restrict__ E,
@@ -132,19 +140,25 @@ __global__ __launch_bounds__(kBlockA) void k_lq_ef_mq(const float *__restrict__ 
   for (int rr = 0; rr < kRowsA; ++rr)
 #pragma unroll
     for (int c = 0; c < RANK; ++c) acc[rr][c] = 0.0f;
+  const int nr = n - row0 < kRowsA ? (int)(n - row0) : kRowsA;
   for (int64_t j = (int64_t)threadIdx.x * VEC; j < m; j += (int64_t)kBlockA * VEC) {
+    // every load of this column group is issued before the first store
+    float g[kRowsA][VEC], e[kRowsA][VEC];
+#pragma unroll
+    for (int rr = 0; rr < kRowsA; ++rr)
+      if (rr < nr) {
+        ldv_nt<VEC>(G + (row0 + rr) * m + j, g[rr]);
+        ldv_nt<VEC>(E + (row0 + rr) * m + j, e[rr]);
+      }
     float q[RANK][VEC];
     load_q_rows<RANK, VEC>(Q, j, q);
 #pragma unroll
     for (int rr = 0; rr < kRowsA; ++rr) {
-      const int64_t row = row0 + rr;
-      if (row < n) {
-        float g[VEC], e[VEC], mv[VEC];
-        ldv_nt<VEC>(G + row * m + j, g);
-        ldv_nt<VEC>(E + row * m + j, e);
+      if (rr < nr) {
+        float mv[VEC];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) mv[v] = g[v] + e[v];
-        stv<VEC>(E + row * m + j, mv);
+        for (int v = 0; v < VEC; ++v) mv[v] = g[rr][v] + e[rr][v];
+        stv<VEC>(E + (row0 + rr) * m + j, mv);
 #pragma unroll
         for (int c = 0; c < RANK; ++c)
 #pragma unroll
@@ -177,195 +191,290 @@ __global__ __launch_bounds__(kBlockA) void k_lq_ef_mq(const float *__restrict__ 
     double g = 0.0;
 #pragma unroll
     for (int rr = 0; rr < kRowsA; ++rr) g += (double)pv[rr * RANK + a] * (double)pv[rr * RANK + b];
-    gpart[(int64_t)blockIdx.x * NG + threadIdx.x] = g;
+    gpart[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = g;  // entry-major: [NG][nblocks]
   }
 }
 
-// Upper-triangular T with (P T)^T (P T) = I given G = P^T P: Gram-Schmidt carried out on G
-// (column c: remove its components along the previous orthonormal columns, then normalise;
-// a column with no remaining norm becomes zero).  RANK x RANK, in registers.
+// v from lane l (l a compile-time or wave-uniform index): two v_readlane_b32.
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = __builtin_amdgcn_readlane((unsigned)b, l);
+  const unsigned hi = __builtin_amdgcn_readlane((unsigned)(b >> 32), l);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Upper-triangular T with (P T)^T (P T) = I given G = P^T P, column by column as Gram-Schmidt
+// does it, through the Cholesky factor: G = R^T R (R upper triangular; a pivot that is not
+// positive marks a column with no remaining norm, whose row of R and column of T are zero),
+// then T[:, c] = (e_c - sum_{k<c} R[k][c] T[:, k]) / R[c][c].
+// Spread over the lanes of one wave: lane j (< RANK) holds column j of G (g[k] = G[k][j]),
+// of R and of T; the entries a step needs from another column are read from its lane with
+// v_readlane (uniform values).  Every entry is formed with the same operations in the same
+// order as the one-thread form of these formulas.
 template <int RANK>
-__device__ __forceinline__ void gram_schmidt_T(const double (&G)[RANK][RANK],
-                                               double (&T)[RANK][RANK]) {
+__device__ __forceinline__ void lane_gram_schmidt_T(const double (&g)[RANK], int j,
+                                                    double (&tcol)[RANK]) {
+  double rcol[RANK];  // R[k][j]
 #pragma unroll
-  for (int a = 0; a < RANK; ++a)
-#pragma unroll
-    for (int b = 0; b < RANK; ++b) T[a][b] = 0.0;
+  for (int k = 0; k < RANK; ++k) {
+    rcol[k] = 0.0;
+    tcol[k] = 0.0;
+  }
 #pragma unroll
   for (int c = 0; c < RANK; ++c) {
-    double wv[RANK];
+    double rkc[RANK > 1 ? RANK - 1 : 1];  // R[k][c], k < c
 #pragma unroll
-    for (int a = 0; a < RANK; ++a) wv[a] = a == c ? 1.0 : 0.0;
+    for (int k = 0; k < c; ++k) rkc[k] = readlane_d(rcol[k], c);
+    double d = readlane_d(g[c], c);  // G[c][c]
 #pragma unroll
-    for (int j = 0; j < c; ++j) {
-      double d = 0.0;  // (P T_j)^T (P wv) = T_j^T G wv
+    for (int k = 0; k < c; ++k) d -= rkc[k] * rkc[k];
+    if (d > 0.0) {  // the same value in every lane
+      const double rc = sqrt(d), inv = 1.0 / rc;
+      double v = g[c];  // G[c][j]
 #pragma unroll
-      for (int a = 0; a <= j; ++a) {
-        double gw = 0.0;
+      for (int k = 0; k < c; ++k) v -= rkc[k] * rcol[k];
+      if (j > c) rcol[c] = v * inv;
+      if (j == c) rcol[c] = rc;
+      // column c of T (uniform values; lane c keeps them)
 #pragma unroll
-        for (int b = 0; b <= c; ++b) gw += G[a][b] * wv[b];
-        d += T[a][j] * gw;
+      for (int a = 0; a <= c; ++a) {
+        double u = a == c ? 1.0 : 0.0;
+#pragma unroll
+        for (int k = a; k < c; ++k) u -= rkc[k] * readlane_d(tcol[a], k);  // T[a][k], a <= k
+        if (j == c) tcol[a] = u * inv;
       }
-#pragma unroll
-      for (int a = 0; a <= j; ++a) wv[a] -= d * T[a][j];
     }
-    double nrm2 = 0.0;
-#pragma unroll
-    for (int a = 0; a <= c; ++a) {
-      double gw = 0.0;
-#pragma unroll
-      for (int b = 0; b <= c; ++b) gw += G[a][b] * wv[b];
-      nrm2 += wv[a] * gw;
-    }
-    const double inv = nrm2 > 0.0 ? 1.0 / sqrt(nrm2) : 0.0;
-#pragma unroll
-    for (int a = 0; a <= c; ++a) T[a][c] = wv[a] * inv;
   }
 }
 
-// Orthonormalise P: fixed-order sum of the block Gram partials, two Cholesky-QR rounds in
-// r x r space (one thread), then Pt = fp32(P T) with fp64 products.
+// Orthonormalise P (r x r part): fixed-order sum of the block Gram partials, then two
+// Cholesky-QR rounds in r x r space (lane-parallel in one wave) giving T = T1 T2.
 template <int RANK>
-__global__ __launch_bounds__(kBlockSolve) void k_lq_solve(const float *__restrict__ P,
-                                                          const double *__restrict__ gpart,
-                                                          int64_t nblocks, float *__restrict__ Pt,
-                                                          float *__restrict__ p_pre, int64_t n) {
+__global__ __launch_bounds__(solve_block<RANK>()) void k_lq_solve(const double *__restrict__ gpart,
+                                                          int64_t nblocks,
+                                                          double *__restrict__ Tout,
+                                                          unsigned *__restrict__ cmax_bits) {
   constexpr int NG = RANK * (RANK + 1) / 2;
-  __shared__ double red[kBlockSolve / 64][NG];
   __shared__ double Gs[RANK][RANK];
-  __shared__ double Ts[RANK][RANK];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  double g[NG];
+  if (tid < 2 * RANK) cmax_bits[tid] = 0u;  // column maxima of Pt and Q' start at +0
+  // wave w sums entries t = w, w + NW, ...: lane l adds blocks l, l + 64, ... in order, UB
+  // loads per entry issued together, then the lanes are combined in a fixed butterfly
+  constexpr int NW = solve_block<RANK>() / 64, TE = (NG + NW - 1) / NW, UB = TE > 2 ? 8 : 16;
+  double acc[TE];
 #pragma unroll
-  for (int t = 0; t < NG; ++t) g[t] = 0.0;
-  for (int64_t b = tid; b < nblocks; b += kBlockSolve)
+  for (int e = 0; e < TE; ++e) acc[e] = 0.0;
+  for (int64_t b0 = lane; b0 < nblocks; b0 += UB * 64) {
+    double v[TE][UB];
 #pragma unroll
-    for (int t = 0; t < NG; ++t) g[t] += gpart[b * NG + t];
+    for (int e = 0; e < TE; ++e) {
+      const int t = w + e * NW;
 #pragma unroll
-  for (int t = 0; t < NG; ++t) {
-    const double s = wave_sum_d(g[t]);
-    if (lane == 0) red[w][t] = s;
+      for (int u = 0; u < UB; ++u) {
+        const int64_t b = b0 + (int64_t)u * 64;
+        v[e][u] = (t < NG && b < nblocks) ? gpart[(int64_t)t * nblocks + b] : 0.0;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < TE; ++e)
+#pragma unroll
+      for (int u = 0; u < UB; ++u) acc[e] += v[e][u];
+  }
+#pragma unroll
+  for (int e = 0; e < TE; ++e) {
+    const int t = w + e * NW;
+    const double sum = wave_sum_d(acc[e]);
+    if (t < NG && lane == 0) {
+      int a, b;
+      tri_index<RANK>(t, a, b);
+      Gs[a][b] = sum;
+      Gs[b][a] = sum;
+    }
   }
   __syncthreads();
-  if (tid < NG) {
-    double s = 0.0;
-    for (int i = 0; i < kBlockSolve / 64; ++i) s += red[i][tid];
-    int a, b;
-    tri_index<RANK>(tid, a, b);
-    Gs[a][b] = s;
-    Gs[b][a] = s;
+  // r x r part in wave 0 (lane j < RANK owns column j; lanes beyond compute lane 0's values)
+  if (w != 0) return;
+  const int jc = lane < RANK ? lane : 0;
+  double g[RANK], t1[RANK], t2[RANK], gt[RANK];
+#pragma unroll
+  for (int k = 0; k < RANK; ++k) g[k] = Gs[k][jc];
+  lane_gram_schmidt_T<RANK>(g, jc, t1);
+  // column jc of G T1: entry x sums G[x][b] T1[b][jc] over b <= jc (G[x][b] = g[x] of lane b)
+#pragma unroll
+  for (int x = 0; x < RANK; ++x) {
+    double sum = 0.0;
+#pragma unroll
+    for (int b = 0; b < RANK; ++b) {
+      const double gxb = readlane_d(g[x], b);
+      if (b <= jc) sum += gxb * t1[b];
+    }
+    gt[x] = sum;
   }
-  __syncthreads();
-  if (tid == 0) {
-    double G[RANK][RANK], T1[RANK][RANK], T2[RANK][RANK];
+  // column jc of T1^T G T1 (the Gram matrix of P T1): entry c sums T1[b][c] (G T1)[b][jc]
+  // over b <= c
 #pragma unroll
-    for (int a = 0; a < RANK; ++a)
+  for (int c = 0; c < RANK; ++c) {
+    double sum = 0.0;
 #pragma unroll
-      for (int b = 0; b < RANK; ++b) G[a][b] = Gs[a][b];
-    gram_schmidt_T<RANK>(G, T1);
-    // G <- T1^T G T1 (the Gram matrix of P T1), with T2 as scratch for G T1
-#pragma unroll
-    for (int a = 0; a < RANK; ++a)
-#pragma unroll
-      for (int c = 0; c < RANK; ++c) {
-        double s = 0.0;
-#pragma unroll
-        for (int b = 0; b <= c; ++b) s += G[a][b] * T1[b][c];
-        T2[a][c] = s;
-      }
-#pragma unroll
-    for (int a = 0; a < RANK; ++a)
-#pragma unroll
-      for (int c = 0; c < RANK; ++c) {
-        double s = 0.0;
-#pragma unroll
-        for (int b = 0; b <= a; ++b) s += T1[b][a] * T2[b][c];
-        G[a][c] = s;
-      }
-    gram_schmidt_T<RANK>(G, T2);
-#pragma unroll
-    for (int a = 0; a < RANK; ++a)
-#pragma unroll
-      for (int c = 0; c < RANK; ++c) {
-        double s = 0.0;
-#pragma unroll
-        for (int k = a; k <= c; ++k) s += T1[a][k] * T2[k][c];
-        Ts[a][c] = s;
-      }
+    for (int b = 0; b <= c; ++b) sum += readlane_d(t1[b], c) * gt[b];
+    g[c] = sum;
   }
-  __syncthreads();
-  for (int64_t i = tid; i < n; i += kBlockSolve) {
-    double v[RANK];
+  lane_gram_schmidt_T<RANK>(g, jc, t2);
+  // column jc of T = T1 T2: entry a sums T1[a][k] T2[k][jc] over a <= k <= jc
+  if (lane < RANK) {
 #pragma unroll
-    for (int c = 0; c < RANK; ++c) v[c] = (double)P[i * RANK + c];
+    for (int a = 0; a < RANK; ++a) {
+      double sum = 0.0;
 #pragma unroll
-    for (int c = 0; c < RANK; ++c) {
-      double s = 0.0;
-#pragma unroll
-      for (int a = 0; a <= c; ++a) s += v[a] * Ts[a][c];
-      const float o = (float)s;
-      Pt[i * RANK + c] = o;
-      if (p_pre) p_pre[i * RANK + c] = o;
+      for (int k = a; k < RANK; ++k) {
+        const double t1ak = readlane_d(t1[a], k);
+        if (k <= jc) sum += t1ak * t2[k];
+      }
+      Tout[a * RANK + jc] = sum;
     }
   }
 }
 
 // Pass 2 (partials): part[chunk][j][c] = sum over the chunk's rows of E[row][j] * Pt[row][c].
+// Each block first forms its chunk's rows of Pt = fp32(P T) (fp64 products) in LDS; the blocks
+// of the first column tile also store them (Pt for the quantiser, the optional p_pre copy)
+// and take the column maxima of Pt: the bit patterns of non-negative floats order like
+// unsigned integers, so integer atomicMax (in LDS per block, then once per column in memory)
+// is the exact, order-independent maximum.  Wave w takes rows w, w + 8, ... of the chunk,
+// loaded 8 at a time; the 8 waves' sums are combined in LDS in wave order in one round and
+// written as contiguous (j, c) runs.
 template <int RANK, int VEC>
 __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict__ M,
-                                                         const float *__restrict__ Pt,
+                                                         const float *__restrict__ P,
+                                                         const double *__restrict__ T,
+                                                         float *__restrict__ Pt,
+                                                         float *__restrict__ p_pre,
+                                                         unsigned *__restrict__ cmax_bits,
                                                          float *__restrict__ part, int64_t n,
                                                          int64_t m) {
-  __shared__ float red[kWavesC][64 * VEC];
+  constexpr int RW = kRowsC / kWavesC;  // rows per wave
+  constexpr int RB = 8;                 // rows per load batch
+  constexpr int COLS = 64 * VEC;        // columns per block
+  __shared__ float red[kWavesC][COLS * RANK];
+  __shared__ float ptile[kRowsC * RANK];
+  __shared__ unsigned smax[RANK];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t j = (int64_t)blockIdx.x * 64 * VEC + (int64_t)lane * VEC;
+  const int64_t j0 = (int64_t)blockIdx.x * COLS;
+  const int64_t j = j0 + (int64_t)lane * VEC;
   const int64_t r0 = (int64_t)blockIdx.y * kRowsC;
   const int64_t r1 = r0 + kRowsC < n ? r0 + kRowsC : n;
-  const bool active = j < m;
+  const bool first_tile = blockIdx.x == 0;
+  float mv[RB][VEC];
+  // the first batch of rows is in flight while the Pt tile is formed
+#pragma unroll
+  for (int u = 0; u < RB; ++u) {
+    const int64_t row = r0 + w + (int64_t)u * kWavesC;
+    if (j < m && row < r1) {
+      ldv_nt<VEC>(M + row * m + j, mv[u]);
+    } else {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) mv[u][v] = 0.0f;
+    }
+  }
+  if (first_tile && threadIdx.x < RANK) smax[threadIdx.x] = 0u;
+  __syncthreads();
+  for (int e = threadIdx.x; e < kRowsC * RANK; e += kWavesC * 64) {
+    const int64_t row = r0 + e / RANK;
+    const int c = e % RANK;
+    float o = 0.0f;
+    if (row < r1) {
+      double sum = 0.0;
+      for (int a = 0; a <= c; ++a) sum += (double)P[row * RANK + a] * T[a * RANK + c];
+      o = (float)sum;
+      if (first_tile) {
+        Pt[row * RANK + c] = o;
+        if (p_pre) p_pre[row * RANK + c] = o;
+        atomicMax(&smax[c], __float_as_uint(fabsf(o)));
+      }
+    }
+    ptile[e] = o;
+  }
+  __syncthreads();
+  if (first_tile && threadIdx.x < RANK) atomicMax(&cmax_bits[threadIdx.x], smax[threadIdx.x]);
   float acc[VEC][RANK];
 #pragma unroll
   for (int v = 0; v < VEC; ++v)
 #pragma unroll
     for (int c = 0; c < RANK; ++c) acc[v][c] = 0.0f;
-  if (active) {
-    for (int64_t row = r0 + w; row < r1; row += kWavesC) {
-      float p[RANK], mv[VEC];
+  if (j < m) {
+#pragma unroll 1
+    for (int u0 = 0; u0 < RW; u0 += RB) {
+      if (u0 > 0) {
 #pragma unroll
-      for (int c = 0; c < RANK; ++c) p[c] = Pt[row * RANK + c];
-      ldv_nt<VEC>(M + row * m + j, mv);
+        for (int u = 0; u < RB; ++u) {
+          const int64_t row = r0 + w + (int64_t)(u0 + u) * kWavesC;
+          if (row < r1) {
+            ldv_nt<VEC>(M + row * m + j, mv[u]);
+          } else {
 #pragma unroll
-      for (int v = 0; v < VEC; ++v)
+            for (int v = 0; v < VEC; ++v) mv[u][v] = 0.0f;
+          }
+        }
+      }
 #pragma unroll
-        for (int c = 0; c < RANK; ++c) acc[v][c] = fmaf(mv[v], p[c], acc[v][c]);
+      for (int u = 0; u < RB; ++u) {
+        const int64_t row = r0 + w + (int64_t)(u0 + u) * kWavesC;
+        if (row < r1) {
+          const int lr = w + (u0 + u) * kWavesC;
+          float p[RANK];
+#pragma unroll
+          for (int c = 0; c < RANK; ++c) p[c] = ptile[lr * RANK + c];
+#pragma unroll
+          for (int v = 0; v < VEC; ++v)
+#pragma unroll
+            for (int c = 0; c < RANK; ++c) acc[v][c] = fmaf(mv[u][v], p[c], acc[v][c]);
+        }
+      }
     }
   }
 #pragma unroll
-  for (int c = 0; c < RANK; ++c) {
+  for (int v = 0; v < VEC; ++v)
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) red[w][lane * VEC + v] = acc[v][c];
-    __syncthreads();
-    if (w == 0 && active) {
+    for (int c = 0; c < RANK; ++c) red[w][(lane * VEC + v) * RANK + c] = acc[v][c];
+  __syncthreads();
+  const int64_t ncols = m - j0 < COLS ? m - j0 : COLS;
+  float *dst = part + ((int64_t)blockIdx.y * m + j0) * RANK;
+  for (int o = threadIdx.x; o < ncols * RANK; o += kWavesC * 64) {
+    float s = 0.0f;
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        float s = 0.0f;
-        for (int i = 0; i < kWavesC; ++i) s += red[i][lane * VEC + v];
-        part[((int64_t)blockIdx.y * m + j + v) * RANK + c] = s;
-      }
-    }
-    __syncthreads();
+    for (int i = 0; i < kWavesC; ++i) s += red[i][o];
+    dst[o] = s;
   }
 }
 
-// Pass 2 (final): Q'[j][c] = sum over chunks, in chunk order.
-__global__ void k_lq_qsum(const float *part, float *Qn, float *q_pre, int64_t count,
-                          int nchunks) {
+// Pass 2 (final): Q'[j][c] = sum over chunks, in chunk order (loads issued 8 chunks at a
+// time), and the column maxima of Q' (as for Pt in k_lq_mtp).
+template <int RANK>
+__global__ __launch_bounds__(256) void k_lq_qsum(const float *__restrict__ part,
+                                                 float *__restrict__ Qn, float *__restrict__ q_pre,
+                                                 unsigned *__restrict__ cmax_bits, int64_t count,
+                                                 int nchunks) {
+  __shared__ unsigned smax[RANK];
+  if (threadIdx.x < RANK) smax[threadIdx.x] = 0u;
+  __syncthreads();
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) {
     float s = 0.0f;
-    for (int ch = 0; ch < nchunks; ++ch) s += part[(int64_t)ch * count + i];
+    for (int ch0 = 0; ch0 < nchunks; ch0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = ch0 + u < nchunks ? part[(int64_t)(ch0 + u) * count + i] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (ch0 + u < nchunks) s += v[u];
+    }
     Qn[i] = s;
     if (q_pre) q_pre[i] = s;
+    atomicMax(&smax[i % RANK], __float_as_uint(fabsf(s)));
   }
+  __syncthreads();
+  if (threadIdx.x < RANK) atomicMax(&cmax_bits[threadIdx.x], smax[threadIdx.x]);
 }
 
 struct ColJob {
@@ -422,6 +531,65 @@ __global__ __launch_bounds__(1024) void k_lq_quant_cols(ColJob j0, ColJob j1, in
   }
 }
 
+// Log-quantise both factors element by element, the column maxima already known (cmax_bits:
+// RANK words for Pt, then RANK for Q').  Same encode/decode as k_lq_quant_cols.
+struct ElemJob {
+  const float *Pt;       // n x r
+  const float *Qn;       // m x r
+  int64_t n, m;
+  int r;
+  const unsigned *cmax_bits;
+  int8_t *p_codes, *q_codes;
+  float *p_colmax, *q_colmax;
+  float *Ph, *p_hat;     // decoded P (scratch) and the optional output copy
+  float *Qh;             // decoded Q (written into Q)
+};
+
+__global__ __launch_bounds__(256) void k_lq_quant_elems(ElemJob J, const float *tab, int L) {
+  __shared__ float thr[128];
+  __shared__ float lvl[128];
+  const int tid = threadIdx.x;
+  if (tid < L) thr[tid] = tab[tid];
+  if (tid <= L) lvl[tid] = tab[L + tid];
+  __syncthreads();
+  const int64_t np = J.n * J.r, nq = J.m * J.r;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + tid;
+  if (blockIdx.x == 0 && tid < 2 * J.r) {
+    const float mxv = __uint_as_float(J.cmax_bits[tid]);
+    if (tid < J.r) J.p_colmax[tid] = mxv; else J.q_colmax[tid - J.r] = mxv;
+  }
+  if (e >= np + nq) return;
+  const bool isp = e < np;
+  const int64_t i = isp ? e : e - np;
+  const int c = (int)(i % J.r);
+  const float x = isp ? J.Pt[i] : J.Qn[i];
+  const float mx = __uint_as_float(J.cmax_bits[isp ? c : J.r + c]);
+  int k = 0;
+  if (mx > 0.0f) {
+    const float y = fabsf(x) / mx;  // IEEE division, in [0, 1]
+    int lo = 0, hi = L;             // k = #{boundaries <= y}
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (thr[mid] <= y)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    k = lo;
+  }
+  const int8_t code = (int8_t)(x < 0.0f ? -k : k);
+  const float v = lvl[k] * mx;
+  const float fh = x < 0.0f ? -v : v;
+  if (isp) {
+    J.p_codes[i] = code;
+    J.Ph[i] = fh;
+    if (J.p_hat) J.p_hat[i] = fh;
+  } else {
+    J.q_codes[i] = code;
+    J.Qh[i] = fh;
+  }
+}
+
 // Pass 3: E <- E - Phat Qhat^T (Qhat row-major m x RANK).
 template <int RANK, int VEC>
 __global__ __launch_bounds__(kBlockA) void k_lq_ef_update(float *__restrict__ E,
@@ -434,23 +602,25 @@ __global__ __launch_bounds__(kBlockA) void k_lq_ef_update(float *__restrict__ E,
   for (int rr = 0; rr < kRowsA; ++rr)
 #pragma unroll
     for (int c = 0; c < RANK; ++c) p[rr][c] = row0 + rr < n ? Ph[(row0 + rr) * RANK + c] : 0.0f;
+  const int nr = n - row0 < kRowsA ? (int)(n - row0) : kRowsA;
   for (int64_t j = (int64_t)threadIdx.x * VEC; j < m; j += (int64_t)kBlockA * VEC) {
     float q[RANK][VEC];
+    float mv[kRowsA][VEC];
+#pragma unroll
+    for (int rr = 0; rr < kRowsA; ++rr)
+      if (rr < nr) ldv_nt<VEC>(E + (row0 + rr) * m + j, mv[rr]);
     load_q_rows<RANK, VEC>(Qh, j, q);
 #pragma unroll
     for (int rr = 0; rr < kRowsA; ++rr) {
-      const int64_t row = row0 + rr;
-      if (row < n) {
-        float mv[VEC];
-        ldv_nt<VEC>(E + row * m + j, mv);
+      if (rr < nr) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
           float s = 0.0f;
 #pragma unroll
           for (int c = 0; c < RANK; ++c) s = fmaf(p[rr][c], q[c][v], s);
-          mv[v] -= s;
+          mv[rr][v] -= s;
         }
-        stv<VEC>(E + row * m + j, mv);
+        stv<VEC>(E + (row0 + rr) * m + j, mv[rr]);
       }
     }
   }
@@ -511,7 +681,8 @@ hipError_t tables(LqState &st, double alpha, int bits, hipStream_t s, const LqTa
 
 struct StepBufs {
   float *P, *Pt, *part, *Qn, *Ph;
-  double *gpart;
+  double *gpart, *T;
+  unsigned *cmax_bits;
   int nchunks;
   int64_t nblocks;
 };
@@ -521,17 +692,18 @@ void launch_step(const LqStepArgs &a, const StepBufs &b, const LqTables &tab, hi
   const int64_t n = a.n, m = a.m;
   hipLaunchKernelGGL((k_lq_ef_mq<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA), 0, s,
                      a.G, a.E, a.Q, b.P, b.gpart, n, m);
-  hipLaunchKernelGGL((k_lq_solve<RANK>), dim3(1), dim3(kBlockSolve), 0, s, b.P, b.gpart,
-                     b.nblocks, b.Pt, a.p_pre, n);
+  hipLaunchKernelGGL((k_lq_solve<RANK>), dim3(1), dim3(solve_block<RANK>()), 0, s, b.gpart, b.nblocks,
+                     b.T, b.cmax_bits);
   hipLaunchKernelGGL((k_lq_mtp<RANK, VEC>),
                      dim3((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)b.nchunks),
-                     dim3(kWavesC * 64), 0, s, a.E, b.Pt, b.part, n, m);
-  hipLaunchKernelGGL(k_lq_qsum, dim3((unsigned)((m * RANK + 255) / 256)), dim3(256), 0, s,
-                     b.part, b.Qn, a.q_pre, m * RANK, b.nchunks);
-  ColJob jp{b.Pt, n, RANK, a.p_codes, a.p_colmax, b.Ph, a.p_hat};
-  ColJob jq{b.Qn, m, RANK, a.q_codes, a.q_colmax, a.Q, nullptr};
-  hipLaunchKernelGGL(k_lq_quant_cols, dim3(2 * RANK), dim3(1024), 0, s, jp, jq, RANK, tab.dev,
-                     tab.L);
+                     dim3(kWavesC * 64), 0, s, a.E, b.P, b.T, b.Pt, a.p_pre, b.cmax_bits, b.part,
+                     n, m);
+  hipLaunchKernelGGL((k_lq_qsum<RANK>), dim3((unsigned)((m * RANK + 255) / 256)), dim3(256), 0,
+                     s, b.part, b.Qn, a.q_pre, b.cmax_bits + RANK, m * RANK, b.nchunks);
+  ElemJob je{b.Pt, b.Qn, n, m, RANK, b.cmax_bits, a.p_codes, a.q_codes, a.p_colmax, a.q_colmax,
+             b.Ph, a.p_hat, a.Q};
+  hipLaunchKernelGGL(k_lq_quant_elems, dim3((unsigned)(((n + m) * RANK + 255) / 256)),
+                     dim3(256), 0, s, je, tab.dev, tab.L);
   hipLaunchKernelGGL((k_lq_ef_update<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA), 0,
                      s, a.E, b.Ph, a.Q, n, m);
 }
@@ -573,6 +745,8 @@ hipError_t lq_step(LqState &st, const LqStepArgs &a, hipStream_t s) {
   const size_t oPart = off; off += align256(sizeof(float) * (size_t)b.nchunks * m * r);
   const size_t oQn = off; off += align256(sizeof(float) * m * r);
   const size_t oPh = off; off += align256(sizeof(float) * n * r);
+  const size_t oT = off; off += align256(sizeof(double) * r * r);
+  const size_t oC = off; off += align256(sizeof(unsigned) * 2 * r);
   e = ensure(st, off, s);
   if (e != hipSuccess) return e;
   char *base = static_cast<char *>(st.scratch);
@@ -582,6 +756,8 @@ hipError_t lq_step(LqState &st, const LqStepArgs &a, hipStream_t s) {
   b.part = reinterpret_cast<float *>(base + oPart);
   b.Qn = reinterpret_cast<float *>(base + oQn);
   b.Ph = reinterpret_cast<float *>(base + oPh);
+  b.T = reinterpret_cast<double *>(base + oT);
+  b.cmax_bits = reinterpret_cast<unsigned *>(base + oC);
   const bool vec4 = (m % 4) == 0;
   switch (a.r) {
     case 1: launch_step_v<1>(a, vec4, b, *tab, s); break;

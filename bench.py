@@ -86,7 +86,10 @@ def time_calls(torch, fn, iters, warmup=1):
     return t.mean_ms()
 
 
-def rows_breakdown(torch, gq, W, grads, S, w, args):
+ROW_GROUPS = ("flat-1.3G-steps", "resnet50", "gpt2", "lq-4096x4096", "lq-4096x11008")
+
+
+def rows_breakdown(torch, gq, W, grads, S, w, args, groups=ROW_GROUPS):
     """Each step of the path timed on its own, with its algorithmic bytes."""
     rows = {}
     n, K = w.n, w.K
@@ -99,7 +102,23 @@ def rows_breakdown(torch, gq, W, grads, S, w, args):
         log("row %-28s %9.3f ms %8.1f GB/s (%.1f%% of HBM)" % (name, ms, gbs,
                                                                 100 * gbs / HBM_PEAK_GBS))
 
-    # per-worker quantise + pack, accumulate, dequantize, parity-mode fused on the same bucket
+    if "flat-1.3G-steps" in groups:
+        rows_flat(torch, gq, grads, S, w, row, it)
+    if "resnet50" in groups:
+        rows_resnet50(torch, gq, W, row)
+    if "gpt2" in groups:
+        rows_gpt2(torch, gq, W, row)
+    for shape in W.LQ_SHAPES:
+        if "lq-%dx%d" % shape in groups:
+            rows_lq(torch, gq, W, shape, row)
+    torch.cuda.empty_cache()
+    return rows
+
+
+def rows_flat(torch, gq, grads, S, w, row, it):
+    """Per-worker quantise + pack, accumulate, dequantize, parity-mode fused on the 1.3e9
+    bucket."""
+    n, K = w.n, w.K
     codes = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(K)]
     ms = time_calls(torch, lambda: gq.quantize_pack(grads[0], S, w.grid, w.levels, w.bits, 1, 0,
                                                     codes=codes[0]), it)
@@ -120,7 +139,9 @@ def rows_breakdown(torch, gq, W, grads, S, w, args):
     del codes, sums, out
     torch.cuda.empty_cache()
 
-    # exponential grid, 161 ResNet-50 segments
+
+def rows_resnet50(torch, gq, W, row):
+    """Exponential grid, 161 ResNet-50 segments."""
     w2 = W.get("resnet50-161t-f32-K8-exp7")
     g2 = W.gradients(w2, "cuda")
     S2, _ = gq.global_norm(g2, w2.offsets)
@@ -138,7 +159,9 @@ def rows_breakdown(torch, gq, W, grads, S, w, args):
     del g2, o2, c2
     torch.cuda.empty_cache()
 
-    # bf16, 9 GPT-2 buckets, K = 16
+
+def rows_gpt2(torch, gq, W, row):
+    """bf16, 9 GPT-2 buckets, K = 16."""
     w3 = W.get("gpt2s-148t-bf16-K16-uniform7")
     g3 = W.gradients(w3, "cuda")
     S3, _ = gq.global_norm(g3, w3.offsets)
@@ -151,20 +174,21 @@ def rows_breakdown(torch, gq, W, grads, S, w, args):
     del g3, o3
     torch.cuda.empty_cache()
 
-    # LQ-SGD step on the largest shape
-    for (n5, m5) in W.LQ_SHAPES:
-        for r5 in (1, 7):
-            G, Q0 = W.lq_problem(n5, m5, r5, 0, "cuda")
-            E = torch.zeros_like(G)
-            Q = Q0.clone()
-            o5 = {}
-            ms = time_calls(torch, lambda: gq.powersgd_logquant(G, E, Q, W.LQ_ALPHA, W.LQ_BITS,
-                                                                out=o5), 5)
-            row("lq_step_%dx%d_r%d" % (n5, m5, r5), ms, 6 * n5 * m5 * 4,
-                "G read, E read+write, E read, E read+write")
-            del G, E, Q
-    torch.cuda.empty_cache()
-    return rows
+
+def rows_lq(torch, gq, W, shape, row):
+    """One LQ-SGD step at ranks 1, 4 and 7."""
+    n5, m5 = shape
+    for r5 in W.LQ_RANKS:
+        G, Q0 = W.lq_problem(n5, m5, r5, 0, "cuda")
+        E = torch.zeros_like(G)
+        Q = Q0.clone()
+        o5 = {"p_hat": torch.empty(n5, r5, dtype=torch.float32, device="cuda")}
+        o5 = gq.powersgd_logquant(G, E, Q, W.LQ_ALPHA, W.LQ_BITS, out=o5)
+        ms = time_calls(torch, lambda: gq.powersgd_logquant(G, E, Q, W.LQ_ALPHA, W.LQ_BITS,
+                                                            out=o5), 5)
+        row("lq_step_%dx%d_r%d" % (n5, m5, r5), ms, 6 * n5 * m5 * 4,
+            "G read, E read+write, E read, E read+write")
+        del G, E, Q
 
 
 def measure_ceilings(torch, grads, out):
@@ -175,20 +199,25 @@ def measure_ceilings(torch, grads, out):
     lib = C.CDLL(B.CEILING_LIB)
     lib.gqc_stream.restype = C.c_int
     lib.gqc_stream.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_void_p,
-                               C.c_void_p]
+                               C.c_int, C.c_int, C.c_void_p]
     K, n = len(grads), grads[0].numel()
     srcs = (C.c_void_p * K)(*[g.data_ptr() for g in grads])
     sink = torch.zeros(4, dtype=torch.float32, device="cuda")
     stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
     res = {}
-    for name, o, nbytes in (("read_K%d_write1" % K, out.data_ptr(), (K + 1) * (n // 512) * 2048),
-                            ("read_K%d" % K, None, K * (n // 512) * 2048)):
-        def run():
-            assert lib.gqc_stream(srcs, K, n, o, sink.data_ptr(), stream) == 0
-        ms = time_calls(torch, run, 5)
-        res[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
-        log("ceiling %-22s %8.1f GB/s (%.1f%% of HBM)" % (name, res[name],
-                                                          100 * res[name] / HBM_PEAK_GBS))
+    for name, o, nbytes in (("read_K%d_write1" % K, out.data_ptr(), (K + 1) * (n // 2048) * 8192),
+                            ("read_K%d" % K, None, K * (n // 2048) * 8192)):
+        best = 0.0
+        for grid in (1024, 2048, 4096, 8192, 16384):
+            for chunk in (1, 2, 4):
+                def run():
+                    assert lib.gqc_stream(srcs, K, n, o, sink.data_ptr(), grid, chunk,
+                                          stream) == 0
+                ms = time_calls(torch, run, 3)
+                best = max(best, nbytes / (ms * 1e-3) / 1e9)
+        res[name] = round(best, 1)
+        log("ceiling %-22s %8.1f GB/s (%.1f%% of HBM), best of 15 launch shapes"
+            % (name, res[name], 100 * res[name] / HBM_PEAK_GBS))
     return res
 
 
@@ -217,6 +246,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 26)
+    ap.add_argument("--rows-only", choices=ROW_GROUPS, default=None,
+                    help="time only this group of rows (no headline step, no CPU baseline): "
+                         "one workload per rocprofv3 summary")
     ap.add_argument("--profile-once", action="store_true",
                     help="for rocprofv3 counter runs: one 1 GiB torch copy (a plain copy kernel of "
                          "known size, to calibrate FETCH_SIZE/WRITE_SIZE) then one step, no JSON")
@@ -236,6 +268,10 @@ def main():
 
     torch.cuda.set_device(0)
     w = W.get(WORKLOAD)
+    if args.rows_only and args.rows_only != "flat-1.3G-steps":
+        rows = rows_breakdown(torch, gq, W, None, None, w, args, groups=(args.rows_only,))
+        print(json.dumps({"rows": rows}), flush=True)
+        return
     log("generating %s: K=%d n=%d (%.1f GB) on the GPU" % (w.name, w.K, w.n, w.grad_bytes() / 1e9))
     grads = W.gradients(w, "cuda")
     S = torch.empty(1, dtype=torch.float32, device="cuda")
@@ -245,6 +281,13 @@ def main():
     def step():
         gq.global_norm(grads, scale_out=S)
         gq.fused_mean(grads, S, w.grid, w.levels, w.bits, 1, w.acc_bits, 0, out=out)
+
+    if args.rows_only:
+        S_ = torch.empty(1, dtype=torch.float32, device="cuda")
+        gq.global_norm(grads, scale_out=S_)
+        rows = rows_breakdown(torch, gq, W, grads, S_, w, args, groups=(args.rows_only,))
+        print(json.dumps({"rows": rows}), flush=True)
+        return
 
     if args.profile_once:
         a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")

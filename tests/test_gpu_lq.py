@@ -157,3 +157,51 @@ def test_step_full_shapes(orc, shape, r):
         ref, out, Eg, Qg = _step_both(orc, Gt.numpy(), E, Q)
         _check_step(ref, out, Eg, Qg)
         E, Q = ref["E"], ref["Q"]
+
+
+def test_step_zero_gradient(orc):
+    """G = E = 0: every column of P has no norm, so both factors, their codes and maxima, the
+    decoded Q and the new error are all exactly zero on both sides."""
+    n, m, r = 200, 150, 4
+    say("lq step zero gradient", n, m, r)
+    rng = np.random.default_rng(11)
+    Q = rng.standard_normal((m, r)).astype(np.float32)
+    Z = np.zeros((n, m), np.float32)
+    ref, out, Eg, Qg = _step_both(orc, Z, Z.copy(), Q)
+    names = {"p_codes": "p_codes", "q_codes": "q_codes", "p_colmax": "p_colmax",
+             "q_colmax": "q_colmax", "p_hat": "p_hat", "p_pre": "P_pre", "q_pre": "Q_pre"}
+    for key, rkey in names.items():
+        assert not host(out[key]).any(), key
+        assert not np.asarray(ref[rkey]).any(), rkey
+    assert not Eg.any() and not Qg.any()
+    assert not ref["E"].any() and not ref["Q"].any()
+
+
+def test_step_dead_column(orc):
+    """A zero column of Q makes that column of P exactly zero: Gram-Schmidt leaves it zero and
+    orthonormalises the others against the rest; its codes and maxima are zero on both sides
+    and the remaining columns match the oracle to the step's tolerance."""
+    n, m, r, dead = 300, 220, 4, 2
+    say("lq step dead column", n, m, r)
+    rng = np.random.default_rng(12)
+    Q = rng.standard_normal((m, r)).astype(np.float32)
+    Q[:, dead] = 0.0
+    G = (rng.standard_normal((n, m)) * 1e-3).astype(np.float32)
+    E = np.zeros((n, m), np.float32)
+    ref, out, Eg, Qg = _step_both(orc, G, E, Q)
+    P_pre = host(out["p_pre"])
+    assert not P_pre[:, dead].any() and not ref["P_pre"][:, dead].any()
+    eye = np.eye(r)
+    eye[dead, dead] = 0.0
+    assert np.abs(P_pre.T.astype(np.float64) @ P_pre - eye).max() < 1e-5
+    assert _rel(P_pre, ref["P_pre"]) < 1e-5
+    assert _rel(host(out["q_pre"]), ref["Q_pre"]) < 1e-5
+    for key in ("p_codes", "q_codes"):
+        gc = host(out[key]).astype(np.int32)
+        rc = ref[key].astype(np.int32)
+        assert not gc[:, dead].any() and not rc[:, dead].any()
+        assert np.abs(gc - rc).max() <= 1 and np.mean(gc != rc) < 1e-3
+    assert host(out["p_colmax"])[dead] == 0 and host(out["q_colmax"])[dead] == 0
+    assert _rel(host(out["p_hat"]), ref["p_hat"]) < 2e-3
+    assert _rel(Qg, ref["Q"]) < 2e-3
+    assert _rel(Eg, ref["E"]) < 2e-3
