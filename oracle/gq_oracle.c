@@ -92,21 +92,17 @@ double orc_sumsq(const void *x, int32_t dtype, int64_t n, double acc)
 }
 
 /* [GQ] abstract: one global norm scales all workers.  Reading: the shared scale of segment g
- * is the largest per-worker L2 norm, so that |x_{k,i}| <= S_g for every worker k. */
-int32_t orc_global_norm(const void *const *xs, int32_t K, int32_t dtype, int64_t n,
-                        const int64_t *offsets, int32_t nseg, float *scale_out,
+ * is the largest per-worker L2 norm, so that |x_{k,i}| <= S_g for every worker k.
+ * sumsq[k*nseg + g] holds worker k's sum of squares over segment g. */
+int32_t orc_norm_finish(const double *sumsq, int32_t K, int32_t nseg, float *scale_out,
                         double *norms_out)
 {
     int32_t g, k, bad = 0;
-    size_t esz = dtype == ORC_BF16 ? 2 : 4;
-    (void)n;
     for (g = 0; g < nseg; ++g) {
-        int64_t lo = offsets[g], hi = offsets[g + 1];
         double best = 0.0;
         int nonfinite = 0;
         for (k = 0; k < K; ++k) {
-            const char *base = (const char *)xs[k] + (size_t)lo * esz;
-            double nrm = sqrt(orc_sumsq(base, dtype, hi - lo, 0.0));
+            double nrm = sqrt(sumsq[(int64_t)k * nseg + g]);
             if (norms_out)
                 norms_out[(int64_t)k * nseg + g] = nrm;
             if (!isfinite(nrm))
@@ -123,6 +119,26 @@ int32_t orc_global_norm(const void *const *xs, int32_t K, int32_t dtype, int64_t
             scale_out[g] = S;
         }
     }
+    return bad;
+}
+
+int32_t orc_global_norm(const void *const *xs, int32_t K, int32_t dtype, int64_t n,
+                        const int64_t *offsets, int32_t nseg, float *scale_out,
+                        double *norms_out)
+{
+    int32_t g, k, bad;
+    size_t esz = dtype == ORC_BF16 ? 2 : 4;
+    double *ss = (double *)malloc(sizeof(double) * (size_t)K * (size_t)(nseg > 0 ? nseg : 1));
+    (void)n;
+    for (g = 0; g < nseg; ++g) {
+        int64_t lo = offsets[g], hi = offsets[g + 1];
+        for (k = 0; k < K; ++k) {
+            const char *base = (const char *)xs[k] + (size_t)lo * esz;
+            ss[(int64_t)k * nseg + g] = orc_sumsq(base, dtype, hi - lo, 0.0);
+        }
+    }
+    bad = orc_norm_finish(ss, K, nseg, scale_out, norms_out);
+    free(ss);
     return bad;
 }
 

@@ -53,8 +53,12 @@ void orc_hash_fill(uint32_t key, uint32_t counter0, int64_t cnt, uint32_t *out);
 double orc_load(const void *x, int32_t dtype, int64_t i);
 /* acc + sum_{i<n} x_i^2 in fp64, strictly in index order (chunks can be chained). */
 double orc_sumsq(const void *x, int32_t dtype, int64_t n, double acc);
-/* S_g = fp32(max_k sqrt(sum_{i in g} x_{k,i}^2)).  A non-finite S_g is replaced by 0 and
- * makes the return value 1 (else 0).  norms_out (K*nseg doubles, k-major) may be NULL. */
+/* S_g = fp32(max_k sqrt(sumsq[k*nseg + g])) from per-worker, per-segment sums of squares.
+ * A non-finite S_g is replaced by 0 and makes the return value 1 (else 0).  norms_out
+ * (K*nseg doubles, k-major) may be NULL. */
+int32_t orc_norm_finish(const double *sumsq, int32_t K, int32_t nseg, float *scale_out,
+                        double *norms_out);
+/* orc_sumsq of every (worker, segment) from 0, then orc_norm_finish. */
 int32_t orc_global_norm(const void *const *xs, int32_t K, int32_t dtype, int64_t n,
                         const int64_t *offsets, int32_t nseg, float *scale_out,
                         double *norms_out);

@@ -54,6 +54,7 @@ def lib():
             "orc_hash_fill": (None, [u32, u32, i64, p]),
             "orc_sumsq": (d, [p, i32, i64, d]),
             "orc_global_norm": (i32, [p, i32, i32, i64, p, i32, p, p]),
+            "orc_norm_finish": (i32, [p, i32, i32, p, p]),
             "orc_quant_one": (i32, [i32, i32, f, f, u32, u32]),
             "orc_quantize": (None, [p, i32, i64, p, i32, p, i32, i32, u64, u32, u32, p]),
             "orc_quantize_list": (None, [p, p, p, i64, i32, i32, u32, p]),
@@ -142,6 +143,18 @@ def global_norm(xs, offsets=None):
     norms = np.zeros((len(xs), nseg), np.float64)
     bad = lib().orc_global_norm(_ptrs(xs), len(xs), _dtype_code(xs[0]), n, _ptr(off), nseg,
                                 _ptr(S), _ptr(norms))
+    return S, norms, bool(bad)
+
+
+def norm_finish(sumsq):
+    """(S, norms, bad) from a K x nseg array of per-worker, per-segment sums of squares (for
+    data streamed through sumsq() chunk by chunk, in index order, which gives global_norm's
+    arithmetic exactly)."""
+    ss = _c(np.atleast_2d(sumsq), np.float64)
+    K, nseg = ss.shape
+    S = np.zeros(nseg, np.float32)
+    norms = np.zeros((K, nseg), np.float64)
+    bad = lib().orc_norm_finish(_ptr(ss), K, nseg, _ptr(S), _ptr(norms))
     return S, norms, bool(bad)
 
 

@@ -1,0 +1,128 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py times.
+
+The oracle cannot quantise 1e10 elements within a test, so at full size:
+
+* Every segment's shared scale is the oracle's own.  Each worker's buffer is brought to the
+  host (whole, or streamed in 2^26-element chunks when the workload is larger than a few GB)
+  and its sum of squares is chained through the chunks in index order, which is exactly the
+  oracle's arithmetic; the oracle then finishes the scale.  gq_global_norm must agree within
+  1e-6 relative (scale and per-worker norms).
+* gq_fused_mean runs over the whole buffers with the oracle's scale (the oracle never takes
+  an input from the HIP path), and sampled runs of outputs are recomputed by the oracle one
+  run at a time, its counters starting at the run's first index: the first and last
+  elements (ragged end), both sides of segment boundaries (up to 40 of them), both sides of
+  tile boundaries, elements past 2^31 and 2^32 bytes into a buffer, and seeded random
+  positions.  The decoded means must match bit for bit.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+from allreduce_compatible_gradient_amd import workloads as W
+from tests.gpu_helpers import first_diff, gq, host, say
+
+pytestmark = pytest.mark.gpu
+
+SEED = 1              # the seed bench.py quantises with
+RUN = 96              # elements per sampled run (even: 4-bit pairs stay aligned)
+TILE = 8192           # elements per streaming tile of the fused kernel
+CHUNK = 1 << 26       # host streaming chunk
+WHOLE_LIMIT = 8 << 30  # bytes of gradient copied to the host at once
+
+
+@pytest.fixture(scope="module")
+def orc():
+    from oracle import oracle
+    oracle.lib()
+    return oracle
+
+
+def _oracle_scale(orc, w, xs):
+    """(S, norms) by the oracle over the full buffers."""
+    if w.grad_bytes() <= WHOLE_LIMIT:
+        xs_h = [W.to_numpy(x) for x in xs]
+        S, norms, bad = orc.global_norm(xs_h, w.offsets)
+        assert not bad
+        return S, norms
+
+    def worker_sums(k):
+        ss = np.zeros(w.nseg, np.float64)
+        for g in range(w.nseg):
+            lo, hi = int(w.offsets[g]), int(w.offsets[g + 1])
+            acc = 0.0
+            for c in range(lo, hi, CHUNK):
+                acc = orc.sumsq(W.to_numpy(xs[k][c:min(c + CHUNK, hi)]), acc)
+            ss[g] = acc
+        return ss
+
+    with ThreadPoolExecutor(max_workers=min(w.K, 8)) as ex:
+        ss = np.stack(list(ex.map(worker_sums, range(w.K))))
+    S, norms, bad = orc.norm_finish(ss)
+    assert not bad
+    return S, norms
+
+
+def _runs(w):
+    """Sampled [a, b) runs, each inside one segment: returns a list of (a, b, segment)."""
+    n, off = w.n, w.offsets
+    rng = np.random.default_rng(20261203 + n)
+    want = [(0, RUN), (n - RUN, n)]
+    segs = range(w.nseg) if w.nseg <= 40 else sorted(rng.choice(w.nseg, 40, replace=False))
+    for g in segs:
+        lo = int(off[g])
+        want += [(lo - RUN // 2, lo), (lo, lo + RUN // 2)]
+    for i in (n // 2 // TILE * TILE, (n - 1) // TILE * TILE, (1 << 29), (1 << 30),
+              ((1 << 29) + TILE - 1) // TILE * TILE, ((1 << 30) + TILE - 1) // TILE * TILE):
+        want += [(i - RUN // 2, i + RUN // 2)]
+    want += [(int(i), int(i) + RUN) for i in rng.integers(0, n - RUN, 16)]
+    runs = []
+    for a, b in want:
+        a, b = max(a, 0), min(b, n)
+        if a >= b:
+            continue
+        # split at segment boundaries
+        g = int(np.searchsorted(off, a, side="right") - 1)
+        while a < b:
+            e = min(b, int(off[g + 1]))
+            if e > a:
+                runs.append((a, e, g))
+            a, g = e, g + 1
+    return sorted(set(runs))
+
+
+@pytest.mark.parametrize("name", W.GLOBAL_QSGD_WORKLOADS)
+def test_full_size_norm_and_fused_sampled(orc, name):
+    w = W.get(name)
+    say("full size", name, "K", w.K, "n", w.n, "nseg", w.nseg, "GB", w.grad_bytes() / 1e9)
+    g = gq()
+    xs = W.gradients(w, "cuda")
+    torch.cuda.synchronize()
+    S_ref, norms_ref = _oracle_scale(orc, w, xs)
+    say("oracle scale done", name)
+
+    norms_d = torch.empty(w.K * w.nseg, dtype=torch.float64, device="cuda")
+    S_gpu, _ = g.global_norm(xs, w.offsets, norms_out=norms_d)
+    S_gpu, norms_gpu = host(S_gpu), host(norms_d).reshape(w.K, w.nseg)
+    np.testing.assert_allclose(S_gpu, S_ref, rtol=1e-6, atol=0)
+    np.testing.assert_allclose(norms_gpu, norms_ref, rtol=1e-6, atol=0)
+
+    out_dtype = 1 if w.out_dtype == "bf16" else 0
+    scale = torch.from_numpy(S_ref).to("cuda")
+    out = g.fused_mean(xs, scale, w.grid, w.levels, w.bits, SEED, w.acc_bits, out_dtype,
+                       offsets=w.offsets)
+    torch.cuda.synchronize()
+    say("fused done", name)
+
+    runs = _runs(w)
+    assert len(runs) >= 20
+    for a, b, seg in runs:
+        xs_run = [W.to_numpy(x[a:b]) for x in xs]
+        ref = orc.allreduce_mean(xs_run, w.grid, w.levels, w.bits, w.acc_bits, SEED,
+                                 index_base=a, out_dtype=out_dtype, scale=S_ref[seg:seg + 1])
+        got = host(out[a:b])
+        assert np.array_equal(got, ref["mean"]), "run [%d, %d) seg %d: %s" % (
+            a, b, seg, first_diff(got, ref["mean"]))
+    del xs, out
+    torch.cuda.empty_cache()

@@ -329,6 +329,33 @@ def test_global_norm_nonfinite_zeroes_segment(orc):
     assert bad and S[1] == 0.0
 
 
+def test_streamed_global_norm_equals_whole(orc):
+    """Sums of squares chained chunk by chunk and finished by norm_finish give global_norm's
+    result bit for bit (the full-size GPU parity streams 41.6 GB this way), and the finish
+    against exact sums stays within the same 1e-12 as the whole-buffer form."""
+    rng = np.random.default_rng(13)
+    off = [0, 5000, 5000, 70001, 100003]
+    xs = [(rng.standard_normal(100003) * 10.0 ** rng.uniform(-3, 3, 100003)).astype(np.float32)
+          for _ in range(3)]
+    S, norms, bad = orc.global_norm(xs, off)
+    ss = np.zeros((3, 4))
+    for k, x in enumerate(xs):
+        for g in range(4):
+            acc = 0.0
+            for c in range(off[g], off[g + 1], 777):
+                acc = orc.sumsq(x[c:min(c + 777, off[g + 1])], acc)
+            ss[k, g] = acc
+    S2, norms2, bad2 = orc.norm_finish(ss)
+    assert np.array_equal(S, S2) and np.array_equal(norms, norms2) and bad == bad2 == False
+    for g in (0, 2, 3):
+        ref = max(math.sqrt(math.fsum(float(v) ** 2 for v in x[off[g]:off[g + 1]])) for x in xs)
+        assert S2[g] == np.float32(ref)
+    assert S2[1] == 0.0
+    ss[1, 2] = np.inf
+    S3, _, bad3 = orc.norm_finish(ss)
+    assert bad3 and S3[2] == 0.0 and S3[0] == S[0]
+
+
 # ----------------------------------------------------------------------------- decode
 def test_decode_factor_exact_rational(orc):
     rng = np.random.default_rng(12)
