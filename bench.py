@@ -75,11 +75,25 @@ class Timer:
         return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
 
 
+_SCRUB = []
+
+
+def evict_mall(torch):
+    """Write a 512 MiB buffer (twice the 256 MB Infinity Cache) so that the next timed call
+    finds none of its inputs cached; not timed."""
+    if not _SCRUB:
+        _SCRUB.append(torch.zeros(1 << 27, dtype=torch.float32, device="cuda"))
+    _SCRUB[0].add_(1.0)
+
+
 def time_calls(torch, fn, iters, warmup=1):
+    """Mean of ``iters`` calls timed one by one with HIP events on the launch stream, the
+    Infinity Cache evicted before each."""
     for _ in range(warmup):
         fn()
     t = Timer(torch)
     for _ in range(iters):
+        evict_mall(torch)
         e = t.start()
         fn()
         t.stop(e)
