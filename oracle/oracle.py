@@ -27,23 +27,34 @@ UNIFORM, EXP = 0, 1
 _lib = None
 
 
+def compile_library(src: str, out: str) -> str:
+    """gcc -O2 -ffp-contract=off (no fast-math) of one oracle source into a shared object."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math",
+                           "-fPIC", "-shared", "-Wall", "-Wextra", "-I", HERE, "-o", tmp, src,
+                           "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = False) -> str:
     """Compile liboracle.so with gcc; returns its path."""
     stale = (not os.path.exists(LIB)) or any(
         os.path.getmtime(p) > os.path.getmtime(LIB) for p in (SRC, HDR))
     if force or stale:
-        tmp = LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math",
-                               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"])
-        os.replace(tmp, LIB)
+        compile_library(SRC, LIB)
     return LIB
 
 
 def lib():
+    """The loaded oracle.  GQ_ORACLE_LIB names another build of it to load instead (the
+    planted-mistake tests use this to run the pins against a deliberately wrong oracle)."""
     global _lib
     if _lib is None:
-        build()
-        L = C.CDLL(LIB)
+        path = os.environ.get("GQ_ORACLE_LIB")
+        if not path:
+            path = build()
+        L = C.CDLL(path)
         p, i32, i64, u32, u64, d, f = (C.c_void_p, C.c_int32, C.c_int64, C.c_uint32,
                                        C.c_uint64, C.c_double, C.c_float)
         sig = {

@@ -82,6 +82,22 @@ def test_code_range_one_hot_at_scale(orc, s):
         assert hit_above, "no case exercised the clamp above the top level"
 
 
+def test_code_never_exceeds_s_when_u_rounds_above(orc):
+    """|x| = S can give u = fl(|x| * fl(s/S)) one ulp above s; the top level must still be s.
+    2^21 elements at such a scale make an unclamped round-up (probability u - s per element,
+    about 2^-17) all but certain to show."""
+    s = 127
+    rng = np.random.default_rng(5)
+    S = rng.uniform(1.0, 2.0, 400000).astype(np.float32)
+    u = (S * (np.float32(s) / S)).astype(np.float32)
+    S = S[np.argmax(u)]
+    assert u.max() > s
+    x = np.full(1 << 21, S, np.float32)
+    x[1::2] = -S
+    q = orc.quantize(x, [S], U, s, seed=3, worker=0)
+    assert q.max() == s and q.min() == -s
+
+
 def test_exp_code_range(orc):
     rng = np.random.default_rng(1)
     for E in (1, 3, 7):
@@ -115,6 +131,12 @@ def test_accumulator_overflow_is_reported(orc):
     assert over == 4
     _, over = orc.accumulate(codes[:258], 4, U, 8, 16)
     assert over == 0
+    # and below: 259 workers at level -127 give -32893 < -32768
+    neg = [orc.pack(np.full(4, -127, np.int32), U, 8)] * 259
+    _, over = orc.accumulate(neg, 4, U, 8, 16)
+    assert over == 4
+    sums, over = orc.accumulate(neg[:258], 4, U, 8, 16)
+    assert over == 0 and sums[0] == -258 * 127
 
 
 # ----------------------------------------------------------------------------- exact levels
