@@ -74,6 +74,11 @@ class Timer:
         self.torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
 
+    def median_ms(self):
+        self.torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in self.pairs)
+        return t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
+
 
 _SCRUB = []
 
@@ -86,9 +91,9 @@ def evict_mall(torch):
     _SCRUB[0].add_(1.0)
 
 
-def time_calls(torch, fn, iters, warmup=1):
-    """Mean of ``iters`` calls timed one by one with HIP events on the launch stream, the
-    Infinity Cache evicted before each."""
+def time_calls(torch, fn, iters, warmup=1, median=True):
+    """Mean (or median) of ``iters`` calls timed one by one with HIP events on the launch
+    stream, the Infinity Cache evicted before each."""
     for _ in range(warmup):
         fn()
     t = Timer(torch)
@@ -97,7 +102,7 @@ def time_calls(torch, fn, iters, warmup=1):
         e = t.start()
         fn()
         t.stop(e)
-    return t.mean_ms()
+    return t.median_ms() if median else t.mean_ms()
 
 
 ROW_GROUPS = ("flat-1.3G-steps", "resnet50", "gpt2", "lq-4096x4096", "lq-4096x11008")
@@ -161,14 +166,14 @@ def rows_resnet50(torch, gq, W, row):
     S2, _ = gq.global_norm(g2, w2.offsets)
     o2 = torch.empty(w2.n, dtype=torch.float32, device="cuda")
     c2 = torch.empty((w2.n + 1) // 2, dtype=torch.uint8, device="cuda")
-    ms = time_calls(torch, lambda: gq.global_norm(g2, w2.offsets, scale_out=S2), 5)
+    ms = time_calls(torch, lambda: gq.global_norm(g2, w2.offsets, scale_out=S2), 11)
     row("norm_resnet50_161seg_K8", ms, w2.K * w2.n * 4, "K fp32 buffers in")
     ms = time_calls(torch, lambda: gq.quantize_pack(g2[0], S2, w2.grid, w2.levels, w2.bits, 1, 0,
-                                                    offsets=w2.offsets, codes=c2), 5)
+                                                    offsets=w2.offsets, codes=c2), 11)
     row("quantize_pack_resnet50_exp7_int4", ms, w2.n * 4 + (w2.n + 1) // 2,
         "one worker, exponential grid, 4-bit codes")
     ms = time_calls(torch, lambda: gq.fused_mean(g2, S2, w2.grid, w2.levels, w2.bits, 1, 16, 0,
-                                                 offsets=w2.offsets, out=o2), 5)
+                                                 offsets=w2.offsets, out=o2), 11)
     row("fused_resnet50_exp7_K8", ms, w2.K * w2.n * 4 + w2.n * 4, "fused pass, 161 segments")
     del g2, o2, c2
     torch.cuda.empty_cache()
@@ -180,10 +185,10 @@ def rows_gpt2(torch, gq, W, row):
     g3 = W.gradients(w3, "cuda")
     S3, _ = gq.global_norm(g3, w3.offsets)
     o3 = torch.empty(w3.n, dtype=torch.bfloat16, device="cuda")
-    ms = time_calls(torch, lambda: gq.global_norm(g3, w3.offsets, scale_out=S3), 3)
+    ms = time_calls(torch, lambda: gq.global_norm(g3, w3.offsets, scale_out=S3), 7)
     row("norm_gpt2_bf16_K16", ms, w3.K * w3.n * 2, "K bf16 buffers in")
     ms = time_calls(torch, lambda: gq.fused_mean(g3, S3, w3.grid, w3.levels, w3.bits, 1, 16, 1,
-                                                 offsets=w3.offsets, out=o3), 3)
+                                                 offsets=w3.offsets, out=o3), 7)
     row("fused_gpt2_bf16_s7_K16", ms, w3.K * w3.n * 2 + w3.n * 2, "fused pass, bf16 in and out")
     del g3, o3
     torch.cuda.empty_cache()
@@ -199,7 +204,7 @@ def rows_lq(torch, gq, W, shape, row):
         o5 = {"p_hat": torch.empty(n5, r5, dtype=torch.float32, device="cuda")}
         o5 = gq.powersgd_logquant(G, E, Q, W.LQ_ALPHA, W.LQ_BITS, out=o5)
         ms = time_calls(torch, lambda: gq.powersgd_logquant(G, E, Q, W.LQ_ALPHA, W.LQ_BITS,
-                                                            out=o5), 5)
+                                                            out=o5), 11)
         row("lq_step_%dx%d_r%d" % (n5, m5, r5), ms, 6 * n5 * m5 * 4,
             "G read, E read+write, E read, E read+write")
         del G, E, Q
@@ -207,7 +212,8 @@ def rows_lq(torch, gq, W, shape, row):
 
 def measure_ceilings(torch, grads, out):
     """Bandwidth of a plain stream with the fused pass's memory pattern and with the norm
-    pass's (libgq_ceiling.so): K fp32 reads + 1 fp32 write, and K fp32 reads."""
+    pass's (libgq_ceiling.so): K fp32 reads + 1 fp32 write, and K fp32 reads; and of a plain
+    one-read, one-write copy with the same lane map."""
     import ctypes as C
     from allreduce_compatible_gradient_amd import build as B
     lib = C.CDLL(B.CEILING_LIB)
@@ -218,15 +224,18 @@ def measure_ceilings(torch, grads, out):
     srcs = (C.c_void_p * K)(*[g.data_ptr() for g in grads])
     sink = torch.zeros(4, dtype=torch.float32, device="cuda")
     stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    src1 = (C.c_void_p * 1)(grads[0].data_ptr())
     res = {}
-    for name, o, nbytes in (("read_K%d_write1" % K, out.data_ptr(), (K + 1) * (n // 2048) * 8192),
-                            ("read_K%d" % K, None, K * (n // 2048) * 8192)):
+    for name, kk, o, nbytes in (
+            ("read_K%d_write1" % K, K, out.data_ptr(), (K + 1) * (n // 2048) * 8192),
+            ("read_K%d" % K, K, None, K * (n // 2048) * 8192),
+            ("copy_read1_write1", 1, out.data_ptr(), 2 * (n // 2048) * 8192)):
         best = 0.0
         for grid in (1024, 2048, 4096, 8192, 16384):
             for chunk in (1, 2, 4):
                 def run():
-                    assert lib.gqc_stream(srcs, K, n, o, sink.data_ptr(), grid, chunk,
-                                          stream) == 0
+                    assert lib.gqc_stream(srcs if kk == K else src1, kk, n, o, sink.data_ptr(),
+                                          grid, chunk, stream) == 0
                 ms = time_calls(torch, run, 3)
                 best = max(best, nbytes / (ms * 1e-3) / 1e9)
         res[name] = round(best, 1)
@@ -245,8 +254,16 @@ def cpu_baseline(grads, w, sample):
     dt = time.perf_counter() - t0
     assert res["mean"].size == sample
     gbs = w.K * sample * 4 / dt / 1e9
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2),
+            "seconds": round(dt, 2), "host": {"nproc": os.cpu_count(), "cpu": model},
             "sample": "first %d elements of each of the %d workers of %s (%.2f GB of gradient): "
                       "global norm, quantise, pack, integer sum and decode, single thread"
                       % (sample, w.K, w.name, w.K * sample * 4 / 1e9)}
@@ -372,6 +389,8 @@ def main():
         grad_bytes / norm_ms / 1e6 / ceil["read_K8"], 4)
     if not args.no_rows:
         result["rows"] = rows_breakdown(torch, gq, W, grads, S, w, args)
+        for r in result["rows"].values():
+            r["frac_of_copy_ceiling"] = round(r["GBps"] / ceil["copy_read1_write1"], 4)
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on %d elements per worker" % args.cpu_sample)
         result["cpu_baseline"] = cpu_baseline(grads, w, args.cpu_sample)
