@@ -344,23 +344,20 @@ __device__ __forceinline__ float quant_uniform_mag(float x, float inv, float sf,
   return h < c ? ceilf(u) : fl;               // p > 0 whenever h < c, so ceil(u) = fl + 1
 }
 
-// Exponential grid: index j in [0, E] of the level (level j > 0 is 2^(j-E)).
+// Exponential grid: index j in [0, E] of the level (level j > 0 is 2^(j-E)).  Above the
+// lowest level u lies in the binade of level j = E + exponent(u), and the probability of
+// rounding up is u / 2^exponent - 1, whose 23 mantissa bits times 2^32 are the integer
+// mantissa << 9; below it, p = u / 2^(1-E) (both scalings exact).
 __device__ __forceinline__ uint32_t quant_exp_index(float x, float inv, int E, float two_em1,
                                                     uint32_t h) {
   const float u = fminf(fabsf(x) * inv, 1.0f);
   const uint32_t b = __float_as_uint(u);
-  const int e = (int)(b >> 23) - 127;  // binade of u (u normal when e >= 1 - E)
-  uint32_t j;
-  float p;
-  if (e < 1 - E) {
-    j = 0;
-    p = u * two_em1;                   // (u - 0) / 2^(1-E), exact
-  } else {
-    j = (uint32_t)(E + e);
-    p = __uint_as_float((b & 0x7FFFFFu) | 0x3F800000u) - 1.0f;  // u / 2^e - 1, exact
-  }
-  const uint32_t c = (uint32_t)ceilf(p * 4294967296.0f);
-  return j + (h < c ? 1u : 0u);
+  const int32_t jn = (int32_t)(b >> 23) - (127 - E);  // <= 0 below the lowest level
+  const bool low = jn <= 0;
+  const uint32_t c_hi = (b & 0x7FFFFFu) << 9;
+  const uint32_t c_lo = (uint32_t)ceilf((u * two_em1) * 4294967296.0f);
+  const uint32_t c = low ? c_lo : c_hi;
+  return (low ? 0u : (uint32_t)jn) + (h < c ? 1u : 0u);
 }
 
 // Code field of a uniform level (signed, two's complement in `bits`).
@@ -635,12 +632,12 @@ __device__ __forceinline__ void fused_batch(const FusedArgs &a, int k0, int kn,
   }
 }
 
-// The uniform fast path fits in 128 VGPRs (4 waves per SIMD, enough loads in flight per CU
-// to cover HBM latency); the exponential grid and the code-storing variant keep more values
-// live and get 256 (2 waves per SIMD) rather than spilling.
+// Without the code stores both grids fit in 128 VGPRs (4 waves per SIMD, enough loads in
+// flight per CU to cover HBM latency); the code-storing variants keep more values live and
+// get 256 (2 waves per SIMD) rather than spilling.
 template <int KT, int DT, int GRID, bool STORE>
 __global__ __launch_bounds__(kBlock)
-__attribute__((amdgpu_waves_per_eu((GRID == 0 && !STORE) ? 4 : 2, 8)))
+__attribute__((amdgpu_waves_per_eu(!STORE ? 4 : 2, 8)))
 void k_fused(FusedArgs a) {
   constexpr int P = DT == 0 ? 4 : 8;
   constexpr int NP = kChunk / (64 * P);
