@@ -1,6 +1,6 @@
 """ctypes binding of the plain C oracle (gq_oracle.c).
 
-TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, the smoke check at the repository root and the
 ``cpu_baseline`` leg of ``bench.py``.  The product package never imports this module, and this
 module imports nothing from the product package.
 
