@@ -190,3 +190,21 @@ def test_argument_errors():
     # nothing was launched by the failed calls; a valid call still works
     out = g.fused_mean([x, x], S, U, 7, 4, 1, 16)
     assert out.shape == x.shape
+
+
+@pytest.mark.parametrize("grid,levels,bits", [(U, 127, 8), (X, 7, 4)])
+def test_counter_at_the_top_of_its_range(orc, grid, levels, bits):
+    """index_base + n = 2^32 exactly: the last element draws counter 2^32 - 1; segments and a
+    ragged end on the way, every entry point against the oracle."""
+    say("counter top", grid)
+    n = 3 * 8192 + 77
+    base = 2 ** 32 - n
+    rng = np.random.default_rng(21)
+    xs = [rng.standard_normal(n).astype(np.float32) for _ in range(3)]
+    off = [0, 8192, 8200, n]
+    ref = _run_both(orc, xs, grid, levels, bits, 16, seed=5, offsets=off, index_base=base)
+    # the fast path (no codes or sums stored) too
+    g = gq()
+    out = g.fused_mean([dev(x) for x in xs], dev(ref["scale"]), grid, levels, bits, 5, 16, 0,
+                       base, off)
+    assert np.array_equal(host(out), ref["mean"]), first_diff(host(out), ref["mean"])

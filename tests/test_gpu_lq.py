@@ -205,3 +205,20 @@ def test_step_dead_column(orc):
     assert _rel(host(out["p_hat"]), ref["p_hat"]) < 2e-3
     assert _rel(Qg, ref["Q"]) < 2e-3
     assert _rel(Eg, ref["E"]) < 2e-3
+
+
+@pytest.mark.parametrize("alpha", [1.0, 100.0])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_logquant_other_alphas_and_widths(orc, alpha, bits):
+    """The table encode and decode stay bit-exact for other curvatures and code widths (the
+    oracle's bins for these are pinned against 60-digit boundaries on the CPU)."""
+    say("logquant alpha", alpha, "bits", bits)
+    g = gq()
+    rng = np.random.default_rng(int(alpha) * 10 + bits)
+    F = (rng.standard_normal((3000, 5)) * 10.0 ** rng.uniform(-3, 3, 5)).astype(np.float32)
+    codes, cmax, Fh = orc.logquant(F, alpha, bits)
+    gc, gm, gh = g.logquant(dev(F), alpha, bits)
+    assert np.array_equal(host(gc), codes), first_diff(host(gc), codes)
+    assert np.array_equal(host(gm), cmax)
+    assert np.array_equal(host(gh), Fh), first_diff(host(gh), Fh)
+    assert np.abs(codes).max() <= (1 << (bits - 1)) - 1
