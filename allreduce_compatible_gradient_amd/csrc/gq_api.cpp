@@ -452,8 +452,8 @@ GQ_EXPORT gq_status gq_logquant(gq_ctx *c, const float *F, int64_t rows, int32_t
 }
 
 GQ_EXPORT gq_status gq_powersgd_logquant(gq_ctx *c, const float *G, float *E, float *Q, int64_t n,
-                                         int64_t m, int32_t r, double alpha, int32_t bits,
-                                         int8_t *p_codes, float *p_colmax, int8_t *q_codes,
+                                         int64_t m, int32_t r, double alpha, int32_t bits_p,
+                                         int32_t bits_q, int8_t *p_codes, float *p_colmax, int8_t *q_codes,
                                          float *q_colmax, float *p_hat_or_null,
                                          float *p_pre_or_null, float *q_pre_or_null, void *stream) {
   if (!c) return GQ_EINVAL;
@@ -462,7 +462,8 @@ GQ_EXPORT gq_status gq_powersgd_logquant(gq_ctx *c, const float *G, float *E, fl
   if (n > (1ll << 30) || m > (1ll << 30)) return fail(c, GQ_EINVAL, "n or m too large");
   if (r < 1 || r > gq::kLqMaxRank) return fail(c, GQ_EINVAL, "r = %d outside [1, %d]", r, gq::kLqMaxRank);
   if (!(alpha > 0.0) || !std::isfinite(alpha)) return fail(c, GQ_EINVAL, "alpha must be positive and finite");
-  if (bits < 2 || bits > 8) return fail(c, GQ_EINVAL, "bits = %d outside [2, 8]", bits);
+  if (bits_p < 2 || bits_p > 8) return fail(c, GQ_EINVAL, "bits_p = %d outside [2, 8]", bits_p);
+  if (bits_q < 2 || bits_q > 8) return fail(c, GQ_EINVAL, "bits_q = %d outside [2, 8]", bits_q);
   TRY(check_ptr(c, G, "G"));
   TRY(check_ptr(c, E, "E"));
   TRY(check_ptr(c, Q, "Q"));
@@ -473,7 +474,7 @@ GQ_EXPORT gq_status gq_powersgd_logquant(gq_ctx *c, const float *G, float *E, fl
   if (p_hat_or_null) TRY(check_ptr(c, p_hat_or_null, "p_hat"));
   if (p_pre_or_null) TRY(check_ptr(c, p_pre_or_null, "p_pre"));
   if (q_pre_or_null) TRY(check_ptr(c, q_pre_or_null, "q_pre"));
-  gq::LqStepArgs a{G, E, Q, n, m, r, alpha, bits, p_codes, p_colmax, q_codes, q_colmax,
+  gq::LqStepArgs a{G, E, Q, n, m, r, alpha, bits_p, bits_q, p_codes, p_colmax, q_codes, q_colmax,
                    p_hat_or_null, p_pre_or_null, q_pre_or_null};
   hipError_t e = gq::lq_step(c->lq, a, s);
   if (e == hipErrorOutOfMemory) return fail(c, GQ_ENOMEM, "LQ scratch allocation failed");

@@ -32,7 +32,7 @@ struct LqStepArgs {
   int64_t n, m;
   int32_t r;
   double alpha;
-  int32_t bits;
+  int32_t bits_p, bits_q;  // code widths of P and of Q'
   int8_t *p_codes;
   float *p_colmax;
   int8_t *q_codes;

@@ -532,7 +532,8 @@ __global__ __launch_bounds__(1024) void k_lq_quant_cols(ColJob j0, ColJob j1, in
 }
 
 // Log-quantise both factors element by element, the column maxima already known (cmax_bits:
-// RANK words for Pt, then RANK for Q').  Same encode/decode as k_lq_quant_cols.
+// RANK words for Pt, then RANK for Q'), each with its own tables (code widths b_p and b_q).
+// Same encode/decode as k_lq_quant_cols.
 struct ElemJob {
   const float *Pt;       // n x r
   const float *Qn;       // m x r
@@ -545,12 +546,15 @@ struct ElemJob {
   float *Qh;             // decoded Q (written into Q)
 };
 
-__global__ __launch_bounds__(256) void k_lq_quant_elems(ElemJob J, const float *tab, int L) {
-  __shared__ float thr[128];
-  __shared__ float lvl[128];
+__global__ __launch_bounds__(256) void k_lq_quant_elems(ElemJob J, const float *tab_p, int Lp,
+                                                        const float *tab_q, int Lq) {
+  __shared__ float thr[2][128];
+  __shared__ float lvl[2][128];
   const int tid = threadIdx.x;
-  if (tid < L) thr[tid] = tab[tid];
-  if (tid <= L) lvl[tid] = tab[L + tid];
+  if (tid < Lp) thr[0][tid] = tab_p[tid];
+  if (tid <= Lp) lvl[0][tid] = tab_p[Lp + tid];
+  if (tid < Lq) thr[1][tid] = tab_q[tid];
+  if (tid <= Lq) lvl[1][tid] = tab_q[Lq + tid];
   __syncthreads();
   const int64_t np = J.n * J.r, nq = J.m * J.r;
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + tid;
@@ -564,13 +568,14 @@ __global__ __launch_bounds__(256) void k_lq_quant_elems(ElemJob J, const float *
   const int c = (int)(i % J.r);
   const float x = isp ? J.Pt[i] : J.Qn[i];
   const float mx = __uint_as_float(J.cmax_bits[isp ? c : J.r + c]);
+  const int t = isp ? 0 : 1;
   int k = 0;
   if (mx > 0.0f) {
     const float y = fabsf(x) / mx;  // IEEE division, in [0, 1]
-    int lo = 0, hi = L;             // k = #{boundaries <= y}
+    int lo = 0, hi = isp ? Lp : Lq; // k = #{boundaries <= y}
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (thr[mid] <= y)
+      if (thr[t][mid] <= y)
         lo = mid + 1;
       else
         hi = mid;
@@ -578,7 +583,7 @@ __global__ __launch_bounds__(256) void k_lq_quant_elems(ElemJob J, const float *
     k = lo;
   }
   const int8_t code = (int8_t)(x < 0.0f ? -k : k);
-  const float v = lvl[k] * mx;
+  const float v = lvl[t][k] * mx;
   const float fh = x < 0.0f ? -v : v;
   if (isp) {
     J.p_codes[i] = code;
@@ -688,7 +693,8 @@ struct StepBufs {
 };
 
 template <int RANK, int VEC>
-void launch_step(const LqStepArgs &a, const StepBufs &b, const LqTables &tab, hipStream_t s) {
+void launch_step(const LqStepArgs &a, const StepBufs &b, const LqTables &tp, const LqTables &tq,
+                 hipStream_t s) {
   const int64_t n = a.n, m = a.m;
   hipLaunchKernelGGL((k_lq_ef_mq<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA), 0, s,
                      a.G, a.E, a.Q, b.P, b.gpart, n, m);
@@ -703,18 +709,18 @@ void launch_step(const LqStepArgs &a, const StepBufs &b, const LqTables &tab, hi
   ElemJob je{b.Pt, b.Qn, n, m, RANK, b.cmax_bits, a.p_codes, a.q_codes, a.p_colmax, a.q_colmax,
              b.Ph, a.p_hat, a.Q};
   hipLaunchKernelGGL(k_lq_quant_elems, dim3((unsigned)(((n + m) * RANK + 255) / 256)),
-                     dim3(256), 0, s, je, tab.dev, tab.L);
+                     dim3(256), 0, s, je, tp.dev, tp.L, tq.dev, tq.L);
   hipLaunchKernelGGL((k_lq_ef_update<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA), 0,
                      s, a.E, b.Ph, a.Q, n, m);
 }
 
 template <int RANK>
-void launch_step_v(const LqStepArgs &a, bool vec4, const StepBufs &b, const LqTables &tab,
-                   hipStream_t s) {
+void launch_step_v(const LqStepArgs &a, bool vec4, const StepBufs &b, const LqTables &tp,
+                   const LqTables &tq, hipStream_t s) {
   if (vec4)
-    launch_step<RANK, 4>(a, b, tab, s);
+    launch_step<RANK, 4>(a, b, tp, tq, s);
   else
-    launch_step<RANK, 1>(a, b, tab, s);
+    launch_step<RANK, 1>(a, b, tp, tq, s);
 }
 
 }  // namespace
@@ -730,8 +736,10 @@ hipError_t lq_logquant(LqState &st, const float *F, int64_t rows, int r, double 
 }
 
 hipError_t lq_step(LqState &st, const LqStepArgs &a, hipStream_t s) {
-  const LqTables *tab = nullptr;
-  hipError_t e = tables(st, a.alpha, a.bits, s, &tab);
+  const LqTables *tp = nullptr, *tq = nullptr;
+  hipError_t e = tables(st, a.alpha, a.bits_p, s, &tp);
+  if (e != hipSuccess) return e;
+  e = tables(st, a.alpha, a.bits_q, s, &tq);  // map insertion keeps tp valid
   if (e != hipSuccess) return e;
   const int64_t n = a.n, m = a.m, r = a.r;
   StepBufs b;
@@ -760,14 +768,14 @@ hipError_t lq_step(LqState &st, const LqStepArgs &a, hipStream_t s) {
   b.cmax_bits = reinterpret_cast<unsigned *>(base + oC);
   const bool vec4 = (m % 4) == 0;
   switch (a.r) {
-    case 1: launch_step_v<1>(a, vec4, b, *tab, s); break;
-    case 2: launch_step_v<2>(a, vec4, b, *tab, s); break;
-    case 3: launch_step_v<3>(a, vec4, b, *tab, s); break;
-    case 4: launch_step_v<4>(a, vec4, b, *tab, s); break;
-    case 5: launch_step_v<5>(a, vec4, b, *tab, s); break;
-    case 6: launch_step_v<6>(a, vec4, b, *tab, s); break;
-    case 7: launch_step_v<7>(a, vec4, b, *tab, s); break;
-    case 8: launch_step_v<8>(a, vec4, b, *tab, s); break;
+    case 1: launch_step_v<1>(a, vec4, b, *tp, *tq, s); break;
+    case 2: launch_step_v<2>(a, vec4, b, *tp, *tq, s); break;
+    case 3: launch_step_v<3>(a, vec4, b, *tp, *tq, s); break;
+    case 4: launch_step_v<4>(a, vec4, b, *tp, *tq, s); break;
+    case 5: launch_step_v<5>(a, vec4, b, *tp, *tq, s); break;
+    case 6: launch_step_v<6>(a, vec4, b, *tp, *tq, s); break;
+    case 7: launch_step_v<7>(a, vec4, b, *tp, *tq, s); break;
+    case 8: launch_step_v<8>(a, vec4, b, *tp, *tq, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

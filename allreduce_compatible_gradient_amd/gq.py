@@ -42,8 +42,8 @@ _SIGS = {
     "gq_fused_mean": (_i32, [_p, _p, _i32, _i32, _i64, _p, _i32, _p, _i32, _i32, _i32, _u64, _u32,
                              _i32, _p, _p, _i32, _p, _p]),
     "gq_logquant": (_i32, [_p, _p, _i64, _i32, _d, _i32, _p, _p, _p, _p]),
-    "gq_powersgd_logquant": (_i32, [_p, _p, _p, _p, _i64, _i64, _i32, _d, _i32, _p, _p, _p, _p,
-                                    _p, _p, _p, _p]),
+    "gq_powersgd_logquant": (_i32, [_p, _p, _p, _p, _i64, _i64, _i32, _d, _i32, _i32, _p, _p,
+                                    _p, _p, _p, _p, _p, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -251,8 +251,9 @@ def logquant(F, alpha, bits, codes=None, colmax=None, F_hat=None, want_hat=True,
 
 
 def powersgd_logquant(G, E, Q, alpha, bits, out=None, want_hat=True, want_pre=False,
-                      ctx: Optional[Context] = None):
-    """One LQ-SGD compressor step; E and Q are updated in place.  Returns a dict of outputs."""
+                      bits_q=None, ctx: Optional[Context] = None):
+    """One LQ-SGD compressor step; E and Q are updated in place.  ``bits`` is the code width of
+    P, ``bits_q`` that of Q' (default: the same).  Returns a dict of outputs."""
     ctx = ctx or context()
     n, m = G.shape
     r = Q.shape[1]
@@ -273,7 +274,7 @@ def powersgd_logquant(G, E, Q, alpha, bits, out=None, want_hat=True, want_pre=Fa
 
     ctx.check(_lib.gq_powersgd_logquant(
         ctx.handle, _dev(G, "G", torch.float32), _dev(E, "E", torch.float32),
-        _dev(Q, "Q", torch.float32), n, m, r, alpha, bits,
+        _dev(Q, "Q", torch.float32), n, m, r, alpha, bits, bits if bits_q is None else bits_q,
         _dev(o["p_codes"], "p_codes", torch.int8), _dev(o["p_colmax"], "p_colmax", torch.float32),
         _dev(o["q_codes"], "q_codes", torch.int8), _dev(o["q_colmax"], "q_colmax", torch.float32),
         opt("p_hat"), opt("p_pre"), opt("q_pre"), _stream()))

@@ -144,15 +144,16 @@ gq_status gq_logquant(gq_ctx *ctx, const float *F, int64_t rows, int32_t r, doub
 /* One LQ-SGD compressor step for one worker (LQ-SGD review: "What carries the argument",
  * "Core claim", referee major comment 1):
  *   M = G + E (fp32, written into E);  P = M Q;  P <- Gram-Schmidt(P) (columns in order);
- *   Q' = M^T P;  log-quantise P and Q' per column (as gq_logquant);
+ *   Q' = M^T P;  log-quantise P with bits_p and Q' with bits_q per column (as gq_logquant;
+ *   the referee's comment on Section V lists b_p and b_q as separate settings, 2..8 each);
  *   E <- M - Phat Q'hat^T;  Q <- Q'hat (warm start of the next step).
  *   G n x m fp32 row-major;  E n x m fp32 in/out;  Q m x r fp32 in/out;  1 <= r <= 8
  *   p_codes n x r int8, p_colmax r;  q_codes m x r int8, q_colmax r
  *   p_hat_or_null n x r fp32 or NULL (decoded P);  p_pre_or_null n x r and q_pre_or_null m x r
  *   fp32 or NULL (the factors before quantisation). */
 gq_status gq_powersgd_logquant(gq_ctx *ctx, const float *G, float *E, float *Q, int64_t n,
-                               int64_t m, int32_t r, double alpha, int32_t bits,
-                               int8_t *p_codes, float *p_colmax, int8_t *q_codes,
+                               int64_t m, int32_t r, double alpha, int32_t bits_p,
+                               int32_t bits_q, int8_t *p_codes, float *p_colmax, int8_t *q_codes,
                                float *q_colmax, float *p_hat_or_null, float *p_pre_or_null,
                                float *q_pre_or_null, void *stream);
 

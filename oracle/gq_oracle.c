@@ -461,7 +461,8 @@ void orc_mgs(float *P, int64_t n, int32_t r)
 /* [LQ] "What carries the argument": G ~ P Q^T with error feedback E_t = G'_t - Ghat_t;
  * "Core claim": Q warm-started from the previous iteration.  One worker, one power step. */
 void orc_powersgd_logquant(const float *G, float *E, float *Q, int64_t n, int64_t m,
-                           int32_t r, double alpha, int32_t bits, int8_t *p_codes,
+                           int32_t r, double alpha, int32_t bits_p, int32_t bits_q,
+                           int8_t *p_codes,
                            float *p_colmax, int8_t *q_codes, float *q_colmax, float *p_hat,
                            float *P_pre, float *Q_pre)
 {
@@ -502,8 +503,8 @@ void orc_powersgd_logquant(const float *G, float *E, float *Q, int64_t n, int64_
     if (Q_pre)
         memcpy(Q_pre, Qn, (size_t)(m * r) * sizeof(float));
 
-    orc_logquant(P, n, r, alpha, bits, p_codes, p_colmax, Ph);
-    orc_logquant(Qn, m, r, alpha, bits, q_codes, q_colmax, Qh);
+    orc_logquant(P, n, r, alpha, bits_p, p_codes, p_colmax, Ph);
+    orc_logquant(Qn, m, r, alpha, bits_q, q_codes, q_colmax, Qh);
 
     /* E = M - Phat Qhat^T (fp64 products, one rounding) */
     for (i = 0; i < n; ++i)

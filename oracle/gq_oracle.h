@@ -112,11 +112,13 @@ void orc_logquant(const float *F, int64_t rows, int32_t r, double alpha, int32_t
                   int8_t *codes, float *colmax, float *Fhat);
 /* Modified Gram-Schmidt on the columns of P (n x r, row-major, fp32 in and out), fp64 math. */
 void orc_mgs(float *P, int64_t n, int32_t r);
-/* One compressor step: M = G + E; P = M Qprev; P <- MGS(P); Q = M^T P; quantise P, Q;
- * E <- M - Phat Qhat^T; Qprev <- Qhat.  E and Q are updated in place.
+/* One compressor step: M = G + E; P = M Qprev; P <- MGS(P); Q = M^T P; quantise P with
+ * bits_p and Q with bits_q (the review's referee comment on Section V names b_p and b_q as
+ * separate settings); E <- M - Phat Qhat^T; Qprev <- Qhat.  E and Q are updated in place.
  * P_pre and Q_pre (may be NULL) receive the unquantised factors. */
 void orc_powersgd_logquant(const float *G, float *E, float *Q, int64_t n, int64_t m,
-                           int32_t r, double alpha, int32_t bits, int8_t *p_codes,
+                           int32_t r, double alpha, int32_t bits_p, int32_t bits_q,
+                           int8_t *p_codes,
                            float *p_colmax, int8_t *q_codes, float *q_colmax, float *p_hat,
                            float *P_pre, float *Q_pre);
 

@@ -80,7 +80,7 @@ def lib():
             "orc_logq_level": (f, [i32, d, i32]),
             "orc_logquant": (None, [p, i64, i32, d, i32, p, p, p]),
             "orc_mgs": (None, [p, i64, i32]),
-            "orc_powersgd_logquant": (None, [p, p, p, i64, i64, i32, d, i32, p, p, p, p, p,
+            "orc_powersgd_logquant": (None, [p, p, p, i64, i64, i32, d, i32, i32, p, p, p, p, p,
                                              p, p]),
         }
         for name, (res, args) in sig.items():
@@ -279,8 +279,9 @@ def mgs(P):
     return P
 
 
-def powersgd_logquant(G, E, Q, alpha, bits):
-    """One step.  Returns dict with the updated E and Q (new arrays) and all outputs."""
+def powersgd_logquant(G, E, Q, alpha, bits, bits_q=None):
+    """One step (P coded with ``bits``, Q with ``bits_q``, default the same).  Returns a dict
+    with the updated E and Q (new arrays) and all outputs."""
     G = _c(G, np.float32)
     E = np.array(E, dtype=np.float32, order="C", copy=True)
     Q = np.array(Q, dtype=np.float32, order="C", copy=True)
@@ -293,7 +294,8 @@ def powersgd_logquant(G, E, Q, alpha, bits):
     ph = np.empty((n, r), np.float32)
     ppre = np.empty((n, r), np.float32)
     qpre = np.empty((m, r), np.float32)
-    lib().orc_powersgd_logquant(_ptr(G), _ptr(E), _ptr(Q), n, m, r, alpha, bits, _ptr(pc),
+    lib().orc_powersgd_logquant(_ptr(G), _ptr(E), _ptr(Q), n, m, r, alpha, bits,
+                                bits if bits_q is None else bits_q, _ptr(pc),
                                 _ptr(pm), _ptr(qc), _ptr(qm), _ptr(ph), _ptr(ppre), _ptr(qpre))
     return dict(E=E, Q=Q, p_codes=pc, p_colmax=pm, q_codes=qc, q_colmax=qm, p_hat=ph,
                 P_pre=ppre, Q_pre=qpre)

@@ -72,11 +72,11 @@ def test_logquant_at_bin_boundaries(orc):
     assert codes[2::2, 0].tolist() == list(range(1, L + 1))
 
 
-def _step_both(orc, G, E, Q):
+def _step_both(orc, G, E, Q, bits=BITS, bits_q=None):
     g = gq()
-    ref = orc.powersgd_logquant(G, E, Q, ALPHA, BITS)
+    ref = orc.powersgd_logquant(G, E, Q, ALPHA, bits, bits_q=bits_q)
     Ed, Qd = dev(E), dev(Q)
-    out = g.powersgd_logquant(dev(G), Ed, Qd, ALPHA, BITS, want_pre=True)
+    out = g.powersgd_logquant(dev(G), Ed, Qd, ALPHA, bits, want_pre=True, bits_q=bits_q)
     return ref, out, host(Ed), host(Qd)
 
 
@@ -222,3 +222,25 @@ def test_logquant_other_alphas_and_widths(orc, alpha, bits):
     assert np.array_equal(host(gm), cmax)
     assert np.array_equal(host(gh), Fh), first_diff(host(gh), Fh)
     assert np.abs(codes).max() <= (1 << (bits - 1)) - 1
+
+
+@pytest.mark.parametrize("bp,bq", [(8, 4), (4, 8)])
+def test_step_separate_code_widths(orc, bp, bq):
+    """P coded with b_p bits and Q' with b_q bits, against the oracle over 3 steps; given the
+    GPU's own unquantised factors the oracle's quantiser reproduces its codes exactly."""
+    n, m, r = 600, 520, 4
+    say("lq step widths", bp, bq)
+    rng = np.random.default_rng(bp * 10 + bq)
+    E = np.zeros((n, m), np.float32)
+    Q = rng.standard_normal((m, r)).astype(np.float32)
+    for t in range(3):
+        G = (rng.standard_normal((n, m)) * 1e-3
+             + np.outer(rng.standard_normal(n), rng.standard_normal(m)) * 1e-3).astype(np.float32)
+        ref, out, Eg, Qg = _step_both(orc, G, E, Q, bits=bp, bits_q=bq)
+        _check_step(ref, out, Eg, Qg)
+        pc, _, _ = orc.logquant(host(out["p_pre"]), ALPHA, bp)
+        qc, _, _ = orc.logquant(host(out["q_pre"]), ALPHA, bq)
+        assert np.array_equal(host(out["p_codes"]), pc)
+        assert np.array_equal(host(out["q_codes"]), qc)
+        assert np.abs(host(out["q_codes"]).astype(int)).max() <= (1 << (bq - 1)) - 1
+        E, Q = ref["E"], ref["Q"]

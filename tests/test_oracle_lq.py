@@ -189,3 +189,28 @@ def test_payload_bits(orc):
     assert code_bytes * 8 == r * (n + m) * 8
     assert 1 - code_bytes / (4 * r * (n + m)) == 0.75
     assert out["p_colmax"].nbytes + out["q_colmax"].nbytes == 8 * r
+
+
+@pytest.mark.parametrize("bp,bq", [(8, 4), (4, 8), (3, 6)])
+def test_separate_code_widths(orc, bp, bq):
+    """b_p and b_q act on their own factors: the step's codes are exactly the log quantiser's
+    codes of its unquantised P (width b_p) and Q (width b_q), each within its own range, and
+    the error-feedback identity holds whatever the widths; the payload is r(n b_p + m b_q)
+    bits."""
+    rng = np.random.default_rng(40 + bp + bq)
+    n, m, r = 50, 36, 3
+    G = rng.standard_normal((n, m)).astype(np.float32)
+    E = (0.1 * rng.standard_normal((n, m))).astype(np.float32)
+    Q = rng.standard_normal((m, r)).astype(np.float32)
+    out = orc.powersgd_logquant(G, E, Q, 10.0, bp, bits_q=bq)
+    pc, pm, ph = orc.logquant(out["P_pre"], 10.0, bp)
+    qc, qm, qh = orc.logquant(out["Q_pre"], 10.0, bq)
+    assert np.array_equal(out["p_codes"], pc) and np.array_equal(out["q_codes"], qc)
+    assert np.array_equal(out["p_hat"], ph) and np.array_equal(out["Q"], qh)
+    assert np.abs(out["p_codes"]).max() == (1 << (bp - 1)) - 1
+    assert np.abs(out["q_codes"]).max() == (1 << (bq - 1)) - 1
+    M = G.astype(np.float64) + E
+    ghat = out["p_hat"].astype(np.float64) @ out["Q"].astype(np.float64).T
+    assert np.abs(ghat + out["E"] - M).max() < 1e-6 * np.abs(M).max()
+    assert r * (n * bp + m * bq) == sum(int(np.ceil(np.log2(2 * ((1 << (b - 1)) - 1) + 1))) * c
+                                        for b, c in ((bp, r * n), (bq, r * m)))

@@ -76,6 +76,8 @@ MUTATIONS = [
      "E[i * m + j] = (float)((double)E[i * m + j] + acc);"),
     ("power step: Q from the transposed index", "Qacc[j * r + c] += (double)E[i * m + j] * (double)P[i * r + c];",
      "Qacc[j * r + c] += (double)E[i * m + j] * (double)P[i * r + (r - 1 - c)];"),
+    ("power step: P coded with Q's width", "orc_logquant(P, n, r, alpha, bits_p,",
+     "orc_logquant(P, n, r, alpha, bits_q,"),
     ("power step: Q not warm-started", "    memcpy(Q, Qh, (size_t)(m * r) * sizeof(float));\n", "\n"),
 ]
 
