@@ -244,3 +244,25 @@ def test_step_separate_code_widths(orc, bp, bq):
         assert np.array_equal(host(out["q_codes"]), qc)
         assert np.abs(host(out["q_codes"]).astype(int)).max() <= (1 << (bq - 1)) - 1
         E, Q = ref["E"], ref["Q"]
+
+
+def test_error_feedback_bounded_on_gpu():
+    """A long run on the GPU alone (state kept on the device): on a fixed gradient the error
+    matrix stops growing and the running mean of the decoded gradients converges to G."""
+    g = gq()
+    n, m, r = 128, 96, 2   # small enough that the error plateaus within the run
+    say("lq long run", n, m, r)
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    G = torch.randn(n, m, device="cuda", generator=gen)
+    E = torch.zeros_like(G)
+    Q = torch.randn(m, r, device="cuda", generator=gen)
+    total = torch.zeros(n, m, dtype=torch.float64, device="cuda")
+    err, mean_err = {}, {}
+    for t in range(1, 301):
+        out = g.powersgd_logquant(G, E, Q, ALPHA, BITS)
+        total += out["p_hat"].double() @ Q.double().T
+        if t in (150, 300):
+            err[t] = E.double().norm().item()
+            mean_err[t] = (total / t - G.double()).norm().item()
+    assert err[300] <= 1.1 * err[150]
+    assert mean_err[300] <= 0.6 * mean_err[150]

@@ -214,3 +214,27 @@ def test_separate_code_widths(orc, bp, bq):
     assert np.abs(ghat + out["E"] - M).max() < 1e-6 * np.abs(M).max()
     assert r * (n * bp + m * bq) == sum(int(np.ceil(np.log2(2 * ((1 << (b - 1)) - 1) + 1))) * c
                                         for b, c in ((bp, r * n), (bq, r * m)))
+
+
+@pytest.mark.parametrize("r", [1, 4])
+def test_error_feedback_stays_bounded_and_recovers(orc, r):
+    """The review's falsifier for error feedback: the error matrix must not keep growing.  On a
+    fixed gradient G, E_t rises while the compressor catches up and then stays flat, and the
+    running mean of the decoded gradients converges to G like 1/T (sum_t Ghat_t = T G - E_T)."""
+    rng = np.random.default_rng(50 + r)
+    n, m = 64, 48
+    G = rng.standard_normal((n, m)).astype(np.float32)
+    E = np.zeros((n, m), np.float32)
+    Q = rng.standard_normal((m, r)).astype(np.float32)
+    total = np.zeros((n, m))
+    err, mean_err = {}, {}
+    for t in range(1, 201):
+        out = orc.powersgd_logquant(G, E, Q, 10.0, 8)
+        total += out["p_hat"].astype(np.float64) @ out["Q"].astype(np.float64).T
+        E, Q = out["E"], out["Q"]
+        if t in (100, 150, 200):
+            err[t] = np.linalg.norm(E)
+            mean_err[t] = np.linalg.norm(total / t - G)
+    assert err[200] <= 1.1 * err[100] and err[150] <= 1.1 * err[100]
+    assert mean_err[200] <= 0.6 * mean_err[100]
+    assert mean_err[200] < 0.2 * np.linalg.norm(G)
