@@ -353,7 +353,8 @@ __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict
                                                          float *__restrict__ part, int64_t n,
                                                          int64_t m) {
   constexpr int RW = kRowsC / kWavesC;  // rows per wave
-  constexpr int RB = 8;                 // rows per load batch
+  constexpr int RB = RANK <= 4 ? 16 : 8;  // rows per load batch (all of them at low rank)
+  static_assert(RW % RB == 0, "row batches must tile the wave's rows");
   constexpr int COLS = 64 * VEC;        // columns per block
   __shared__ float red[kWavesC][COLS * RANK];
   __shared__ float ptile[kRowsC * RANK];
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict
   }
 }
 
-// Pass 2 (final): Q'[j][c] = sum over chunks, in chunk order (loads issued 8 chunks at a
+// Pass 2 (final): Q'[j][c] = sum over chunks, in chunk order (loads issued 16 chunks at a
 // time), and the column maxima of Q' (as for Pt in k_lq_mtp).
 template <int RANK>
 __global__ __launch_bounds__(256) void k_lq_qsum(const float *__restrict__ part,
@@ -460,13 +461,13 @@ __global__ __launch_bounds__(256) void k_lq_qsum(const float *__restrict__ part,
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) {
     float s = 0.0f;
-    for (int ch0 = 0; ch0 < nchunks; ch0 += 8) {
-      float v[8];
+    for (int ch0 = 0; ch0 < nchunks; ch0 += 16) {
+      float v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 16; ++u)
         v[u] = ch0 + u < nchunks ? part[(int64_t)(ch0 + u) * count + i] : 0.0f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 16; ++u)
         if (ch0 + u < nchunks) s += v[u];
     }
     Qn[i] = s;
@@ -551,23 +552,25 @@ __global__ __launch_bounds__(256) void k_lq_quant_elems(ElemJob J, const float *
   __shared__ float thr[2][128];
   __shared__ float lvl[2][128];
   const int tid = threadIdx.x;
+  const int64_t np = J.n * J.r, nq = J.m * J.r;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + tid;
+  // the element and its column maximum are fetched while the tables are staged
+  const bool live = e < np + nq;
+  const bool isp = e < np;
+  const int64_t i = isp ? e : e - np;
+  const int c = live ? (int)(i % J.r) : 0;
+  const float x = live ? (isp ? J.Pt[i] : J.Qn[i]) : 0.0f;
+  const float mx = live ? __uint_as_float(J.cmax_bits[isp ? c : J.r + c]) : 0.0f;
   if (tid < Lp) thr[0][tid] = tab_p[tid];
   if (tid <= Lp) lvl[0][tid] = tab_p[Lp + tid];
   if (tid < Lq) thr[1][tid] = tab_q[tid];
   if (tid <= Lq) lvl[1][tid] = tab_q[Lq + tid];
   __syncthreads();
-  const int64_t np = J.n * J.r, nq = J.m * J.r;
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + tid;
   if (blockIdx.x == 0 && tid < 2 * J.r) {
     const float mxv = __uint_as_float(J.cmax_bits[tid]);
     if (tid < J.r) J.p_colmax[tid] = mxv; else J.q_colmax[tid - J.r] = mxv;
   }
-  if (e >= np + nq) return;
-  const bool isp = e < np;
-  const int64_t i = isp ? e : e - np;
-  const int c = (int)(i % J.r);
-  const float x = isp ? J.Pt[i] : J.Qn[i];
-  const float mx = __uint_as_float(J.cmax_bits[isp ? c : J.r + c]);
+  if (!live) return;
   const int t = isp ? 0 : 1;
   int k = 0;
   if (mx > 0.0f) {

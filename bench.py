@@ -84,11 +84,15 @@ _SCRUB = []
 
 
 def evict_mall(torch):
-    """Write a 512 MiB buffer (twice the 256 MB Infinity Cache) so that the next timed call
-    finds none of its inputs cached; not timed."""
+    """Write one 512 MiB buffer, then read another (each twice the 256 MB Infinity Cache), so
+    that the next timed call finds none of its inputs cached and no dirty lines left to drain
+    while it runs (the read pushes the written lines out to HBM); not timed."""
     if not _SCRUB:
         _SCRUB.append(torch.zeros(1 << 27, dtype=torch.float32, device="cuda"))
+        _SCRUB.append(torch.ones(1 << 27, dtype=torch.float32, device="cuda"))
+        _SCRUB.append(torch.zeros(1, dtype=torch.float32, device="cuda"))
     _SCRUB[0].add_(1.0)
+    torch.sum(_SCRUB[1], dim=0, keepdim=True, out=_SCRUB[2])
 
 
 def time_calls(torch, fn, iters, warmup=1, median=True):
