@@ -12,6 +12,9 @@
 //   pass 1  E <- G + E and P = E Q              (read G, E; write E)   k_lq_ef_mq
 //   pass 2  Q' = E^T Pt                         (read E)               k_lq_mtp + k_lq_qsum
 //   pass 3  E <- E - Phat Q'hat^T               (read E; write E)      k_lq_ef_update
+// Cache use: G and the incoming E are streamed once (non-temporal loads); the passes over M
+// read it with ordinary loads, so what the column pass brings in can still be cached when the
+// last pass reads it again.
 // Row passes give each block 4 rows so every Q value fetched (from L2: Q is at most
 // m x 8 fp32) is used 4 times, and issue all of a column group's row loads before the first
 // store; Q is read in its own row-major layout (a thread's 4 columns are 4r consecutive
@@ -57,6 +60,16 @@ __device__ __forceinline__ void ldv_nt(const float *p, float (&v)[VEC]) {
     v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
   } else {
     v[0] = __builtin_nontemporal_load(p);
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void ldv(const float *p, float (&v)[VEC]) {
+  if constexpr (VEC == 4) {
+    const f32x4 t = *reinterpret_cast<const f32x4 *>(p);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  } else {
+    v[0] = *p;
   }
 }
 
@@ -371,7 +384,7 @@ __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict
   for (int u = 0; u < RB; ++u) {
     const int64_t row = r0 + w + (int64_t)u * kWavesC;
     if (j < m && row < r1) {
-      ldv_nt<VEC>(M + row * m + j, mv[u]);
+      ldv<VEC>(M + row * m + j, mv[u]);
     } else {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) mv[u][v] = 0.0f;
@@ -410,7 +423,7 @@ __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict
         for (int u = 0; u < RB; ++u) {
           const int64_t row = r0 + w + (int64_t)(u0 + u) * kWavesC;
           if (row < r1) {
-            ldv_nt<VEC>(M + row * m + j, mv[u]);
+            ldv<VEC>(M + row * m + j, mv[u]);
           } else {
 #pragma unroll
             for (int v = 0; v < VEC; ++v) mv[u][v] = 0.0f;
@@ -616,7 +629,7 @@ __global__ __launch_bounds__(kBlockA) void k_lq_ef_update(float *__restrict__ E,
     float mv[kRowsA][VEC];
 #pragma unroll
     for (int rr = 0; rr < kRowsA; ++rr)
-      if (rr < nr) ldv_nt<VEC>(E + (row0 + rr) * m + j, mv[rr]);
+      if (rr < nr) ldv<VEC>(E + (row0 + rr) * m + j, mv[rr]);
     load_q_rows<RANK, VEC>(Qh, j, q);
 #pragma unroll
     for (int rr = 0; rr < kRowsA; ++rr) {
