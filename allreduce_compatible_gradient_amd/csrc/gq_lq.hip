@@ -19,8 +19,9 @@
 // m x 8 fp32) is used 4 times, and issue all of a column group's row loads before the first
 // store; Q is read in its own row-major layout (a thread's 4 columns are 4r consecutive
 // floats), so no transposed copy is made.  The column pass gives each
-// 512-thread block 128 rows x (64*VEC) columns and reduces its 8 waves in LDS, so the
-// per-chunk partials stay a few percent of the pass.
+// 512-thread block 128 rows x (64*VEC) columns (64 rows when that leaves too few blocks to
+// fill the GPU) and reduces its 8 waves in LDS, so the per-chunk partials stay a few percent
+// of the pass.
 // Orthonormalisation: pass 1 also emits each block's r x r Gram contribution (products of the
 // fp32 P values, exact in fp64); k_lq_solve sums them in a fixed order and runs Cholesky-QR
 // twice in r x r space -- T1 from G, then T2 from T1^T G T1, which measures and removes the
@@ -46,8 +47,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsA = 4;      // rows per block in the row passes
 constexpr int kBlockA = 256;
-constexpr int kRowsC = 128;    // rows per chunk in the column pass
-constexpr int kWavesC = 8;     // kRowsC / kWavesC rows per wave, all loaded at once
+constexpr int kWavesC = 8;     // waves per column-pass block
+// Rows per column-pass chunk: 128, or 64 when 128-row chunks would give fewer than
+// kColBlocksMin blocks (the pass is then latency-bound and wants more of them).
+constexpr int kColBlocksMin = 1024;
 // threads of the one-block solve: 16 waves, 8 at rank 8 (so that its r x r work fits in
 // registers)
 template <int RANK>
@@ -356,7 +359,7 @@ __global__ __launch_bounds__(solve_block<RANK>()) void k_lq_solve(const double *
 // is the exact, order-independent maximum.  Wave w takes rows w, w + 8, ... of the chunk,
 // loaded 8 at a time; the 8 waves' sums are combined in LDS in wave order in one round and
 // written as contiguous (j, c) runs.
-template <int RANK, int VEC>
+template <int RANK, int VEC, int ROWSC>
 __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict__ M,
                                                          const float *__restrict__ P,
                                                          const double *__restrict__ T,
@@ -365,18 +368,18 @@ __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict
                                                          unsigned *__restrict__ cmax_bits,
                                                          float *__restrict__ part, int64_t n,
                                                          int64_t m) {
-  constexpr int RW = kRowsC / kWavesC;  // rows per wave
-  constexpr int RB = RANK <= 4 ? 16 : 8;  // rows per load batch (all of them at low rank)
+  constexpr int RW = ROWSC / kWavesC;   // rows per wave
+  constexpr int RB = (RANK <= 4 || RW < 8) ? RW : 8;  // rows per load batch (all of them at low rank)
   static_assert(RW % RB == 0, "row batches must tile the wave's rows");
   constexpr int COLS = 64 * VEC;        // columns per block
   __shared__ float red[kWavesC][COLS * RANK];
-  __shared__ float ptile[kRowsC * RANK];
+  __shared__ float ptile[ROWSC * RANK];
   __shared__ unsigned smax[RANK];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t j0 = (int64_t)blockIdx.x * COLS;
   const int64_t j = j0 + (int64_t)lane * VEC;
-  const int64_t r0 = (int64_t)blockIdx.y * kRowsC;
-  const int64_t r1 = r0 + kRowsC < n ? r0 + kRowsC : n;
+  const int64_t r0 = (int64_t)blockIdx.y * ROWSC;
+  const int64_t r1 = r0 + ROWSC < n ? r0 + ROWSC : n;
   const bool first_tile = blockIdx.x == 0;
   float mv[RB][VEC];
   // the first batch of rows is in flight while the Pt tile is formed
@@ -392,7 +395,7 @@ __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict
   }
   if (first_tile && threadIdx.x < RANK) smax[threadIdx.x] = 0u;
   __syncthreads();
-  for (int e = threadIdx.x; e < kRowsC * RANK; e += kWavesC * 64) {
+  for (int e = threadIdx.x; e < ROWSC * RANK; e += kWavesC * 64) {
     const int64_t row = r0 + e / RANK;
     const int c = e % RANK;
     float o = 0.0f;
@@ -704,7 +707,7 @@ struct StepBufs {
   float *P, *Pt, *part, *Qn, *Ph;
   double *gpart, *T;
   unsigned *cmax_bits;
-  int nchunks;
+  int nchunks, rows_chunk;
   int64_t nblocks;
 };
 
@@ -716,10 +719,13 @@ void launch_step(const LqStepArgs &a, const StepBufs &b, const LqTables &tp, con
                      a.G, a.E, a.Q, b.P, b.gpart, n, m);
   hipLaunchKernelGGL((k_lq_solve<RANK>), dim3(1), dim3(solve_block<RANK>()), 0, s, b.gpart, b.nblocks,
                      b.T, b.cmax_bits);
-  hipLaunchKernelGGL((k_lq_mtp<RANK, VEC>),
-                     dim3((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)b.nchunks),
-                     dim3(kWavesC * 64), 0, s, a.E, b.P, b.T, b.Pt, a.p_pre, b.cmax_bits, b.part,
-                     n, m);
+  const dim3 gcol((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)b.nchunks);
+  if (b.rows_chunk == 64)
+    hipLaunchKernelGGL((k_lq_mtp<RANK, VEC, 64>), gcol, dim3(kWavesC * 64), 0, s, a.E, b.P, b.T,
+                       b.Pt, a.p_pre, b.cmax_bits, b.part, n, m);
+  else
+    hipLaunchKernelGGL((k_lq_mtp<RANK, VEC, 128>), gcol, dim3(kWavesC * 64), 0, s, a.E, b.P,
+                       b.T, b.Pt, a.p_pre, b.cmax_bits, b.part, n, m);
   hipLaunchKernelGGL((k_lq_qsum<RANK>), dim3((unsigned)((m * RANK + 255) / 256)), dim3(256), 0,
                      s, b.part, b.Qn, a.q_pre, b.cmax_bits + RANK, m * RANK, b.nchunks);
   ElemJob je{b.Pt, b.Qn, n, m, RANK, b.cmax_bits, a.p_codes, a.q_codes, a.p_colmax, a.q_colmax,
@@ -759,7 +765,10 @@ hipError_t lq_step(LqState &st, const LqStepArgs &a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int64_t n = a.n, m = a.m, r = a.r;
   StepBufs b;
-  b.nchunks = (int)((n + kRowsC - 1) / kRowsC);
+  const bool vec4 = (m % 4) == 0;
+  const int64_t col_tiles = vec4 ? (m + 255) / 256 : (m + 63) / 64;
+  b.rows_chunk = col_tiles * ((n + 127) / 128) < kColBlocksMin ? 64 : 128;
+  b.nchunks = (int)((n + b.rows_chunk - 1) / b.rows_chunk);
   b.nblocks = (n + kRowsA - 1) / kRowsA;
   const int64_t ng = r * (r + 1) / 2;
   size_t off = 0;
@@ -782,7 +791,6 @@ hipError_t lq_step(LqState &st, const LqStepArgs &a, hipStream_t s) {
   b.Ph = reinterpret_cast<float *>(base + oPh);
   b.T = reinterpret_cast<double *>(base + oT);
   b.cmax_bits = reinterpret_cast<unsigned *>(base + oC);
-  const bool vec4 = (m % 4) == 0;
   switch (a.r) {
     case 1: launch_step_v<1>(a, vec4, b, *tp, *tq, s); break;
     case 2: launch_step_v<2>(a, vec4, b, *tp, *tq, s); break;
