@@ -1,0 +1,100 @@
+"""The hot path under HIP graph capture.
+
+After one eager call has sized a context's scratch and cached its tables, a call only
+launches kernels, so the global norm + fused pass and the LQ-SGD step can be captured into a
+graph and replayed.  Each test captures on a context of its own (a graph keeps pointers to
+that context's scratch), replays several times with eager work and synchronisations in
+between, and checks every replay against the same calls made eagerly: bit for bit, since the
+kernels are deterministic.
+"""
+import numpy as np
+import pytest
+import torch
+
+from allreduce_compatible_gradient_amd import workloads as W
+from tests.gpu_helpers import dev, first_diff, gq, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    from oracle import oracle
+    oracle.lib()
+    return oracle
+
+
+def test_norm_and_fused_pass_in_a_graph(orc):
+    g = gq()
+    say("graph: norm + fused")
+    w = W.reduced("resnet50-161t-f32-K8-exp7")
+    xs = [x.to("cuda") for x in W.gradients(w, "cpu")]
+    gctx, ectx = g.Context(), g.Context()
+    S = torch.empty(w.nseg, dtype=torch.float32, device="cuda")
+    out = torch.empty(w.n, dtype=torch.float32, device="cuda")
+
+    def step(ctx, S_, out_):
+        g.global_norm(xs, w.offsets, scale_out=S_, ctx=ctx)
+        g.fused_mean(xs, S_, w.grid, w.levels, w.bits, 11, w.acc_bits, 0, offsets=w.offsets,
+                     out=out_, ctx=ctx)
+
+    step(gctx, S, out)                       # sizes the scratch, caches the segment table
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(gctx, S, out)
+    S_e = torch.empty_like(S)
+    out_e = torch.empty_like(out)
+    for rep in range(3):
+        for x in xs:                         # eager work between replays: new gradients
+            x.mul_(1.5 if rep % 2 == 0 else -0.75)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(ectx, S_e, out_e)
+        torch.cuda.synchronize()
+        assert torch.equal(S, S_e), "replay %d: scale" % rep
+        assert torch.equal(out, out_e), "replay %d: %s" % (rep, first_diff(host(out), host(out_e)))
+    # and the last replay against the oracle
+    ref = orc.allreduce_mean([host(x) for x in xs], w.grid, w.levels, w.bits, w.acc_bits, 11, 0,
+                             w.offsets, scale=host(S))
+    assert np.array_equal(host(out), ref["mean"]), first_diff(host(out), ref["mean"])
+    del graph
+    gctx.close()
+    ectx.close()
+
+
+def test_lq_step_in_a_graph():
+    g = gq()
+    n, m, r = 1024, 768, 4
+    say("graph: lq step", n, m, r)
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    G = torch.randn(n, m, device="cuda", generator=gen) * 1e-3
+    E0 = torch.randn(n, m, device="cuda", generator=gen) * 1e-4
+    Q0 = torch.randn(m, r, device="cuda", generator=gen)
+    gctx, ectx = g.Context(), g.Context()
+    Eg, Qg = E0.clone(), Q0.clone()
+    Ee, Qe = E0.clone(), Q0.clone()
+    og = g.powersgd_logquant(G, Eg, Qg, W.LQ_ALPHA, W.LQ_BITS, ctx=gctx)   # warm-up: one step
+    oe = g.powersgd_logquant(G, Ee, Qe, W.LQ_ALPHA, W.LQ_BITS, ctx=ectx)
+    torch.cuda.synchronize()
+    assert torch.equal(Eg, Ee) and torch.equal(Qg, Qe)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        og = g.powersgd_logquant(G, Eg, Qg, W.LQ_ALPHA, W.LQ_BITS, out=og, ctx=gctx)
+    # capture does not run the step: both copies are still one step in
+    torch.cuda.synchronize()
+    for rep in range(4):
+        G.mul_(-1.25)                          # a new gradient every step, eagerly
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        oe = g.powersgd_logquant(G, Ee, Qe, W.LQ_ALPHA, W.LQ_BITS, out=oe, ctx=ectx)
+        torch.cuda.synchronize()
+        for k in ("p_codes", "q_codes", "p_colmax", "q_colmax", "p_hat"):
+            assert torch.equal(og[k], oe[k]), "replay %d: %s" % (rep, k)
+        assert torch.equal(Eg, Ee), "replay %d: E" % rep
+        assert torch.equal(Qg, Qe), "replay %d: Q" % rep
+    del graph
+    gctx.close()
+    ectx.close()
