@@ -98,3 +98,30 @@ def test_lq_step_in_a_graph():
     del graph
     gctx.close()
     ectx.close()
+
+
+def test_two_contexts_on_two_streams():
+    """Each context owns its scratch: two contexts driving two streams at once (default
+    priority) give the same results as one after the other."""
+    g = gq()
+    say("two streams")
+    w = W.reduced("flat-1.3G-f32-K8-uniform127")
+    xa = [x.to("cuda") for x in W.gradients(w, "cpu")]
+    xb = [(-2.0 * x).contiguous() for x in xa]
+    ca, cb = g.Context(), g.Context()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = {}
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for name, xs, ctx, st in (("a", xa, ca, sa), ("b", xb, cb, sb)):
+            with torch.cuda.stream(st):
+                S, _ = g.global_norm(xs, ctx=ctx)
+                outs[name] = g.fused_mean(xs, S, w.grid, w.levels, w.bits, 3, w.acc_bits, ctx=ctx)
+    torch.cuda.synchronize()
+    for name, xs in (("a", xa), ("b", xb)):
+        S, _ = g.global_norm(xs)
+        ref = g.fused_mean(xs, S, w.grid, w.levels, w.bits, 3, w.acc_bits)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[name], ref), name
+    ca.close()
+    cb.close()
