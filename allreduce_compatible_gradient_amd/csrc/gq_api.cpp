@@ -388,6 +388,87 @@ GQ_EXPORT gq_status gq_dequantize(gq_ctx *c, const void *sums, int32_t acc_bits,
   return e == hipSuccess ? GQ_OK : hip_fail(c, e, "dequantize launch");
 }
 
+// ---------------------------------------------------------------- summable wire payload
+namespace {
+int64_t wire_offset(int32_t grid, int32_t levels) {
+  return grid == GQ_EXP ? ((int64_t)1 << (levels - 1)) : (int64_t)levels;
+}
+
+bool wire_codec_ok(int32_t grid, int32_t levels) {
+  if (grid == GQ_UNIFORM) return levels >= 1 && levels <= 127;
+  if (grid == GQ_EXP) return levels >= 1 && levels <= 30;
+  return false;
+}
+}  // namespace
+
+GQ_EXPORT int32_t gq_wire_lane_bytes(int32_t grid, int32_t levels, int32_t world) {
+  if (!wire_codec_ok(grid, levels) || world < 1 || world > 65536) return 0;
+  const int64_t top = (int64_t)world * 2 * wire_offset(grid, levels);
+  for (int32_t w = 1; w <= 4; w *= 2)
+    if (top <= (int64_t)((((uint64_t)1) << (8 * w)) - 1)) return w;
+  return 0;
+}
+
+GQ_EXPORT gq_status gq_quantize_wire(gq_ctx *c, const void *grad, int32_t dtype, int64_t n,
+                                     const int64_t *offsets, int32_t nseg, const float *scale,
+                                     int32_t grid, int32_t levels, uint64_t seed,
+                                     uint32_t worker, uint32_t index_base, int32_t world,
+                                     void *payload, void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(check_dtype(c, dtype, "dtype"));
+  const int32_t wb = gq_wire_lane_bytes(grid, levels, world);
+  if (wb == 0)
+    return fail(c, GQ_EINVAL, "no lane width holds %d workers at grid %d, levels %d", world,
+                grid, levels);
+  TRY(check_ptr(c, grad, "grad", n == 0));
+  TRY(check_ptr(c, scale, "scale"));
+  TRY(check_ptr(c, payload, "payload", n == 0));
+  TRY(check_counter(c, n, index_base));
+  TileView tv;
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  gq::WireQuantArgs a;
+  a.grad = grad;
+  a.scale = scale;
+  a.payload = static_cast<uint8_t *>(payload);
+  a.tv = tv;
+  a.levels = levels;
+  a.offset = (int32_t)wire_offset(grid, levels);
+  a.key_mix = key_mix(worker_key(seed, worker));
+  a.index_base = index_base;
+  hipError_t e = gq::launch_quantize_wire(a, dtype, grid, wb, s);
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "quantize_wire launch");
+}
+
+GQ_EXPORT gq_status gq_dequantize_wire(gq_ctx *c, const void *payload, int64_t n,
+                                       const int64_t *offsets, int32_t nseg,
+                                       const float *scale, int32_t grid, int32_t levels,
+                                       int32_t world, int32_t out_dtype, void *out,
+                                       void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t wb = gq_wire_lane_bytes(grid, levels, world);
+  if (wb == 0)
+    return fail(c, GQ_EINVAL, "no lane width holds %d workers at grid %d, levels %d", world,
+                grid, levels);
+  TRY(check_dtype(c, out_dtype, "out_dtype"));
+  TRY(check_ptr(c, payload, "payload", n == 0));
+  TRY(check_ptr(c, scale, "scale"));
+  TRY(check_ptr(c, out, "out", n == 0));
+  TileView tv;
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  gq::WireDequantArgs a;
+  a.payload = static_cast<const uint8_t *>(payload);
+  a.scale = scale;
+  a.out = out;
+  a.tv = tv;
+  a.world_offset = (int64_t)world * wire_offset(grid, levels);
+  a.out_dtype = out_dtype;
+  a.denom = decode_denominator(grid, levels, world);
+  hipError_t e = gq::launch_dequantize_wire(a, wb, s);
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "dequantize_wire launch");
+}
+
 GQ_EXPORT gq_status gq_fused_mean(gq_ctx *c, const void *const *grads, int32_t K, int32_t dtype,
                                   int64_t n, const int64_t *offsets, int32_t nseg,
                                   const float *scale, int32_t grid, int32_t levels, int32_t bits,

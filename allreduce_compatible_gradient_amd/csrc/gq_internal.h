@@ -74,6 +74,27 @@ struct DequantArgs {
   double denom;           // D: s*K (uniform) or K*2^(E-1) (exponential)
 };
 
+struct WireQuantArgs {
+  const void *grad;
+  const float *scale;
+  uint8_t *payload;
+  TileView tv;
+  int32_t levels;
+  int32_t offset;         // o: s (uniform) or 2^(E-1) (exponential)
+  uint32_t key_mix;
+  uint32_t index_base;
+};
+
+struct WireDequantArgs {
+  const uint8_t *payload;
+  const float *scale;
+  void *out;
+  TileView tv;
+  int64_t world_offset;   // world * o
+  int32_t out_dtype;
+  double denom;
+};
+
 struct FusedArgs {
   const void *grads[kMaxWorkers];
   uint8_t *codes[kMaxWorkers];   // all nullptr unless codes are materialised
@@ -98,6 +119,9 @@ hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, hipStre
 hipError_t launch_accumulate(const AccArgs &a, int grid, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
 hipError_t launch_fused(const FusedArgs &a, int dtype, int grid, hipStream_t s);
+hipError_t launch_quantize_wire(const WireQuantArgs &a, int dtype, int grid, int wb,
+                                hipStream_t s);
+hipError_t launch_dequantize_wire(const WireDequantArgs &a, int wb, hipStream_t s);
 hipError_t launch_clear_u32(unsigned *p, int count, hipStream_t s);
 
 }  // namespace gq

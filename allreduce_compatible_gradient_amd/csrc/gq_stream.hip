@@ -588,6 +588,176 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(DequantArgs a) {
   }
 }
 
+// ================================================================ summable wire payload
+// Element e travels as the unsigned lane lin_e + o of WB bytes at byte e*WB (little-endian),
+// o = s or 2^(E-1), WB wide enough that `world` payloads added as unsigned 32-bit words never
+// carry between lanes.  A part is P lanes at byte e0*WB (aligned: e0 is a multiple of P).
+template <int P, int WB>
+__device__ __forceinline__ void store_lanes(uint8_t *payload, int64_t e0, int cnt, int64_t n,
+                                            const uint32_t (&v)[P]) {
+  if (cnt == P) {
+    if constexpr (WB == 1) {
+      uint32_t w[P / 4];
+#pragma unroll
+      for (int i = 0; i < P / 4; ++i)
+        w[i] = v[4 * i] | (v[4 * i + 1] << 8) | (v[4 * i + 2] << 16) | (v[4 * i + 3] << 24);
+      if constexpr (P == 4)
+        __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t *>(payload + e0));
+      else
+        __builtin_nontemporal_store((u32x2){w[0], w[1]}, reinterpret_cast<u32x2 *>(payload + e0));
+    } else if constexpr (WB == 2) {
+      uint32_t w[P / 2];
+#pragma unroll
+      for (int i = 0; i < P / 2; ++i) w[i] = v[2 * i] | (v[2 * i + 1] << 16);
+      if constexpr (P == 4)
+        __builtin_nontemporal_store((u32x2){w[0], w[1]},
+                                    reinterpret_cast<u32x2 *>(payload + 2 * e0));
+      else
+        __builtin_nontemporal_store((u32x4){w[0], w[1], w[2], w[3]},
+                                    reinterpret_cast<u32x4 *>(payload + 2 * e0));
+    } else {
+#pragma unroll
+      for (int i = 0; i < P / 4; ++i)
+        __builtin_nontemporal_store((u32x4){v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]},
+                                    reinterpret_cast<u32x4 *>(payload + 4 * (e0 + 4 * i)));
+    }
+  } else {
+    // the buffer's last part: its lanes byte by byte, then the zero padding to 4 bytes
+#pragma unroll
+    for (int e = 0; e < P; ++e)
+      if (e < cnt)
+#pragma unroll
+        for (int b = 0; b < WB; ++b) payload[(e0 + e) * WB + b] = (uint8_t)(v[e] >> (8 * b));
+    const int64_t end = n * WB, padded = (end + 3) / 4 * 4;
+    for (int64_t q = end; q < padded; ++q) payload[q] = 0;
+  }
+}
+
+template <int P, int WB>
+__device__ __forceinline__ void load_lanes(const uint8_t *payload, int64_t e0, int cnt,
+                                           uint32_t (&v)[P]) {
+  if (cnt == P) {
+    if constexpr (WB == 1) {
+      uint32_t w[P / 4];
+      if constexpr (P == 4) {
+        w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(payload + e0));
+      } else {
+        const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(payload + e0));
+        w[0] = t.x;
+        w[1] = t.y;
+      }
+#pragma unroll
+      for (int i = 0; i < P; ++i) v[i] = (w[i / 4] >> (8 * (i % 4))) & 0xFFu;
+    } else if constexpr (WB == 2) {
+      uint32_t w[P / 2];
+      if constexpr (P == 4) {
+        const u32x2 t =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(payload + 2 * e0));
+        w[0] = t.x;
+        w[1] = t.y;
+      } else {
+        const u32x4 t =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(payload + 2 * e0));
+        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+      }
+#pragma unroll
+      for (int i = 0; i < P; ++i) v[i] = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+    } else {
+#pragma unroll
+      for (int i = 0; i < P / 4; ++i) {
+        const u32x4 t = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(payload + 4 * (e0 + 4 * i)));
+        v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      v[e] = 0;
+      if (e < cnt)
+#pragma unroll
+        for (int b = 0; b < WB; ++b) v[e] |= (uint32_t)payload[(e0 + e) * WB + b] << (8 * b);
+    }
+  }
+}
+
+// One worker's quantisation (identical to k_quantize_pack) written as wire lanes.
+template <int DT, int GRID, int WB>
+__global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
+  constexpr int P = DT == 0 ? 4 : 8;
+  constexpr int NP = kChunk / (64 * P);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const float sf = (float)a.levels;
+  const float two_em1 = ldexpf(1.0f, a.levels - 1);
+  for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
+    int64_t begin;
+    int len, seg;
+    tile_of(a.tv, t, kTile, begin, len, seg);
+    const SegQ q = seg_quant<GRID>(a.scale[seg], a.levels);
+    const int nch = (len + kChunk - 1) / kChunk;
+    for (int ci = wv; ci < nch; ci += kBlock / 64) {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int o = part_offset<P>(ci, j, lane);
+        const int cnt = min(P, len - o);
+        if (cnt <= 0) continue;
+        const int64_t e0 = begin + o;
+        uint32_t v[P];
+        if (q.valid) {
+          float x[P];
+          load_part<DT, P>(a.grad, e0, cnt, x);
+          const uint32_t ctr = a.index_base + (uint32_t)e0;
+#pragma unroll
+          for (int e = 0; e < P; ++e) {
+            const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+            int32_t lin;
+            if constexpr (GRID == 0)
+              lin = (int32_t)copysignf(quant_uniform_mag(x[e], q.inv, sf, h), x[e]);
+            else
+              lin = exp_lin(quant_exp_index(x[e], q.inv, a.levels, two_em1, h), x[e] < 0.0f);
+            v[e] = (uint32_t)(lin + a.offset);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < P; ++e) v[e] = (uint32_t)a.offset;
+        }
+        store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
+      }
+    }
+  }
+}
+
+// A summed payload of `world` workers back to the mean: sum = lane - world*o, then the decode
+// of k_dequantize.
+template <int P, int WB>
+__global__ __launch_bounds__(kBlock) void k_dequantize_wire(WireDequantArgs a) {
+  constexpr int NP = kChunk / (64 * P);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
+    int64_t begin;
+    int len, seg;
+    tile_of(a.tv, t, kTile, begin, len, seg);
+    const float f = seg_decode(a.scale[seg], a.denom);
+    const int nch = (len + kChunk - 1) / kChunk;
+    for (int ci = wv; ci < nch; ci += kBlock / 64) {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int o = part_offset<P>(ci, j, lane);
+        const int cnt = min(P, len - o);
+        if (cnt <= 0) continue;
+        const int64_t e0 = begin + o;
+        uint32_t v[P];
+        load_lanes<P, WB>(a.payload, e0, cnt, v);
+        float m[P];
+#pragma unroll
+        for (int e = 0; e < P; ++e)
+          m[e] = (float)(int32_t)((int64_t)v[e] - a.world_offset) * f;
+        store_mean<P>(a.out, a.out_dtype, e0, cnt, m);
+      }
+    }
+  }
+}
+
 // ================================================================ fused pass
 // For each element: the K workers' quantisations in registers, their integer sum, one decode.
 // Workers are processed in batches of KB whose loads are all issued before any arithmetic.
@@ -770,6 +940,40 @@ hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(k_dequantize<8>, g, dim3(kBlock), 0, s, a);
   else
     hipLaunchKernelGGL(k_dequantize<4>, g, dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int GRID>
+static void launch_qw(const WireQuantArgs &a, int wb, dim3 g, hipStream_t s) {
+  if (wb == 1) hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 1>), g, dim3(kBlock), 0, s, a);
+  if (wb == 2) hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 2>), g, dim3(kBlock), 0, s, a);
+  if (wb == 4) hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 4>), g, dim3(kBlock), 0, s, a);
+}
+
+hipError_t launch_quantize_wire(const WireQuantArgs &a, int dtype, int grid, int wb,
+                                hipStream_t s) {
+  if (a.tv.ntiles == 0) return hipSuccess;
+  const dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+  if (dtype == 0 && grid == 0) launch_qw<0, 0>(a, wb, g, s);
+  if (dtype == 0 && grid == 1) launch_qw<0, 1>(a, wb, g, s);
+  if (dtype == 1 && grid == 0) launch_qw<1, 0>(a, wb, g, s);
+  if (dtype == 1 && grid == 1) launch_qw<1, 1>(a, wb, g, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_wire(const WireDequantArgs &a, int wb, hipStream_t s) {
+  if (a.tv.ntiles == 0) return hipSuccess;
+  const dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+  // 16-byte output stores: 8 elements per part for bf16 output, 4 for fp32
+  if (a.out_dtype == 1) {
+    if (wb == 1) hipLaunchKernelGGL((k_dequantize_wire<8, 1>), g, dim3(kBlock), 0, s, a);
+    if (wb == 2) hipLaunchKernelGGL((k_dequantize_wire<8, 2>), g, dim3(kBlock), 0, s, a);
+    if (wb == 4) hipLaunchKernelGGL((k_dequantize_wire<8, 4>), g, dim3(kBlock), 0, s, a);
+  } else {
+    if (wb == 1) hipLaunchKernelGGL((k_dequantize_wire<4, 1>), g, dim3(kBlock), 0, s, a);
+    if (wb == 2) hipLaunchKernelGGL((k_dequantize_wire<4, 2>), g, dim3(kBlock), 0, s, a);
+    if (wb == 4) hipLaunchKernelGGL((k_dequantize_wire<4, 4>), g, dim3(kBlock), 0, s, a);
+  }
   return hipGetLastError();
 }
 

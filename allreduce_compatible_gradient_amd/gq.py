@@ -42,6 +42,10 @@ _SIGS = {
     "gq_fused_mean": (_i32, [_p, _p, _i32, _i32, _i64, _p, _i32, _p, _i32, _i32, _i32, _u64, _u32,
                              _i32, _p, _p, _i32, _p, _p]),
     "gq_logquant": (_i32, [_p, _p, _i64, _i32, _d, _i32, _p, _p, _p, _p]),
+    "gq_wire_lane_bytes": (_i32, [_i32, _i32, _i32]),
+    "gq_quantize_wire": (_i32, [_p, _p, _i32, _i64, _p, _i32, _p, _i32, _i32, _u64, _u32, _u32,
+                                _i32, _p, _p]),
+    "gq_dequantize_wire": (_i32, [_p, _p, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _p, _p]),
     "gq_powersgd_logquant": (_i32, [_p, _p, _p, _p, _i64, _i64, _i32, _d, _i32, _i32, _p, _p,
                                     _p, _p, _p, _p, _p, _p]),
 }
@@ -200,6 +204,44 @@ def dequantize(sums, scale, grid, levels, K, out_dtype=F32, offsets=None, out=No
     ctx.check(_lib.gq_dequantize(ctx.handle, _dev(sums, "sums", (torch.int16, torch.int32)),
                                  acc_bits, n, off, nseg, _dev(scale, "scale", torch.float32),
                                  grid, levels, K, out_dtype, _dev(out, "out"), _stream()))
+    return out
+
+
+def wire_lane_bytes(grid, levels, world) -> int:
+    """Bytes per element of the summable wire payload for `world` workers (0: none fits)."""
+    return int(_lib.gq_wire_lane_bytes(grid, levels, world))
+
+
+def wire_bytes(n: int, grid, levels, world) -> int:
+    return (n * wire_lane_bytes(grid, levels, world) + 3) // 4 * 4
+
+
+def quantize_wire(grad, scale, grid, levels, seed, worker, world, index_base=0, offsets=None,
+                  payload=None, ctx: Optional[Context] = None):
+    """One worker's quantisation as a summable payload (uint8 tensor, a multiple of 4 bytes)."""
+    ctx = ctx or context()
+    n = grad.numel()
+    off, nseg, keep = _offsets(offsets, n)
+    if payload is None:
+        payload = torch.empty(max(wire_bytes(n, grid, levels, world), 4), dtype=torch.uint8,
+                              device=grad.device)
+    ctx.check(_lib.gq_quantize_wire(ctx.handle, _dev(grad, "grad"), _elt(grad), n, off, nseg,
+                                    _dev(scale, "scale", torch.float32), grid, levels, seed,
+                                    worker, index_base, world,
+                                    _dev(payload, "payload", torch.uint8), _stream()))
+    return payload
+
+
+def dequantize_wire(payload, n, scale, grid, levels, world, out_dtype=F32, offsets=None,
+                    out=None, ctx: Optional[Context] = None):
+    """The mean from the word-wise sum of `world` payloads."""
+    ctx = ctx or context()
+    off, nseg, keep = _offsets(offsets, n)
+    if out is None:
+        out = torch.empty(n, dtype=_torch_dtype(out_dtype), device=payload.device)
+    ctx.check(_lib.gq_dequantize_wire(ctx.handle, _dev(payload, "payload", torch.uint8), n, off,
+                                      nseg, _dev(scale, "scale", torch.float32), grid, levels,
+                                      world, out_dtype, _dev(out, "out"), _stream()))
     return out
 
 

@@ -159,7 +159,19 @@ def rows_flat(torch, gq, grads, S, w, row, it):
                                                  codes=codes, sums=sums, out=out), it)
     row("fused_parity_mode_codes_sums", ms, K * n * 4 + 4 * n + K * n + 2 * n,
         "fused pass that also writes every worker's codes and the int16 sums")
-    del codes, sums, out
+    del codes, sums
+    # the summable wire payload (2-byte lanes for 8 workers at s = 127) and its decode
+    wb = gq.wire_lane_bytes(w.grid, w.levels, K)
+    pay = torch.empty(gq.wire_bytes(n, w.grid, w.levels, K), dtype=torch.uint8, device="cuda")
+    ms = time_calls(torch, lambda: gq.quantize_wire(grads[0], S, w.grid, w.levels, 1, 0, K,
+                                                    payload=pay), it)
+    row("quantize_wire_1.3G_s127_%dB_lanes" % wb, ms, n * 4 + n * wb,
+        "one worker: fp32 in, summable payload out")
+    ms = time_calls(torch, lambda: gq.dequantize_wire(pay, n, S, w.grid, w.levels, K, 0,
+                                                      out=out), it)
+    row("dequantize_wire_%dB_lanes_to_f32" % wb, ms, n * wb + 4 * n,
+        "summed payload in, fp32 mean out")
+    del pay, out
     torch.cuda.empty_cache()
 
 
@@ -194,7 +206,14 @@ def rows_gpt2(torch, gq, W, row):
     ms = time_calls(torch, lambda: gq.fused_mean(g3, S3, w3.grid, w3.levels, w3.bits, 1, 16, 1,
                                                  offsets=w3.offsets, out=o3), 7)
     row("fused_gpt2_bf16_s7_K16", ms, w3.K * w3.n * 2 + w3.n * 2, "fused pass, bf16 in and out")
-    del g3, o3
+    wb = gq.wire_lane_bytes(w3.grid, w3.levels, w3.K)
+    p3 = torch.empty(gq.wire_bytes(w3.n, w3.grid, w3.levels, w3.K), dtype=torch.uint8,
+                     device="cuda")
+    ms = time_calls(torch, lambda: gq.quantize_wire(g3[0], S3, w3.grid, w3.levels, 1, 0, w3.K,
+                                                    offsets=w3.offsets, payload=p3), 7)
+    row("quantize_wire_gpt2_bf16_%dB_lanes" % wb, ms, w3.n * 2 + w3.n * wb,
+        "one worker: bf16 in, summable payload out (16 workers, s = 7)")
+    del g3, o3, p3
     torch.cuda.empty_cache()
 
 

@@ -129,6 +129,32 @@ gq_status gq_fused_mean(gq_ctx *ctx, const void *const *grads, int32_t K, int32_
                         uint32_t index_base, int32_t acc_bits, uint8_t *const *codes_or_null,
                         void *sums_or_null, int32_t out_dtype, void *out, void *stream);
 
+/* Summable wire payload, for an Allreduce whose sum runs on unsigned 32-bit words (RCCL has
+ * no 16-bit integer sum).  Reading of the Global-QSGD abstract ("Allreduce-compatible": the
+ * workers' codes are summed by the collective): element i travels as the unsigned lane
+ * lin_i + o of W bytes, little-endian, at byte i*W, with o = s (uniform; lin = the signed
+ * level) or 2^(E-1) (exponential; lin = sign*2^(j-1)); W is the smallest of 1, 2, 4 bytes
+ * whose range holds world*2o, so `world` payloads added word by word (mod 2^32) never carry
+ * from one lane into the next and each summed lane is sum_k lin + world*o.  Returns W, or 0
+ * when no width fits or an argument is out of range (uniform 1..127, exponential 1..30,
+ * 1 <= world <= 65536). */
+int32_t gq_wire_lane_bytes(int32_t grid, int32_t levels, int32_t world);
+
+/* Quantise one worker exactly as gq_quantize_pack (same scale, seed, worker and counters,
+ * hence the same levels) and write its wire payload: round_up(n*W, 4) bytes, the padding
+ * zero.  GQ_EINVAL when gq_wire_lane_bytes is 0. */
+gq_status gq_quantize_wire(gq_ctx *ctx, const void *grad, int32_t dtype, int64_t n,
+                           const int64_t *offsets, int32_t nseg, const float *scale,
+                           int32_t grid, int32_t levels, uint64_t seed, uint32_t worker,
+                           uint32_t index_base, int32_t world, void *payload, void *stream);
+
+/* Decode the word-wise sum of `world` payloads: sum_i = lane_i - world*o, then as
+ * gq_dequantize with K = world: mean_i = fp32(sum_i) * fp32(S_g / D). */
+gq_status gq_dequantize_wire(gq_ctx *ctx, const void *payload, int64_t n,
+                             const int64_t *offsets, int32_t nseg, const float *scale,
+                             int32_t grid, int32_t levels, int32_t world, int32_t out_dtype,
+                             void *out, void *stream);
+
 /* LQ-SGD log quantiser on each column of F (rows x r, row-major fp32; LQ-SGD review, Eq. 5
  * with the max-magnitude normalisation of referee major comment 1, decode by Eq. 6):
  *   m_c = max_i |F_ic|;  y = fp32(|F_ic| / m_c);

@@ -314,6 +314,66 @@ int64_t orc_accumulate(const uint8_t *const *codes, int32_t K, int64_t n, int32_
     return over;
 }
 
+/* ======================= summable wire payload ======================= */
+
+static int64_t wire_offset(int32_t grid, int32_t levels)
+{
+    return grid == ORC_EXP ? ((int64_t)1 << (levels - 1)) : (int64_t)levels;
+}
+
+int32_t orc_wire_lane_bytes(int32_t grid, int32_t levels, int32_t world)
+{
+    int64_t top = (int64_t)world * 2 * wire_offset(grid, levels);
+    int32_t w;
+    for (w = 1; w <= 4; w *= 2)
+        if (top <= (int64_t)(((uint64_t)1 << (8 * w)) - 1))
+            return w;
+    return 0;
+}
+
+void orc_wire_encode(const int32_t *q, int64_t n, int32_t grid, int32_t levels, int32_t world,
+                     uint8_t *payload)
+{
+    int32_t w = orc_wire_lane_bytes(grid, levels, world), b;
+    int64_t o = wire_offset(grid, levels), i, nbytes = (n * w + 3) / 4 * 4;
+    memset(payload, 0, (size_t)nbytes);
+    for (i = 0; i < n; ++i) {
+        uint64_t lane = (uint64_t)(orc_lin(grid, q[i]) + o);
+        for (b = 0; b < w; ++b)
+            payload[i * w + b] = (uint8_t)(lane >> (8 * b));
+    }
+}
+
+void orc_wire_sum(const uint8_t *const *payloads, int32_t K, int64_t nbytes, uint8_t *out)
+{
+    int64_t t;
+    int32_t k, b;
+    for (t = 0; t < nbytes / 4; ++t) {
+        uint32_t acc = 0;
+        for (k = 0; k < K; ++k) {
+            uint32_t word = 0;
+            for (b = 0; b < 4; ++b)
+                word |= (uint32_t)payloads[k][4 * t + b] << (8 * b);
+            acc += word; /* wraps mod 2^32, as an unsigned 32-bit sum does */
+        }
+        for (b = 0; b < 4; ++b)
+            out[4 * t + b] = (uint8_t)(acc >> (8 * b));
+    }
+}
+
+void orc_wire_decode(const uint8_t *payload, int64_t n, int32_t grid, int32_t levels,
+                     int32_t world, int32_t *sums)
+{
+    int32_t w = orc_wire_lane_bytes(grid, levels, world), b;
+    int64_t o = wire_offset(grid, levels), i;
+    for (i = 0; i < n; ++i) {
+        uint64_t lane = 0;
+        for (b = 0; b < w; ++b)
+            lane |= (uint64_t)payload[i * w + b] << (8 * b);
+        sums[i] = (int32_t)((int64_t)lane - (int64_t)world * o);
+    }
+}
+
 /* ======================= decode ======================= */
 
 float orc_decode_factor(int32_t grid, int32_t levels, int32_t K, float S)

@@ -89,6 +89,22 @@ int64_t orc_lin(int32_t grid, int32_t signed_level);
 int64_t orc_accumulate(const uint8_t *const *codes, int32_t K, int64_t n, int32_t grid,
                        int32_t bits, int32_t acc_bits, void *sums);
 
+/* ---------------- summable wire payload ---------------- */
+/* Reading of "the codes can be summed by Allreduce" for a collective whose sum is on
+ * unsigned 32-bit words: element i is stored as the unsigned lane lin_i + o (o = s, or
+ * 2^(E-1) on the exponential grid) of W bytes, little-endian, element i at byte i*W.  W is
+ * the smallest of 1, 2, 4 whose range holds world * 2o, so adding `world` payloads word by
+ * word never carries from one lane into the next.  Returns 0 when no width fits. */
+int32_t orc_wire_lane_bytes(int32_t grid, int32_t levels, int32_t world);
+/* Payload of signed levels q[0..n): round_up(n*W, 4) bytes, the padding zero. */
+void orc_wire_encode(const int32_t *q, int64_t n, int32_t grid, int32_t levels, int32_t world,
+                     uint8_t *payload);
+/* out = word-wise sum (mod 2^32) of K payloads of nbytes bytes (a multiple of 4). */
+void orc_wire_sum(const uint8_t *const *payloads, int32_t K, int64_t nbytes, uint8_t *out);
+/* sums_i = lane_i - world * o: the integer sum of the world workers' linear values. */
+void orc_wire_decode(const uint8_t *payload, int64_t n, int32_t grid, int32_t levels,
+                     int32_t world, int32_t *sums);
+
 /* ---------------- decode of the mean ---------------- */
 /* f = fp32(S / D) with the division in fp64, D = s*K (uniform) or K*2^(E-1) (exponential);
  * 0 when S is not a positive finite number. */

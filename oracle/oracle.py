@@ -74,6 +74,10 @@ def lib():
             "orc_lin": (i64, [i32, i32]),
             "orc_accumulate": (i64, [p, i32, i64, i32, i32, i32, p]),
             "orc_decode_factor": (f, [i32, i32, i32, f]),
+            "orc_wire_lane_bytes": (i32, [i32, i32, i32]),
+            "orc_wire_encode": (None, [p, i64, i32, i32, i32, p]),
+            "orc_wire_sum": (None, [p, i32, i64, p]),
+            "orc_wire_decode": (None, [p, i64, i32, i32, i32, p]),
             "orc_f32_to_bf16": (C.c_uint16, [f]),
             "orc_dequantize": (None, [p, i32, i64, p, i32, p, i32, i32, i32, i32, p]),
             "orc_logq_index": (i32, [f, d, i32]),
@@ -217,6 +221,34 @@ def accumulate(codes_list, n, grid, bits, acc_bits):
     over = lib().orc_accumulate(_ptrs(codes_list), len(codes_list), n, grid, bits, acc_bits,
                                 _ptr(out))
     return out, int(over)
+
+
+def wire_lane_bytes(grid, levels, world) -> int:
+    return lib().orc_wire_lane_bytes(grid, levels, world)
+
+
+def wire_encode(q, grid, levels, world):
+    """Summable payload (uint8 array, a multiple of 4 bytes) of signed levels q."""
+    q = _c(q, np.int32)
+    w = wire_lane_bytes(grid, levels, world)
+    out = np.empty((q.size * w + 3) // 4 * 4, np.uint8)
+    lib().orc_wire_encode(_ptr(q), q.size, grid, levels, world, _ptr(out))
+    return out
+
+
+def wire_sum(payloads):
+    payloads = [_c(p, np.uint8) for p in payloads]
+    out = np.empty(payloads[0].size, np.uint8)
+    lib().orc_wire_sum(_ptrs(payloads), len(payloads), payloads[0].size, _ptr(out))
+    return out
+
+
+def wire_decode(payload, n, grid, levels, world):
+    """Integer sums (int32) held by a summed payload."""
+    payload = _c(payload, np.uint8)
+    out = np.empty(n, np.int32)
+    lib().orc_wire_decode(_ptr(payload), n, grid, levels, world, _ptr(out))
+    return out
 
 
 def decode_factor(grid, levels, K, S) -> float:

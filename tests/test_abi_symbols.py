@@ -26,7 +26,8 @@ def test_header_declares_the_path():
     names = _declared()
     for want in ("gq_global_norm", "gq_quantize_pack", "gq_accumulate_codes", "gq_dequantize",
                  "gq_fused_mean", "gq_logquant", "gq_powersgd_logquant", "gq_create",
-                 "gq_destroy", "gq_last_error", "gq_read_status", "gq_version"):
+                 "gq_destroy", "gq_last_error", "gq_read_status", "gq_version",
+                 "gq_wire_lane_bytes", "gq_quantize_wire", "gq_dequantize_wire"):
         assert want in names
 
 
@@ -65,3 +66,18 @@ def test_oracle_and_product_share_no_code():
         if f.endswith(".py"):
             txt = open(os.path.join(PKG, f)).read()
             assert "import oracle" not in txt and "from oracle" not in txt, f
+
+
+def test_wire_lane_width_rule_matches_the_oracle():
+    """gq_wire_lane_bytes is pure host code: callable without a GPU."""
+    _ensure_built()
+    from oracle import oracle
+    lib = ctypes.CDLL(LIB)
+    lib.gq_wire_lane_bytes.restype = ctypes.c_int32
+    lib.gq_wire_lane_bytes.argtypes = [ctypes.c_int32] * 3
+    for grid, top in ((0, 127), (1, 30)):
+        for levels in range(1, top + 1):
+            for world in (1, 2, 3, 8, 16, 64, 1000, 65536):
+                assert lib.gq_wire_lane_bytes(grid, levels, world) == \
+                    oracle.wire_lane_bytes(grid, levels, world), (grid, levels, world)
+    assert lib.gq_wire_lane_bytes(0, 128, 1) == 0 and lib.gq_wire_lane_bytes(0, 7, 0) == 0

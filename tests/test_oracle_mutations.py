@@ -17,7 +17,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "gq_oracle.c")
-PIN_SUITES = ["tests/test_oracle_rng.py", "tests/test_oracle_quant.py", "tests/test_oracle_lq.py"]
+PIN_SUITES = ["tests/test_oracle_rng.py", "tests/test_oracle_quant.py", "tests/test_oracle_lq.py",
+              "tests/test_oracle_wire.py"]
 
 # (name, text in gq_oracle.c, replacement)
 MUTATIONS = [
@@ -59,6 +60,14 @@ MUTATIONS = [
      "return (uint16_t)hi;"),
     ("bf16: truncation", "    if (dv - dl < dh - dv)\n        return (uint16_t)lo;",
      "    if (1)\n        return (uint16_t)lo;"),
+    ("wire: lane offset dropped", "uint64_t lane = (uint64_t)(orc_lin(grid, q[i]) + o);",
+     "uint64_t lane = (uint64_t)(orc_lin(grid, q[i]));"),
+    ("wire: big-endian lanes", "payload[i * w + b] = (uint8_t)(lane >> (8 * b));",
+     "payload[i * w + b] = (uint8_t)(lane >> (8 * (w - 1 - b)));"),
+    ("wire: lanes twice as wide as needed", "if (top <= (int64_t)(((uint64_t)1 << (8 * w)) - 1))",
+     "if (top <= (int64_t)(((uint64_t)1 << (8 * w - 1)) - 1))"),
+    ("wire: decode without the world's offset", "sums[i] = (int32_t)((int64_t)lane - (int64_t)world * o);",
+     "sums[i] = (int32_t)((int64_t)lane - o);"),
     ("log quantiser: natural log of alpha as the base", "/ log1p(alpha);", "/ log(alpha);"),
     ("log quantiser: rounding down", "double k = floor(z * (double)L + 0.5);",
      "double k = floor(z * (double)L);"),
