@@ -1,5 +1,6 @@
 // gq_stream.hip -- gfx950 kernels of the Global-QSGD path: global norm, stochastic
-// quantisation + packing, integer sum of codes, decode of the mean, and the fused single pass.
+// quantisation + packing, integer sum of codes, decode of the mean, the fused single pass,
+// and the summable wire payload (offset-binary lanes that a uint32 Allreduce adds exactly).
 //
 // Method (Global-QSGD / "Quantize Once, Train Fast", abstract): one global norm scales every
 // worker; unbiased stochastic rounding onto a grid all workers share; the integer codes are
