@@ -191,6 +191,13 @@ def rows_resnet50(torch, gq, W, row):
     ms = time_calls(torch, lambda: gq.fused_mean(g2, S2, w2.grid, w2.levels, w2.bits, 1, 16, 0,
                                                  offsets=w2.offsets, out=o2), 11)
     row("fused_resnet50_exp7_K8", ms, w2.K * w2.n * 4 + w2.n * 4, "fused pass, 161 segments")
+    # the literal 9-level reading {0, 2^-7 .. 2^0} (E = 8) with 8-bit codes: same kernel
+    S8 = torch.empty_like(S2)
+    gq.global_norm(g2, w2.offsets, scale_out=S8)
+    ms = time_calls(torch, lambda: gq.fused_mean(g2, S8, w2.grid, 8, 8, 1, 16, 0,
+                                                 offsets=w2.offsets, out=o2), 11)
+    row("fused_resnet50_exp8_int8_K8", ms, w2.K * w2.n * 4 + w2.n * 4,
+        "fused pass, the 9-level exponential grid in 8-bit codes")
     del g2, o2, c2
     torch.cuda.empty_cache()
 
