@@ -220,8 +220,10 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
 }
 
 // Upper-triangular T with (P T)^T (P T) = I given G = P^T P, column by column as Gram-Schmidt
-// does it, through the Cholesky factor: G = R^T R (R upper triangular; a pivot that is not
-// positive marks a column with no remaining norm, whose row of R and column of T are zero),
+// does it, through the Cholesky factor: G = R^T R (R upper triangular; a pivot below 2^-32 of
+// the column's squared norm marks a column with no remaining norm of its own -- zero, or a
+// combination of the earlier columns up to fp32 rounding -- whose row of R and column of T
+// are zero),
 // then T[:, c] = (e_c - sum_{k<c} R[k][c] T[:, k]) / R[c][c].
 // Spread over the lanes of one wave: lane j (< RANK) holds column j of G (g[k] = G[k][j]),
 // of R and of T; the entries a step needs from another column are read from its lane with
@@ -241,10 +243,12 @@ __device__ __forceinline__ void lane_gram_schmidt_T(const double (&g)[RANK], int
     double rkc[RANK > 1 ? RANK - 1 : 1];  // R[k][c], k < c
 #pragma unroll
     for (int k = 0; k < c; ++k) rkc[k] = readlane_d(rcol[k], c);
-    double d = readlane_d(g[c], c);  // G[c][c]
+    const double gcc = readlane_d(g[c], c);  // G[c][c]: the column's squared norm
+    double d = gcc;
 #pragma unroll
     for (int k = 0; k < c; ++k) d -= rkc[k] * rkc[k];
-    if (d > 0.0) {  // the same value in every lane
+    // less than 2^-32 of the squared norm left: dependent on the earlier columns, set to zero
+    if (d > 0x1p-32 * gcc) {  // the same value in every lane
       const double rc = sqrt(d), inv = 1.0 / rc;
       double v = g[c];  // G[c][j]
 #pragma unroll

@@ -489,8 +489,10 @@ void orc_logquant(const float *F, int64_t rows, int32_t r, double alpha, int32_t
 }
 
 /* [LQ] referee major comment 1: Q is computed from P after P is orthonormalised.  Modified
- * Gram-Schmidt over columns 0..r-1 in order, all arithmetic in fp64; a column left with zero
- * norm stays zero. */
+ * Gram-Schmidt over columns 0..r-1 in order, all arithmetic in fp64.  The pages give no rule
+ * for a column that depends on the earlier ones; reading: if the projections leave less than
+ * 2^-16 of its norm (squared: 2^-32), what is left is rounding of the fp32 factor, not a
+ * direction, and the column is set to zero (as one with no norm at all). */
 void orc_mgs(float *P, int64_t n, int32_t r)
 {
     double *V = (double *)malloc((size_t)(n * r) * sizeof(double));
@@ -499,7 +501,9 @@ void orc_mgs(float *P, int64_t n, int32_t r)
     for (i = 0; i < n * r; ++i)
         V[i] = (double)P[i];
     for (c = 0; c < r; ++c) {
-        double nrm = 0.0;
+        double nrm = 0.0, nrm0 = 0.0;
+        for (i = 0; i < n; ++i)
+            nrm0 += V[i * r + c] * V[i * r + c];
         for (j = 0; j < c; ++j) {
             double d = 0.0;
             for (i = 0; i < n; ++i)
@@ -509,6 +513,8 @@ void orc_mgs(float *P, int64_t n, int32_t r)
         }
         for (i = 0; i < n; ++i)
             nrm += V[i * r + c] * V[i * r + c];
+        if (!(nrm > 0x1p-32 * nrm0))
+            nrm = 0.0;
         nrm = sqrt(nrm);
         for (i = 0; i < n; ++i)
             V[i * r + c] = nrm > 0.0 ? V[i * r + c] / nrm : 0.0;

@@ -126,7 +126,10 @@ float orc_logq_level(int32_t k, double alpha, int32_t L);
  * codes rows x r int8; colmax r fp32; Fhat rows x r (may be NULL). */
 void orc_logquant(const float *F, int64_t rows, int32_t r, double alpha, int32_t bits,
                   int8_t *codes, float *colmax, float *Fhat);
-/* Modified Gram-Schmidt on the columns of P (n x r, row-major, fp32 in and out), fp64 math. */
+/* Modified Gram-Schmidt on the columns of P (n x r, row-major, fp32 in and out), fp64 math.
+ * A column whose norm after the projections is below 2^-16 of its norm before them is
+ * numerically dependent on the earlier columns (the fp32 factor cannot resolve the
+ * difference) and is set to zero, like a column that is exactly zero. */
 void orc_mgs(float *P, int64_t n, int32_t r);
 /* One compressor step: M = G + E; P = M Qprev; P <- MGS(P); Q = M^T P; quantise P with
  * bits_p and Q with bits_q (the review's referee comment on Section V names b_p and b_q as

@@ -114,6 +114,27 @@ def test_mgs_zero_column_stays_zero(orc):
     assert abs(np.linalg.norm(got[:, 2].astype(np.float64)) - 1) < 1e-6
 
 
+def test_mgs_dependent_columns_are_zero(orc):
+    """A column that is a combination of earlier ones up to fp32 rounding has nothing of its
+    own left after the projections; it is set to zero like an exactly zero column, and the
+    columns after it are still orthonormalised against the live ones.  A column with a small
+    but real component of its own (1e-3 of its norm) stays."""
+    rng = np.random.default_rng(31)
+    n = 400
+    P = rng.standard_normal((n, 6)).astype(np.float32)
+    P[:, 1] = 3.0 * P[:, 0]                        # exactly dependent
+    P[:, 3] = (P[:, 0] + P[:, 2]).astype(np.float32)  # dependent up to fp32 rounding
+    W = rng.standard_normal(n)
+    P[:, 4] = (P[:, 2] + 1e-3 * W).astype(np.float32)  # a small part of its own
+    got = orc.mgs(P).astype(np.float64)
+    assert not got[:, 1].any() and not got[:, 3].any()
+    live = [0, 2, 4, 5]
+    assert np.abs(got[:, live].T @ got[:, live] - np.eye(4)).max() < 1e-6
+    # the live columns span what the original ones span
+    q, _ = np.linalg.qr(P[:, live].astype(np.float64))
+    assert np.abs(got[:, live] - q @ (q.T @ got[:, live])).max() < 1e-6
+
+
 def _step(orc, G, E, Q):
     return orc.powersgd_logquant(G, E, Q, 10.0, 8)
 

@@ -79,6 +79,8 @@ MUTATIONS = [
      "V[i * r + c] += d * V[i * r + j];"),
     ("Gram-Schmidt: no normalisation", "V[i * r + c] = nrm > 0.0 ? V[i * r + c] / nrm : 0.0;",
      "V[i * r + c] = V[i * r + c];"),
+    ("Gram-Schmidt: dependent columns kept", "        if (!(nrm > 0x1p-32 * nrm0))\n            nrm = 0.0;\n",
+     "\n"),
     ("power step: P not orthonormalised", "    orc_mgs(P, n, r);\n", "\n"),
     ("power step: no error fed back", "E[i] = G[i] + E[i];", "E[i] = G[i];"),
     ("power step: error of the wrong sign", "E[i * m + j] = (float)((double)E[i * m + j] - acc);",
