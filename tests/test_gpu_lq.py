@@ -289,3 +289,22 @@ def test_step_rank_deficient_gradient(orc, n, m, r, rank):
     live = ~dead
     assert np.abs(P_pre[:, live].T @ P_pre[:, live] - np.eye(rank)).max() < 1e-5
     _check_step(ref, out, Eg, Qg, orthonormal=False)
+
+
+@pytest.mark.parametrize("n,m,r", [(5, 6, 7), (3, 9, 4), (9, 2, 3), (1, 1, 1)])
+def test_step_fewer_rows_than_rank(orc, n, m, r):
+    """n or m below r: at most min(n, m) columns of P can be independent; the others are
+    dependent and zero on both sides."""
+    say("lq tiny", n, m, r)
+    rng = np.random.default_rng(n * 100 + m * 10 + r)
+    G = rng.standard_normal((n, m)).astype(np.float32)
+    E = (0.1 * rng.standard_normal((n, m))).astype(np.float32)
+    Q = rng.standard_normal((m, r)).astype(np.float32)
+    ref, out, Eg, Qg = _step_both(orc, G, E, Q)
+    P_pre = host(out["p_pre"]).astype(np.float64)
+    dead = ~ref["P_pre"].any(axis=0)
+    assert dead.sum() >= r - min(n, m)
+    assert not P_pre[:, dead].any()
+    k = int((~dead).sum())
+    assert np.abs(P_pre[:, ~dead].T @ P_pre[:, ~dead] - np.eye(k)).max() < 1e-5
+    _check_step(ref, out, Eg, Qg, orthonormal=False)
