@@ -468,7 +468,7 @@ __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict
   }
 }
 
-// Pass 2 (final): Q'[j][c] = sum over chunks, in chunk order (loads issued 16 chunks at a
+// Pass 2 (final): Q'[j][c] = sum over chunks, in chunk order (loads issued 32 chunks at a
 // time), and the column maxima of Q' (as for Pt in k_lq_mtp).
 template <int RANK>
 __global__ __launch_bounds__(256) void k_lq_qsum(const float *__restrict__ part,
@@ -481,13 +481,13 @@ __global__ __launch_bounds__(256) void k_lq_qsum(const float *__restrict__ part,
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) {
     float s = 0.0f;
-    for (int ch0 = 0; ch0 < nchunks; ch0 += 16) {
-      float v[16];
+    for (int ch0 = 0; ch0 < nchunks; ch0 += 32) {
+      float v[32];
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
+      for (int u = 0; u < 32; ++u)
         v[u] = ch0 + u < nchunks ? part[(int64_t)(ch0 + u) * count + i] : 0.0f;
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
+      for (int u = 0; u < 32; ++u)
         if (ch0 + u < nchunks) s += v[u];
     }
     Qn[i] = s;
