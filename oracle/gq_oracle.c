@@ -436,6 +436,75 @@ void orc_dequantize(const void *sums, int32_t acc_bits, int64_t n, const int64_t
     }
 }
 
+/* ======================= baselines: per-worker scales ======================= */
+
+/* [NUQ] abstract: QSGD normalises each worker's vector by its own L2 norm; QSGDinf (named
+ * there, not defined) is read as normalisation by the largest magnitude. */
+int32_t orc_worker_scales(const void *const *xs, int32_t K, int32_t dtype, int64_t n,
+                          const int64_t *offsets, int32_t nseg, int32_t norm,
+                          float *scales_out)
+{
+    int32_t g, k, bad = 0;
+    int64_t i;
+    (void)n;
+    for (k = 0; k < K; ++k)
+        for (g = 0; g < nseg; ++g) {
+            double v = 0.0;
+            float S;
+            if (norm == ORC_NORM_MAX) {
+                for (i = offsets[g]; i < offsets[g + 1]; ++i) {
+                    double a = fabs(orc_load(xs[k], dtype, i));
+                    if (isnan(a) || isnan(v))
+                        v = NAN; /* a NaN anywhere makes the scale non-finite */
+                    else if (a > v)
+                        v = a;
+                }
+            } else {
+                for (i = offsets[g]; i < offsets[g + 1]; ++i) {
+                    double x = orc_load(xs[k], dtype, i);
+                    v += x * x; /* exact square, index order */
+                }
+                v = sqrt(v);
+            }
+            S = (float)v;
+            if (!isfinite(v) || !isfinite(S)) {
+                S = 0.0f;
+                bad = 1;
+            }
+            scales_out[(int64_t)k * nseg + g] = S;
+        }
+    return bad;
+}
+
+void orc_worker_mean(const void *const *xs, int32_t K, int32_t dtype, int64_t n,
+                     const int64_t *offsets, int32_t nseg, const float *scales, int32_t grid,
+                     int32_t levels, uint64_t seed, uint32_t index_base, int32_t out_dtype,
+                     void *out)
+{
+    int32_t g, k;
+    int64_t i;
+    uint32_t *keys = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(K > 0 ? K : 1));
+    (void)n;
+    for (k = 0; k < K; ++k)
+        keys[k] = orc_worker_key(seed, (uint32_t)k);
+    for (g = 0; g < nseg; ++g)
+        for (i = offsets[g]; i < offsets[g + 1]; ++i) {
+            float acc = 0.0f;
+            for (k = 0; k < K; ++k) {
+                float S = scales[(int64_t)k * nseg + g];
+                float f = orc_decode_factor(grid, levels, K, S);
+                int32_t q = orc_quant_one(grid, levels, (float)orc_load(xs[k], dtype, i), S,
+                                          keys[k], index_base + (uint32_t)i);
+                acc = fmaf((float)orc_lin(grid, q), f, acc);
+            }
+            if (out_dtype == ORC_BF16)
+                ((uint16_t *)out)[i] = orc_f32_to_bf16(acc);
+            else
+                ((float *)out)[i] = acc;
+        }
+    free(keys);
+}
+
 /* ======================= LQ-SGD ======================= */
 
 /* [LQ] "Core claim" Eq. (5) q(y) = log(1 + alpha y) / log(1 + alpha) on y = |F| / max|column|

@@ -116,6 +116,29 @@ void orc_dequantize(const void *sums, int32_t acc_bits, int64_t n, const int64_t
                     int32_t nseg, const float *scale, int32_t grid, int32_t levels, int32_t K,
                     int32_t out_dtype, void *out);
 
+/* ---------------- baselines with per-worker scales (not summable) ---------------- */
+/* [NUQ] abstract: QSGD, in which every worker normalises by its own L2 norm, and its
+ * heuristic variant QSGDinf, read here as the same quantiser normalised by the largest
+ * magnitude (the L-infinity norm); NUQSGD proper is the exponential grid with per-worker L2
+ * norms.  Codes scaled this way are not summable: the receiver decodes every worker's codes
+ * with that worker's own scale and adds the decoded values. */
+enum { ORC_NORM_L2 = 0, ORC_NORM_MAX = 1 };
+/* scales_out[k*nseg + g] for every worker k and segment g: L2 -> fp32(sqrt(sum of squares in
+ * fp64)); MAX -> the largest |x| (exact).  A non-finite value is replaced by 0 and makes the
+ * return value 1 (else 0). */
+int32_t orc_worker_scales(const void *const *xs, int32_t K, int32_t dtype, int64_t n,
+                          const int64_t *offsets, int32_t nseg, int32_t norm,
+                          float *scales_out);
+/* mean_i for i in segment g: acc = +0, then for k = 0..K-1 in order
+ * acc = fmaf((float)lin(q_{k,i}), f_{k,g}, acc) (one rounding per worker), where q_{k,i} is the
+ * level of x_{k,i} under worker k's own scale S_{k,g} (orc_quant_one with worker k's key and
+ * counter index_base + i) and f_{k,g} = orc_decode_factor(grid, levels, K, S_{k,g}); stored as
+ * fp32 or bf16. */
+void orc_worker_mean(const void *const *xs, int32_t K, int32_t dtype, int64_t n,
+                     const int64_t *offsets, int32_t nseg, const float *scales, int32_t grid,
+                     int32_t levels, uint64_t seed, uint32_t index_base, int32_t out_dtype,
+                     void *out);
+
 /* ---------------- LQ-SGD: log quantiser and one PowerSGD step ---------------- */
 /* Magnitude index in [0, L] of y in [0, 1]: the level k/L nearest to
  * q(y) = log(1 + alpha*y) / log(1 + alpha), ties going up.  L = 2^(bits-1) - 1. */

@@ -23,6 +23,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
 UNIFORM, EXP = 0, 1
+NORM_L2, NORM_MAX = 0, 1
 
 _lib = None
 
@@ -80,6 +81,8 @@ def lib():
             "orc_wire_decode": (None, [p, i64, i32, i32, i32, p]),
             "orc_f32_to_bf16": (C.c_uint16, [f]),
             "orc_dequantize": (None, [p, i32, i64, p, i32, p, i32, i32, i32, i32, p]),
+            "orc_worker_scales": (i32, [p, i32, i32, i64, p, i32, i32, p]),
+            "orc_worker_mean": (None, [p, i32, i32, i64, p, i32, p, i32, i32, u64, u32, i32, p]),
             "orc_logq_index": (i32, [f, d, i32]),
             "orc_logq_level": (f, [i32, d, i32]),
             "orc_logquant": (None, [p, i64, i32, d, i32, p, p, p]),
@@ -284,6 +287,34 @@ def allreduce_mean(xs, grid, levels, bits, acc_bits, seed, index_base=0, offsets
     mean = dequantize(sums, S, grid, levels, len(xs), out_dtype, offsets)
     return dict(scale=S, norms=norms, nonfinite=bad, levels=q, codes=codes, sums=sums,
                 overflow=over, mean=mean)
+
+
+# ---------------------------------------------------------------- per-worker-scale baselines
+def worker_scales(xs, norm=NORM_L2, offsets=None):
+    """K x nseg fp32 scales, each worker normalised on its own (L2 norm, or largest magnitude
+    for NORM_MAX).  Returns (scales, bad)."""
+    xs = [np.ascontiguousarray(x) for x in xs]
+    n = xs[0].size
+    off = _offsets(offsets, n)
+    nseg = off.size - 1
+    S = np.zeros((len(xs), nseg), np.float32)
+    bad = lib().orc_worker_scales(_ptrs(xs), len(xs), _dtype_code(xs[0]), n, _ptr(off), nseg,
+                                  norm, _ptr(S))
+    return S, bool(bad)
+
+
+def worker_mean(xs, scales, grid, levels, seed, index_base=0, offsets=None, out_dtype=F32):
+    """Mean of the K workers' decoded values, each worker quantised and decoded with its own
+    scale (scales: K x nseg)."""
+    xs = [np.ascontiguousarray(x) for x in xs]
+    n = xs[0].size
+    off = _offsets(offsets, n)
+    sc = _c(scales, np.float32)
+    assert sc.size == len(xs) * (off.size - 1)
+    out = np.empty(n, np.uint16 if out_dtype == BF16 else np.float32)
+    lib().orc_worker_mean(_ptrs(xs), len(xs), _dtype_code(xs[0]), n, _ptr(off), off.size - 1,
+                          _ptr(sc), grid, levels, seed, index_base, out_dtype, _ptr(out))
+    return out
 
 
 # ---------------------------------------------------------------- LQ-SGD

@@ -18,7 +18,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "gq_oracle.c")
 PIN_SUITES = ["tests/test_oracle_rng.py", "tests/test_oracle_quant.py", "tests/test_oracle_lq.py",
-              "tests/test_oracle_wire.py"]
+              "tests/test_oracle_wire.py", "tests/test_oracle_baselines.py"]
 
 # (name, text in gq_oracle.c, replacement)
 MUTATIONS = [
@@ -90,6 +90,18 @@ MUTATIONS = [
     ("power step: P coded with Q's width", "orc_logquant(P, n, r, alpha, bits_p,",
      "orc_logquant(P, n, r, alpha, bits_q,"),
     ("power step: Q not warm-started", "    memcpy(Q, Qh, (size_t)(m * r) * sizeof(float));\n", "\n"),
+    ("worker scales: first nonzero magnitude, not the largest", "else if (a > v)",
+     "else if (v == 0.0)"),
+    ("worker scales: NaN ignored", "v = NAN; /* a NaN", "v = v; /* a NaN"),
+    ("worker scales: L2 without the square root", "                v = sqrt(v);\n", "\n"),
+    ("worker mean: worker 0's scale for every worker",
+     "float S = scales[(int64_t)k * nseg + g];", "float S = scales[g];"),
+    ("worker mean: factor without K", "float f = orc_decode_factor(grid, levels, K, S);",
+     "float f = orc_decode_factor(grid, levels, 1, S);"),
+    ("worker mean: worker 0's key for every worker",
+     "keys[k] = orc_worker_key(seed, (uint32_t)k);", "keys[k] = orc_worker_key(seed, 0u);"),
+    ("worker mean: last worker left out", "            for (k = 0; k < K; ++k) {\n                float S",
+     "            for (k = 0; k + 1 < K; ++k) {\n                float S"),
 ]
 
 
