@@ -515,6 +515,71 @@ GQ_EXPORT gq_status gq_fused_mean(gq_ctx *c, const void *const *grads, int32_t K
   return e == hipSuccess ? GQ_OK : hip_fail(c, e, "fused launch");
 }
 
+// ---------------------------------------------------------------- per-worker-scale baselines
+GQ_EXPORT gq_status gq_worker_scales(gq_ctx *c, const void *const *grads, int32_t K, int32_t dtype,
+                                     int64_t n, const int64_t *offsets, int32_t nseg, int32_t norm,
+                                     float *scales_out, void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(check_K(c, K));
+  TRY(check_dtype(c, dtype, "dtype"));
+  if (norm != GQ_NORM_L2 && norm != GQ_NORM_MAX) return fail(c, GQ_EINVAL, "norm = %d", norm);
+  if (!grads) return fail(c, GQ_EINVAL, "grads is NULL");
+  for (int k = 0; k < K; ++k) TRY(check_ptr(c, grads[k], "grads[k]", n == 0));
+  TRY(check_ptr(c, scales_out, "scales_out"));
+  TileView tv;
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, gq::kNormTile));
+  TRY(ensure_scratch(c, (size_t)K * (size_t)tv.ntiles * sizeof(double), s));
+  gq::NormArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int k = 0; k < K; ++k) a.grads[k] = grads[k];
+  a.partial = static_cast<double *>(c->scratch);
+  a.status = c->status;
+  a.tv = tv;
+  a.K = K;
+  hipError_t e = gq::launch_worker_scales(a, dtype, norm, scales_out, s);
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "worker scales launch");
+}
+
+GQ_EXPORT gq_status gq_worker_mean(gq_ctx *c, const void *const *grads, int32_t K, int32_t dtype,
+                                   int64_t n, const int64_t *offsets, int32_t nseg,
+                                   const float *scales, int32_t grid, int32_t levels,
+                                   uint64_t seed, uint32_t index_base, int32_t out_dtype,
+                                   void *out, void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(check_K(c, K));
+  TRY(check_dtype(c, dtype, "dtype"));
+  TRY(check_dtype(c, out_dtype, "out_dtype"));
+  if (grid != GQ_UNIFORM && grid != GQ_EXP) return fail(c, GQ_EINVAL, "grid = %d", grid);
+  if (levels < 1 || levels > (grid == GQ_EXP ? 30 : 127))
+    return fail(c, GQ_EINVAL, "levels = %d outside [1, %d]", levels, grid == GQ_EXP ? 30 : 127);
+  TRY(check_counter(c, n, index_base));
+  if (!grads) return fail(c, GQ_EINVAL, "grads is NULL");
+  for (int k = 0; k < K; ++k) TRY(check_ptr(c, grads[k], "grads[k]", n == 0));
+  TRY(check_ptr(c, scales, "scales"));
+  TRY(check_ptr(c, out, "out", n == 0));
+  TileView tv;
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  TRY(ensure_scratch(c, (size_t)K * (size_t)nseg * sizeof(float2), s));
+  gq::WorkerMeanArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int k = 0; k < K; ++k) {
+    a.grads[k] = grads[k];
+    a.key_mix[k] = key_mix(worker_key(seed, (uint32_t)k));
+  }
+  a.fac = static_cast<const float2 *>(c->scratch);
+  a.out = out;
+  a.tv = tv;
+  a.denom = decode_denominator(grid, levels, K);
+  a.K = K;
+  a.levels = levels;
+  a.out_dtype = out_dtype;
+  a.index_base = index_base;
+  hipError_t e = gq::launch_worker_mean(a, scales, dtype, grid, s);
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "worker mean launch");
+}
+
 GQ_EXPORT gq_status gq_logquant(gq_ctx *c, const float *F, int64_t rows, int32_t r, double alpha,
                                 int32_t bits, int8_t *codes, float *colmax, float *F_hat_or_null,
                                 void *stream) {

@@ -113,6 +113,19 @@ struct FusedArgs {
   uint32_t index_base;
 };
 
+struct WorkerMeanArgs {
+  const void *grads[kMaxWorkers];
+  uint32_t key_mix[kMaxWorkers];  // key ^ (key >> 16) per worker
+  const float2 *fac;             // K * nseg: (s/S or 1/S, 0 if unusable; decode factor)
+  void *out;
+  TileView tv;
+  double denom;                  // D: s*K (uniform) or K*2^(E-1) (exponential)
+  int32_t K;
+  int32_t levels;
+  int32_t out_dtype;
+  uint32_t index_base;
+};
+
 // Kernel launchers (gq_stream.hip).  Each returns the launch error, if any.
 hipError_t launch_global_norm(const NormArgs &a, int dtype, hipStream_t s);
 hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, hipStream_t s);
@@ -122,6 +135,12 @@ hipError_t launch_fused(const FusedArgs &a, int dtype, int grid, hipStream_t s);
 hipError_t launch_quantize_wire(const WireQuantArgs &a, int dtype, int grid, int wb,
                                 hipStream_t s);
 hipError_t launch_dequantize_wire(const WireDequantArgs &a, int wb, hipStream_t s);
+// Per-worker scales: a.partial holds K * ntiles fp64 sums (norm 0) or uint32 maxima (norm 1).
+hipError_t launch_worker_scales(const NormArgs &a, int dtype, int norm, float *scales_out,
+                                hipStream_t s);
+// Fills a.fac from `scales`, then the per-element pass.
+hipError_t launch_worker_mean(const WorkerMeanArgs &a, const float *scales, int dtype, int grid,
+                              hipStream_t s);
 hipError_t launch_clear_u32(unsigned *p, int count, hipStream_t s);
 
 }  // namespace gq

@@ -361,6 +361,10 @@ __device__ __forceinline__ uint32_t quant_exp_index(float x, float inv, int E, f
   return (low ? 0u : (uint32_t)jn) + (h < c ? 1u : 0u);
 }
 
+// Sign of an element: its sign bit, so a NaN under a caller-given finite scale (clamped to the
+// top level) keeps the sign its bits give it on both grids.
+__device__ __forceinline__ bool sign_of(float x) { return __float_as_int(x) < 0; }
+
 // Code field of a uniform level (signed, two's complement in `bits`).
 __device__ __forceinline__ uint32_t uniform_code(float m, float x, int bits) {
   return (uint32_t)(int32_t)copysignf(m, x) & ((1u << bits) - 1u);
@@ -368,7 +372,7 @@ __device__ __forceinline__ uint32_t uniform_code(float m, float x, int bits) {
 
 // Code field of an exponential index: sign bit above j (zero has no sign).
 __device__ __forceinline__ uint32_t exp_code(uint32_t j, float x, int bits) {
-  return ((x < 0.0f && j > 0) ? (1u << (bits - 1)) : 0u) | j;
+  return ((sign_of(x) && j > 0) ? (1u << (bits - 1)) : 0u) | j;
 }
 
 // Signed integer value on the common grid of an exponential index: sign * 2^(j-1), 0 for j = 0.
@@ -715,7 +719,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
             if constexpr (GRID == 0)
               lin = (int32_t)copysignf(quant_uniform_mag(x[e], q.inv, sf, h), x[e]);
             else
-              lin = exp_lin(quant_exp_index(x[e], q.inv, a.levels, two_em1, h), x[e] < 0.0f);
+              lin = exp_lin(quant_exp_index(x[e], q.inv, a.levels, two_em1, h), sign_of(x[e]));
             v[e] = (uint32_t)(lin + a.offset);
           }
         } else {
@@ -793,7 +797,7 @@ __device__ __forceinline__ void fused_batch(const FusedArgs &a, int k0, int kn,
           if constexpr (STORE) c[e] = uniform_code(m, xv, a.bits);
         } else {
           const uint32_t jj = quant_exp_index(xv, q.inv, a.levels, two_em1, h);
-          acci[j][e] += exp_lin(jj, xv < 0.0f);
+          acci[j][e] += exp_lin(jj, sign_of(xv));
           if constexpr (STORE) c[e] = exp_code(jj, xv, a.bits);
         }
       }
@@ -878,6 +882,190 @@ void k_fused(FusedArgs a) {
         if (a.sums) store_sums<P>(a.sums, a.acc_bits, e0[j], cnt[j], s);
         store_mean<P>(a.out, a.out_dtype, e0[j], cnt[j], v);
       }
+    }
+  }
+}
+
+// ================================================================ per-worker-scale baselines
+// QSGD / QSGDinf / NUQSGD with each worker's own scale: codes that are not summable, decoded by
+// the receiver worker by worker.
+
+__device__ __forceinline__ unsigned block_max_u32(unsigned v, unsigned *lds) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, off, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds[w] = v;
+  __syncthreads();
+  unsigned t = 0u;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t = max(t, lds[i]);
+  return t;
+}
+
+// Largest magnitude per (worker, norm tile), kept as the bit pattern of |x|: non-negative
+// floats order like their patterns and an infinity or NaN lies above every finite value, so
+// the integer maximum is exact and independent of order.  Grid: (tiles, K).
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_absmax_partial(NormArgs a) {
+  constexpr int P = DT == 0 ? 4 : 8;
+  constexpr int NP = kChunk / (64 * P);
+  __shared__ unsigned lds[kBlock / 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int k = blockIdx.y;
+  const void *src = a.grads[k];
+  unsigned *part = reinterpret_cast<unsigned *>(a.partial);
+  for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
+    int64_t begin;
+    int len, seg;
+    tile_of(a.tv, t, kNormTile, begin, len, seg);
+    const int nch = (len + kChunk - 1) / kChunk;
+    unsigned m = 0u;
+    for (int ci = wv; ci < nch; ci += kBlock / 64) {
+      float x[NP][P];
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int o = part_offset<P>(ci, j, lane);
+        const int cnt = min(P, len - o);
+        if (cnt > 0) {
+          load_part<DT, P>(src, begin + o, cnt, x[j]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < P; ++e) x[j][e] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NP; ++j)
+#pragma unroll
+        for (int e = 0; e < P; ++e) m = max(m, __float_as_uint(x[j][e]) & 0x7FFFFFFFu);
+    }
+    m = block_max_u32(m, lds);
+    if (threadIdx.x == 0) part[(int64_t)k * a.tv.ntiles + t] = m;
+  }
+}
+
+// One block per (segment, worker): the segment's tile partials reduced in a fixed order, then
+// S = fp32(sqrt(sum)) (L2) or the largest magnitude (MAX); a non-finite S is stored as 0 and
+// raises the status flag.
+template <int NORM>
+__global__ __launch_bounds__(kBlock) void k_worker_scales(NormArgs a, float *scales_out) {
+  __shared__ double lds[kBlock / 64];
+  __shared__ unsigned ldu[kBlock / 64];
+  const int g = blockIdx.x, k = blockIdx.y;
+  const int64_t t0 = seg_first_tile(a.tv, g), t1 = seg_first_tile(a.tv, g + 1);
+  float S;
+  bool bad;
+  if constexpr (NORM == 0) {
+    const double *part = a.partial + (int64_t)k * a.tv.ntiles;
+    double acc = 0.0;
+    for (int64_t t = t0 + threadIdx.x; t < t1; t += kBlock) acc += part[t];
+    const double nrm = sqrt(block_sum(acc, lds));
+    S = (float)nrm;
+    bad = !(nrm <= DBL_MAX) || !(S <= FLT_MAX);
+  } else {
+    const unsigned *part = reinterpret_cast<const unsigned *>(a.partial) + (int64_t)k * a.tv.ntiles;
+    unsigned m = 0u;
+    for (int64_t t = t0 + threadIdx.x; t < t1; t += kBlock) m = max(m, part[t]);
+    m = block_max_u32(m, ldu);
+    S = __uint_as_float(m);
+    bad = m >= 0x7F800000u;
+  }
+  if (threadIdx.x == 0) {
+    if (bad) {
+      S = 0.0f;
+      atomicOr(a.status, 1u);
+    }
+    scales_out[(int64_t)k * a.tv.nseg + g] = S;
+  }
+}
+
+// Per (worker, segment): the quantiser's s/S or 1/S (0 when the scale is not usable: the
+// worker then adds nothing) and the decode factor fp32(S / D).
+template <int GRID>
+__global__ void k_worker_factors(const float *scales, int64_t count, int levels, double denom,
+                                 float2 *fac) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  const float S = scales[i];
+  const SegQ q = seg_quant<GRID>(S, levels);
+  fac[i] = make_float2(q.valid ? q.inv : 0.0f, seg_decode(S, denom));
+}
+
+template <int DT, int GRID, int P, int NP, int KB>
+__device__ __forceinline__ void worker_batch(const WorkerMeanArgs &a, int k0, int kn, int seg,
+                                             const int64_t (&e0)[NP], const int (&cnt)[NP],
+                                             const uint32_t (&am)[NP][P], float sf,
+                                             float two_em1, float (&acc)[NP][P]) {
+  float x[KB][NP][P];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    if (kb < kn)
+#pragma unroll
+      for (int j = 0; j < NP; ++j)
+        if (cnt[j] > 0) load_part<DT, P>(a.grads[k0 + kb], e0[j], cnt[j], x[kb][j]);
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    if (kb >= kn) break;
+    const float2 fk = a.fac[(int64_t)(k0 + kb) * a.tv.nseg + seg];
+    if (!(fk.x > 0.0f)) continue;
+    const uint32_t km = a.key_mix[k0 + kb];
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        const float xv = x[kb][j][e];
+        const uint32_t h = fmix32_tail(am[j][e] ^ km);
+        float l;
+        if constexpr (GRID == 0)
+          l = copysignf(quant_uniform_mag(xv, fk.x, sf, h), xv);
+        else
+          l = (float)exp_lin(quant_exp_index(xv, fk.x, a.levels, two_em1, h), sign_of(xv));
+        acc[j][e] = fmaf(l, fk.y, acc[j][e]);  // one rounding per worker, in worker order
+      }
+  }
+}
+
+// For each element: every worker quantised with its own scale and decoded with its own factor,
+// accumulated by fused multiply-add in worker order.
+template <int KT, int DT, int GRID>
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(4, 8)))
+void k_worker_mean(WorkerMeanArgs a) {
+  constexpr int P = DT == 0 ? 4 : 8;
+  constexpr int NP = kChunk / (64 * P);
+  constexpr int KB = KT == 16 ? 8 : (KT > 0 ? KT : 4);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int K = KT > 0 ? KT : a.K;
+  const float sf = (float)a.levels;
+  const float two_em1 = ldexpf(1.0f, a.levels - 1);
+  for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
+    int64_t begin;
+    int len, seg;
+    tile_of(a.tv, t, kTile, begin, len, seg);
+    const int nch = (len + kChunk - 1) / kChunk;
+    for (int ci = wv; ci < nch; ci += kBlock / 64) {
+      int64_t e0[NP];
+      int cnt[NP];
+      uint32_t am[NP][P];
+      float acc[NP][P];
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int o = part_offset<P>(ci, j, lane);
+        cnt[j] = min(P, len - o);
+        e0[j] = begin + o;
+        const uint32_t ctr = a.index_base + (uint32_t)e0[j];
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          am[j][e] = mix16(ctr + e);
+          acc[j][e] = 0.0f;
+        }
+      }
+#pragma unroll 1
+      for (int k0 = 0; k0 < K; k0 += KB)
+        worker_batch<DT, GRID, P, NP, KB>(a, k0, min(KB, K - k0), seg, e0, cnt, am, sf, two_em1,
+                                          acc);
+#pragma unroll
+      for (int j = 0; j < NP; ++j)
+        if (cnt[j] > 0) store_mean<P>(a.out, a.out_dtype, e0[j], cnt[j], acc[j]);
     }
   }
 }
@@ -1005,6 +1193,53 @@ hipError_t launch_fused(const FusedArgs &a, int dtype, int grid, hipStream_t s) 
     launch_fused_s<true>(a, dtype, grid, g, s);
   else
     launch_fused_s<false>(a, dtype, grid, g, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_worker_scales(const NormArgs &a, int dtype, int norm, float *scales_out,
+                                hipStream_t s) {
+  if (a.tv.ntiles > 0) {
+    dim3 grid(grid_for(a.tv.ntiles, kNormGrid), a.K);
+    if (norm == 0 && dtype == 0) hipLaunchKernelGGL(k_norm_partial<0>, grid, dim3(kBlock), 0, s, a);
+    if (norm == 0 && dtype == 1) hipLaunchKernelGGL(k_norm_partial<1>, grid, dim3(kBlock), 0, s, a);
+    if (norm == 1 && dtype == 0) hipLaunchKernelGGL(k_absmax_partial<0>, grid, dim3(kBlock), 0, s, a);
+    if (norm == 1 && dtype == 1) hipLaunchKernelGGL(k_absmax_partial<1>, grid, dim3(kBlock), 0, s, a);
+  }
+  if (a.tv.nseg > 0) {
+    if (norm == 0)
+      hipLaunchKernelGGL(k_worker_scales<0>, dim3(a.tv.nseg, a.K), dim3(kBlock), 0, s, a, scales_out);
+    else
+      hipLaunchKernelGGL(k_worker_scales<1>, dim3(a.tv.nseg, a.K), dim3(kBlock), 0, s, a, scales_out);
+  }
+  return hipGetLastError();
+}
+
+template <int DT, int GRID>
+static void launch_worker_mean_k(const WorkerMeanArgs &a, dim3 g, hipStream_t s) {
+  switch (a.K) {
+    case 8: hipLaunchKernelGGL((k_worker_mean<8, DT, GRID>), g, dim3(kBlock), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_worker_mean<16, DT, GRID>), g, dim3(kBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_worker_mean<0, DT, GRID>), g, dim3(kBlock), 0, s, a); break;
+  }
+}
+
+hipError_t launch_worker_mean(const WorkerMeanArgs &a, const float *scales, int dtype, int grid,
+                              hipStream_t s) {
+  const int64_t count = (int64_t)a.K * a.tv.nseg;
+  float2 *fac = const_cast<float2 *>(a.fac);
+  if (grid == 0)
+    hipLaunchKernelGGL(k_worker_factors<0>, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,
+                       scales, count, a.levels, a.denom, fac);
+  else
+    hipLaunchKernelGGL(k_worker_factors<1>, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,
+                       scales, count, a.levels, a.denom, fac);
+  if (a.tv.ntiles > 0) {
+    dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+    if (dtype == 0 && grid == 0) launch_worker_mean_k<0, 0>(a, g, s);
+    if (dtype == 0 && grid == 1) launch_worker_mean_k<0, 1>(a, g, s);
+    if (dtype == 1 && grid == 0) launch_worker_mean_k<1, 0>(a, g, s);
+    if (dtype == 1 && grid == 1) launch_worker_mean_k<1, 1>(a, g, s);
+  }
   return hipGetLastError();
 }
 

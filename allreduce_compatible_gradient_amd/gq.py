@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libgq.so")
 OK, EINVAL, EOVERFLOW, EALIGN, ELAUNCH, ENONFINITE, ENOMEM = range(7)
 F32, BF16 = 0, 1
 UNIFORM, EXP = 0, 1
+NORM_L2, NORM_MAX = 0, 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libgq.so is not built (%s); run `python -m "
@@ -41,6 +42,9 @@ _SIGS = {
     "gq_dequantize": (_i32, [_p, _p, _i32, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _p, _p]),
     "gq_fused_mean": (_i32, [_p, _p, _i32, _i32, _i64, _p, _i32, _p, _i32, _i32, _i32, _u64, _u32,
                              _i32, _p, _p, _i32, _p, _p]),
+    "gq_worker_scales": (_i32, [_p, _p, _i32, _i32, _i64, _p, _i32, _i32, _p, _p]),
+    "gq_worker_mean": (_i32, [_p, _p, _i32, _i32, _i64, _p, _i32, _p, _i32, _i32, _u64, _u32,
+                              _i32, _p, _p]),
     "gq_logquant": (_i32, [_p, _p, _i64, _i32, _d, _i32, _p, _p, _p, _p]),
     "gq_wire_lane_bytes": (_i32, [_i32, _i32, _i32]),
     "gq_quantize_wire": (_i32, [_p, _p, _i32, _i64, _p, _i32, _p, _i32, _i32, _u64, _u32, _u32,
@@ -263,6 +267,39 @@ def fused_mean(grads, scale, grid, levels, bits, seed, acc_bits, out_dtype=F32, 
                                  seed, index_base, acc_bits, cptr,
                                  None if sums is None else _dev(sums, "sums"), out_dtype,
                                  _dev(out, "out"), _stream()))
+    return out
+
+
+# ----------------------------------------------------------------------------- baselines
+def worker_scales(grads, norm=NORM_L2, offsets=None, out=None, ctx: Optional[Context] = None):
+    """Each worker's own scale per segment (K x nseg fp32): L2 norm, or largest magnitude for
+    NORM_MAX (QSGD / QSGDinf)."""
+    ctx = ctx or context()
+    n = grads[0].numel()
+    ptrs = [_dev(g, "grads[%d]" % k, grads[0].dtype) for k, g in enumerate(grads)]
+    off, nseg, keep = _offsets(offsets, n)
+    if out is None:
+        out = torch.empty(len(grads), nseg, dtype=torch.float32, device=grads[0].device)
+    ctx.check(_lib.gq_worker_scales(ctx.handle, _ptr_array(ptrs), len(grads), _elt(grads[0]), n,
+                                    off, nseg, norm, _dev(out, "out", torch.float32), _stream()))
+    return out
+
+
+def worker_mean(grads, scales, grid, levels, seed, out_dtype=F32, index_base=0, offsets=None,
+                out=None, ctx: Optional[Context] = None):
+    """Mean of the workers' decoded values, each quantised and decoded with its own scale
+    (scales: K x nseg fp32, e.g. from worker_scales)."""
+    ctx = ctx or context()
+    n = grads[0].numel()
+    ptrs = [_dev(g, "grads[%d]" % k, grads[0].dtype) for k, g in enumerate(grads)]
+    off, nseg, keep = _offsets(offsets, n)
+    if scales.numel() != len(grads) * nseg:
+        raise ValueError("scales must hold K * nseg values")
+    if out is None:
+        out = torch.empty(n, dtype=_torch_dtype(out_dtype), device=grads[0].device)
+    ctx.check(_lib.gq_worker_mean(ctx.handle, _ptr_array(ptrs), len(grads), _elt(grads[0]), n,
+                                  off, nseg, _dev(scales, "scales", torch.float32), grid, levels,
+                                  seed, index_base, out_dtype, _dev(out, "out"), _stream()))
     return out
 
 

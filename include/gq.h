@@ -155,6 +155,37 @@ gq_status gq_dequantize_wire(gq_ctx *ctx, const void *payload, int64_t n,
                              int32_t grid, int32_t levels, int32_t world, int32_t out_dtype,
                              void *out, void *stream);
 
+/* Baselines with per-worker scales ("NUQSGD", abstract: QSGD, where each worker normalises by
+ * its own L2 norm, and its heuristic variant QSGDinf, read here as normalisation by the
+ * largest magnitude; NUQSGD itself is the exponential grid with per-worker L2 norms).  Codes
+ * scaled per worker are not summable: each receiver decodes every worker's codes with that
+ * worker's own scale.  These two calls are that receiver's local step on one GPU.
+ *
+ * Scale of every worker and segment:
+ *   norm = GQ_NORM_L2:  S_{k,g} = fp32( sqrt( sum_{i in g} x_{k,i}^2 ) ), squares in fp64;
+ *   norm = GQ_NORM_MAX: S_{k,g} = max_{i in g} |x_{k,i}| (exact).
+ * A non-finite S_{k,g} is stored as 0 and flags GQ_ENONFINITE for gq_read_status.
+ *   grads       (host) array of K device pointers, each n elements of `dtype`
+ *   scales_out  K*nseg fp32, k-major (worker k's segment g at k*nseg + g) */
+#define GQ_NORM_L2 0
+#define GQ_NORM_MAX 1
+gq_status gq_worker_scales(gq_ctx *ctx, const void *const *grads, int32_t K, int32_t dtype,
+                           int64_t n, const int64_t *offsets, int32_t nseg, int32_t norm,
+                           float *scales_out, void *stream);
+
+/* Mean of the K workers' decoded values, each worker quantised with its own scale exactly as
+ * gq_quantize_pack (scale row k of `scales`, worker = k, same counters) and decoded with its
+ * own factor f_{k,g} = fp32(S_{k,g} / D), D = s*K (uniform) or K*2^(E-1) (exponential; 0 for
+ * a scale that is not a positive finite number):
+ *   acc = +0;  for k = 0..K-1 in order: acc = fma((float)lin_{k,i}, f_{k,g}, acc)
+ * (one rounding per worker), stored as fp32 or bf16 (round to nearest even).
+ *   scales  K*nseg fp32 (device), k-major, e.g. from gq_worker_scales
+ *   levels  uniform 1..127, exponential 1..30;  out n elements of out_dtype */
+gq_status gq_worker_mean(gq_ctx *ctx, const void *const *grads, int32_t K, int32_t dtype,
+                         int64_t n, const int64_t *offsets, int32_t nseg, const float *scales,
+                         int32_t grid, int32_t levels, uint64_t seed, uint32_t index_base,
+                         int32_t out_dtype, void *out, void *stream);
+
 /* LQ-SGD log quantiser on each column of F (rows x r, row-major fp32; LQ-SGD review, Eq. 5
  * with the max-magnitude normalisation of referee major comment 1, decode by Eq. 6):
  *   m_c = max_i |F_ic|;  y = fp32(|F_ic| / m_c);

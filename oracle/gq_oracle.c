@@ -166,7 +166,7 @@ static int32_t quant_uniform(int32_t s, float x, float S, uint32_t key, uint32_t
     p = (double)u - l;           /* exact */
     r = orc_uniform(key, counter);
     m = (int32_t)l + (r < p ? 1 : 0);
-    return x < 0.0f ? -m : m;
+    return signbit(x) ? -m : m; /* a NaN keeps the sign its sign bit gives it */
 }
 
 /* Exponential grid ([NUQ] abstract: nonuniform levels).  Levels of |x|/S are 0 and 2^(j-E)
@@ -199,7 +199,7 @@ static int32_t quant_exp(int32_t E, float x, float S, uint32_t key, uint32_t cou
     r = orc_uniform(key, counter);
     if (r < p)
         j += 1;
-    return (x < 0.0f && j > 0) ? -j : j;
+    return (signbit(x) && j > 0) ? -j : j;
 }
 
 int32_t orc_quant_one(int32_t grid, int32_t levels, float x, float S, uint32_t key,

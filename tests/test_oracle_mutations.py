@@ -38,7 +38,7 @@ MUTATIONS = [
     ("uniform: round up on r <= p", "m = (int32_t)l + (r < p ? 1 : 0);",
      "m = (int32_t)l + (r <= p ? 1 : 0);"),
     ("uniform: nearest level, not floor", "l = floor((double)u);", "l = floor((double)u + 0.5);"),
-    ("uniform: sign dropped", "return x < 0.0f ? -m : m;", "return m;"),
+    ("uniform: sign dropped", "return signbit(x) ? -m : m;", "return m;"),
     ("uniform: counter without index base", "scale[g], key, index_base + (uint32_t)i);",
      "scale[g], key, (uint32_t)i);"),
     ("exponential: probability over the upper level", "p = ((double)u - lo) / (hi - lo);",
