@@ -991,10 +991,10 @@ __global__ void k_worker_factors(const float *scales, int64_t count, int levels,
 }
 
 template <int DT, int GRID, int P, int NP, int KB>
-__device__ __forceinline__ void worker_batch(const WorkerMeanArgs &a, int k0, int kn, int seg,
-                                             const int64_t (&e0)[NP], const int (&cnt)[NP],
-                                             const uint32_t (&am)[NP][P], float sf,
-                                             float two_em1, float (&acc)[NP][P]) {
+__device__ __forceinline__ void worker_batch(const WorkerMeanArgs &a, int k0, int kn,
+                                             float2 fl, const int64_t (&e0)[NP],
+                                             const int (&cnt)[NP], const uint32_t (&am)[NP][P],
+                                             float sf, float two_em1, float (&acc)[NP][P]) {
   float x[KB][NP][P];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
@@ -1005,8 +1005,10 @@ __device__ __forceinline__ void worker_batch(const WorkerMeanArgs &a, int k0, in
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     if (kb >= kn) break;
-    const float2 fk = a.fac[(int64_t)(k0 + kb) * a.tv.nseg + seg];
-    if (!(fk.x > 0.0f)) continue;
+    // worker k's factors sit in lane k of fl: read them into scalar registers
+    const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl.x), k0 + kb));
+    const float fac = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl.y), k0 + kb));
+    if (!(inv > 0.0f)) continue;
     const uint32_t km = a.key_mix[k0 + kb];
 #pragma unroll
     for (int j = 0; j < NP; ++j)
@@ -1016,10 +1018,10 @@ __device__ __forceinline__ void worker_batch(const WorkerMeanArgs &a, int k0, in
         const uint32_t h = fmix32_tail(am[j][e] ^ km);
         float l;
         if constexpr (GRID == 0)
-          l = copysignf(quant_uniform_mag(xv, fk.x, sf, h), xv);
+          l = copysignf(quant_uniform_mag(xv, inv, sf, h), xv);
         else
-          l = (float)exp_lin(quant_exp_index(xv, fk.x, a.levels, two_em1, h), sign_of(xv));
-        acc[j][e] = fmaf(l, fk.y, acc[j][e]);  // one rounding per worker, in worker order
+          l = (float)exp_lin(quant_exp_index(xv, inv, a.levels, two_em1, h), sign_of(xv));
+        acc[j][e] = fmaf(l, fac, acc[j][e]);  // one rounding per worker, in worker order
       }
   }
 }
@@ -1042,6 +1044,8 @@ void k_worker_mean(WorkerMeanArgs a) {
     int len, seg;
     tile_of(a.tv, t, kTile, begin, len, seg);
     const int nch = (len + kChunk - 1) / kChunk;
+    // lane k holds worker k's (s/S or 1/S, decode factor) for this tile's segment (K <= 64)
+    const float2 fl = a.fac[(int64_t)(lane < K ? lane : 0) * a.tv.nseg + seg];
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
       int64_t e0[NP];
       int cnt[NP];
@@ -1061,7 +1065,7 @@ void k_worker_mean(WorkerMeanArgs a) {
       }
 #pragma unroll 1
       for (int k0 = 0; k0 < K; k0 += KB)
-        worker_batch<DT, GRID, P, NP, KB>(a, k0, min(KB, K - k0), seg, e0, cnt, am, sf, two_em1,
+        worker_batch<DT, GRID, P, NP, KB>(a, k0, min(KB, K - k0), fl, e0, cnt, am, sf, two_em1,
                                           acc);
 #pragma unroll
       for (int j = 0; j < NP; ++j)

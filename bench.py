@@ -109,7 +109,9 @@ def time_calls(torch, fn, iters, warmup=1, median=True):
     return t.median_ms() if median else t.mean_ms()
 
 
-ROW_GROUPS = ("flat-1.3G-steps", "resnet50", "gpt2", "lq-4096x4096", "lq-4096x11008")
+ROW_GROUPS = ("flat-1.3G-steps", "resnet50", "gpt2", "lq-4096x4096", "lq-4096x11008",
+              "baselines")
+FLAT_GROUPS = ("flat-1.3G-steps", "baselines")  # groups timed on the resident 1.3e9 buffers
 
 
 def rows_breakdown(torch, gq, W, grads, S, w, args, groups=ROW_GROUPS):
@@ -134,6 +136,8 @@ def rows_breakdown(torch, gq, W, grads, S, w, args, groups=ROW_GROUPS):
     for shape in W.LQ_SHAPES:
         if "lq-%dx%d" % shape in groups:
             rows_lq(torch, gq, W, shape, row)
+    if "baselines" in groups:
+        rows_baselines(torch, gq, W, grads, w, row, it)
     torch.cuda.empty_cache()
     return rows
 
@@ -240,6 +244,44 @@ def rows_lq(torch, gq, W, shape, row):
         del G, E, Q
 
 
+def rows_baselines(torch, gq, W, grads, w, row, it):
+    """QSGD (each worker's own L2 norm), QSGDinf (own largest magnitude) and NUQSGD (exponential
+    grid, own L2 norm): the per-worker scales and the receiver's decode of every worker with its
+    own scale, on the same buffers as the Global-QSGD step."""
+    n, K = w.n, w.K
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    for norm, tag in ((gq.NORM_L2, "qsgd_l2"), (gq.NORM_MAX, "qsgdinf_max")):
+        Sk = gq.worker_scales(grads, norm)
+        ms = time_calls(torch, lambda: gq.worker_scales(grads, norm, out=Sk), it)
+        row("worker_scales_%s_1.3G_K8" % tag, ms, K * n * 4, "K fp32 buffers in, K scales out")
+        ms = time_calls(torch, lambda: gq.worker_mean(grads, Sk, w.grid, w.levels, 1, 0,
+                                                      out=out), it)
+        row("worker_mean_%s_1.3G_s127_K8" % tag, ms, K * n * 4 + n * 4,
+            "each worker quantised and decoded with its own scale, fp32 mean out")
+    del out
+    torch.cuda.empty_cache()
+    w2 = W.get("resnet50-161t-f32-K8-exp7")
+    g2 = W.gradients(w2, "cuda")
+    S2 = gq.worker_scales(g2, gq.NORM_L2, w2.offsets)
+    o2 = torch.empty(w2.n, dtype=torch.float32, device="cuda")
+    ms = time_calls(torch, lambda: gq.worker_mean(g2, S2, w2.grid, w2.levels, 1, 0,
+                                                  offsets=w2.offsets, out=o2), 11)
+    row("worker_mean_nuqsgd_resnet50_exp7_K8", ms, w2.K * w2.n * 4 + w2.n * 4,
+        "NUQSGD: exponential grid, each worker's own L2 norm per segment")
+    del g2, o2
+    torch.cuda.empty_cache()
+    w3 = W.get("gpt2s-148t-bf16-K16-uniform7")
+    g3 = W.gradients(w3, "cuda")
+    S3 = gq.worker_scales(g3, gq.NORM_L2, w3.offsets)
+    o3 = torch.empty(w3.n, dtype=torch.bfloat16, device="cuda")
+    ms = time_calls(torch, lambda: gq.worker_mean(g3, S3, w3.grid, w3.levels, 1, 1,
+                                                  offsets=w3.offsets, out=o3), 7)
+    row("worker_mean_qsgd_gpt2_bf16_s7_K16", ms, w3.K * w3.n * 2 + w3.n * 2,
+        "QSGD on the GPT-2 buckets, bf16 in and out")
+    del g3, o3
+    torch.cuda.empty_cache()
+
+
 def measure_ceilings(torch, grads, out):
     """Bandwidth of a plain stream with the fused pass's memory pattern and with the norm
     pass's (libgq_ceiling.so): K fp32 reads + 1 fp32 write, and K fp32 reads; and of a plain
@@ -329,7 +371,7 @@ def main():
 
     torch.cuda.set_device(0)
     w = W.get(WORKLOAD)
-    if args.rows_only and args.rows_only != "flat-1.3G-steps":
+    if args.rows_only and args.rows_only not in FLAT_GROUPS:
         rows = rows_breakdown(torch, gq, W, None, None, w, args, groups=(args.rows_only,))
         print(json.dumps({"rows": rows}), flush=True)
         return
