@@ -505,6 +505,28 @@ void orc_worker_mean(const void *const *xs, int32_t K, int32_t dtype, int64_t n,
     free(keys);
 }
 
+void orc_decode_workers(const uint8_t *const *codes, int32_t K, int64_t n,
+                        const int64_t *offsets, int32_t nseg, const float *scales, int32_t grid,
+                        int32_t levels, int32_t bits, int32_t out_dtype, void *out)
+{
+    int32_t g, k;
+    int64_t i;
+    (void)n;
+    for (g = 0; g < nseg; ++g)
+        for (i = offsets[g]; i < offsets[g + 1]; ++i) {
+            float acc = 0.0f;
+            for (k = 0; k < K; ++k) {
+                float f = orc_decode_factor(grid, levels, K, scales[(int64_t)k * nseg + g]);
+                int32_t q = orc_unpack_one(codes[k], i, grid, bits);
+                acc = fmaf((float)orc_lin(grid, q), f, acc);
+            }
+            if (out_dtype == ORC_BF16)
+                ((uint16_t *)out)[i] = orc_f32_to_bf16(acc);
+            else
+                ((float *)out)[i] = acc;
+        }
+}
+
 /* ======================= LQ-SGD ======================= */
 
 /* [LQ] "Core claim" Eq. (5) q(y) = log(1 + alpha y) / log(1 + alpha) on y = |F| / max|column|

@@ -141,6 +141,12 @@ void orc_worker_mean(const void *const *xs, int32_t K, int32_t dtype, int64_t n,
                      int32_t levels, uint64_t seed, uint32_t index_base, int32_t out_dtype,
                      void *out);
 
+/* The receiver's side after an allgather of such codes: mean_i = the same fma chain as
+ * orc_worker_mean with q_{k,i} read from worker k's packed codes (orc_unpack_one). */
+void orc_decode_workers(const uint8_t *const *codes, int32_t K, int64_t n,
+                        const int64_t *offsets, int32_t nseg, const float *scales, int32_t grid,
+                        int32_t levels, int32_t bits, int32_t out_dtype, void *out);
+
 /* ---------------- LQ-SGD: log quantiser and one PowerSGD step ---------------- */
 /* Magnitude index in [0, L] of y in [0, 1]: the level k/L nearest to
  * q(y) = log(1 + alpha*y) / log(1 + alpha), ties going up.  L = 2^(bits-1) - 1. */

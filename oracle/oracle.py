@@ -83,6 +83,7 @@ def lib():
             "orc_dequantize": (None, [p, i32, i64, p, i32, p, i32, i32, i32, i32, p]),
             "orc_worker_scales": (i32, [p, i32, i32, i64, p, i32, i32, p]),
             "orc_worker_mean": (None, [p, i32, i32, i64, p, i32, p, i32, i32, u64, u32, i32, p]),
+            "orc_decode_workers": (None, [p, i32, i64, p, i32, p, i32, i32, i32, i32, p]),
             "orc_logq_index": (i32, [f, d, i32]),
             "orc_logq_level": (f, [i32, d, i32]),
             "orc_logquant": (None, [p, i64, i32, d, i32, p, p, p]),
@@ -314,6 +315,18 @@ def worker_mean(xs, scales, grid, levels, seed, index_base=0, offsets=None, out_
     out = np.empty(n, np.uint16 if out_dtype == BF16 else np.float32)
     lib().orc_worker_mean(_ptrs(xs), len(xs), _dtype_code(xs[0]), n, _ptr(off), off.size - 1,
                           _ptr(sc), grid, levels, seed, index_base, out_dtype, _ptr(out))
+    return out
+
+
+def decode_workers(codes_list, n, scales, grid, levels, bits, offsets=None, out_dtype=F32):
+    """Receiver's mean from K workers' packed codes, each decoded with its own scale."""
+    codes_list = [_c(c, np.uint8) for c in codes_list]
+    off = _offsets(offsets, n)
+    sc = _c(scales, np.float32)
+    assert sc.size == len(codes_list) * (off.size - 1)
+    out = np.empty(n, np.uint16 if out_dtype == BF16 else np.float32)
+    lib().orc_decode_workers(_ptrs(codes_list), len(codes_list), n, _ptr(off), off.size - 1,
+                             _ptr(sc), grid, levels, bits, out_dtype, _ptr(out))
     return out
 
 

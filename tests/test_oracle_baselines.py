@@ -246,3 +246,35 @@ def test_bf16_output_is_the_rounded_fp32_mean(orc):
     import torch
     ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(b, ref)
+
+
+# ----------------------------------------------------------------------------- receiver
+@pytest.mark.parametrize("grid,levels,bits", [(U, 7, 4), (U, 127, 8), (X, 7, 4), (X, 8, 8)])
+def test_decoding_codes_gives_the_exact_mean(orc, grid, levels, bits):
+    """The receiver's decode of packed codes with power-of-two factors is the exact rational
+    mean of the levels; distinct exponents per worker and segment catch a wrong factor."""
+    rng = np.random.default_rng(32)
+    K, n = 4, 301
+    off = _segments(rng, n, 3)
+    D = levels * K if grid == U else K * 2 ** (levels - 1)
+    e = rng.integers(-12, -4, size=(K, 3))
+    scales = (D * np.exp2(e.astype(np.float64))).astype(np.float32)
+    xs = [np.empty(n, np.float32) for _ in range(K)]
+    for k in range(K):
+        for g in range(3):
+            seg = slice(off[g], off[g + 1])
+            xs[k][seg] = rng.uniform(-1, 1, off[g + 1] - off[g]) * float(scales[k, g])
+    codes = [orc.pack(orc.quantize(x, scales[k], grid, levels, 17, k, 0, off), grid, bits)
+             for k, x in enumerate(xs)]
+    got = orc.decode_workers(codes, n, scales, grid, levels, bits, off)
+    exact = _exact_mean_pow2(orc, xs, scales, grid, levels, 17, off)
+    assert all(Fraction(float(got[i])) == exact[i] for i in range(n))
+
+
+def test_codes_of_an_unusable_scale_add_nothing(orc):
+    """A worker whose scale is 0 has decode factor 0: even nonzero codes add nothing."""
+    n, s = 64, 7
+    codes = [orc.pack(np.full(n, 3, np.int32), U, 8), orc.pack(np.full(n, -5, np.int32), U, 8)]
+    scales = np.array([[2.0 * s * 2], [0.0]], np.float32)  # factor of worker 0: 2^1
+    got = orc.decode_workers(codes, n, scales, U, s, 8)
+    assert np.all(got == 6.0)

@@ -100,6 +100,12 @@ MUTATIONS = [
      "float f = orc_decode_factor(grid, levels, 1, S);"),
     ("worker mean: worker 0's key for every worker",
      "keys[k] = orc_worker_key(seed, (uint32_t)k);", "keys[k] = orc_worker_key(seed, 0u);"),
+    ("decode workers: worker 0's factor for every worker",
+     "float f = orc_decode_factor(grid, levels, K, scales[(int64_t)k * nseg + g]);",
+     "float f = orc_decode_factor(grid, levels, K, scales[g]);"),
+    ("decode workers: worker 0's codes for every worker",
+     "int32_t q = orc_unpack_one(codes[k], i, grid, bits);",
+     "int32_t q = orc_unpack_one(codes[0], i, grid, bits);"),
     ("worker mean: last worker left out", "            for (k = 0; k < K; ++k) {\n                float S",
      "            for (k = 0; k + 1 < K; ++k) {\n                float S"),
 ]
