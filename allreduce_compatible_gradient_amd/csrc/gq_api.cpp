@@ -580,6 +580,36 @@ GQ_EXPORT gq_status gq_worker_mean(gq_ctx *c, const void *const *grads, int32_t 
   return e == hipSuccess ? GQ_OK : hip_fail(c, e, "worker mean launch");
 }
 
+GQ_EXPORT gq_status gq_decode_workers(gq_ctx *c, const uint8_t *const *codes, int32_t K, int64_t n,
+                                      const int64_t *offsets, int32_t nseg, const float *scales,
+                                      int32_t grid, int32_t levels, int32_t bits,
+                                      int32_t out_dtype, void *out, void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(check_K(c, K));
+  TRY(check_codec(c, grid, levels, bits));
+  TRY(check_dtype(c, out_dtype, "out_dtype"));
+  if (!codes) return fail(c, GQ_EINVAL, "codes is NULL");
+  for (int k = 0; k < K; ++k) TRY(check_ptr(c, codes[k], "codes[k]", n == 0));
+  TRY(check_ptr(c, scales, "scales"));
+  TRY(check_ptr(c, out, "out", n == 0));
+  TileView tv;
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  TRY(ensure_scratch(c, (size_t)K * (size_t)nseg * sizeof(float2), s));
+  gq::DecodeWorkersArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int k = 0; k < K; ++k) a.codes[k] = codes[k];
+  a.fac = static_cast<const float2 *>(c->scratch);
+  a.out = out;
+  a.tv = tv;
+  a.K = K;
+  a.bits = bits;
+  a.out_dtype = out_dtype;
+  hipError_t e = gq::launch_decode_workers(a, scales, grid, levels,
+                                           decode_denominator(grid, levels, K), s);
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "decode workers launch");
+}
+
 GQ_EXPORT gq_status gq_logquant(gq_ctx *c, const float *F, int64_t rows, int32_t r, double alpha,
                                 int32_t bits, int8_t *codes, float *colmax, float *F_hat_or_null,
                                 void *stream) {

@@ -126,6 +126,16 @@ struct WorkerMeanArgs {
   uint32_t index_base;
 };
 
+struct DecodeWorkersArgs {
+  const uint8_t *codes[kMaxWorkers];
+  const float2 *fac;             // K * nseg, as in WorkerMeanArgs (only the factor is used)
+  void *out;
+  TileView tv;
+  int32_t K;
+  int32_t bits;
+  int32_t out_dtype;
+};
+
 // Kernel launchers (gq_stream.hip).  Each returns the launch error, if any.
 hipError_t launch_global_norm(const NormArgs &a, int dtype, hipStream_t s);
 hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, hipStream_t s);
@@ -141,6 +151,9 @@ hipError_t launch_worker_scales(const NormArgs &a, int dtype, int norm, float *s
 // Fills a.fac from `scales`, then the per-element pass.
 hipError_t launch_worker_mean(const WorkerMeanArgs &a, const float *scales, int dtype, int grid,
                               hipStream_t s);
+// Fills a.fac from `scales`, then decodes the K code streams.
+hipError_t launch_decode_workers(const DecodeWorkersArgs &a, const float *scales, int grid,
+                                 int levels, double denom, hipStream_t s);
 hipError_t launch_clear_u32(unsigned *p, int count, hipStream_t s);
 
 }  // namespace gq

@@ -1074,6 +1074,44 @@ void k_worker_mean(WorkerMeanArgs a) {
   }
 }
 
+// The receiver's side after an allgather of per-worker-scaled codes: each worker's packed
+// codes decoded with its own factor (lane k of `fl`), accumulated by fused multiply-add in
+// worker order.  P = 8 elements per part: 8 (8-bit) or 4 (4-bit) code bytes per worker.
+template <int GRID>
+__global__ __launch_bounds__(kBlock) void k_decode_workers(DecodeWorkersArgs a) {
+  constexpr int P = 8;
+  constexpr int NP = kChunk / (64 * P);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
+    int64_t begin;
+    int len, seg;
+    tile_of(a.tv, t, kTile, begin, len, seg);
+    const float fl = a.fac[(int64_t)(lane < a.K ? lane : 0) * a.tv.nseg + seg].y;
+    const int nch = (len + kChunk - 1) / kChunk;
+    for (int ci = wv; ci < nch; ci += kBlock / 64) {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int o = part_offset<P>(ci, j, lane);
+        const int cnt = min(P, len - o);
+        if (cnt <= 0) continue;
+        const int64_t e0 = begin + o;
+        float acc[P];
+#pragma unroll
+        for (int e = 0; e < P; ++e) acc[e] = 0.0f;
+        for (int k = 0; k < a.K; ++k) {
+          const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), k));
+          uint32_t c[P];
+          load_codes<P>(a.codes[k], e0, cnt, a.bits, c);
+#pragma unroll
+          for (int e = 0; e < P; ++e)
+            acc[e] = fmaf((float)lin_of_code<GRID>(c[e], a.bits), f, acc[e]);
+        }
+        store_mean<P>(a.out, a.out_dtype, e0, cnt, acc);
+      }
+    }
+  }
+}
+
 __global__ void k_clear_u32(unsigned *p, int count) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) p[i] = 0u;
@@ -1243,6 +1281,26 @@ hipError_t launch_worker_mean(const WorkerMeanArgs &a, const float *scales, int 
     if (dtype == 0 && grid == 1) launch_worker_mean_k<0, 1>(a, g, s);
     if (dtype == 1 && grid == 0) launch_worker_mean_k<1, 0>(a, g, s);
     if (dtype == 1 && grid == 1) launch_worker_mean_k<1, 1>(a, g, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_workers(const DecodeWorkersArgs &a, const float *scales, int grid,
+                                 int levels, double denom, hipStream_t s) {
+  const int64_t count = (int64_t)a.K * a.tv.nseg;
+  float2 *fac = const_cast<float2 *>(a.fac);
+  if (grid == 0)
+    hipLaunchKernelGGL(k_worker_factors<0>, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,
+                       scales, count, levels, denom, fac);
+  else
+    hipLaunchKernelGGL(k_worker_factors<1>, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,
+                       scales, count, levels, denom, fac);
+  if (a.tv.ntiles > 0) {
+    dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+    if (grid == 0)
+      hipLaunchKernelGGL(k_decode_workers<0>, g, dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_decode_workers<1>, g, dim3(kBlock), 0, s, a);
   }
   return hipGetLastError();
 }

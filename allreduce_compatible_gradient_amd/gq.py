@@ -45,6 +45,8 @@ _SIGS = {
     "gq_worker_scales": (_i32, [_p, _p, _i32, _i32, _i64, _p, _i32, _i32, _p, _p]),
     "gq_worker_mean": (_i32, [_p, _p, _i32, _i32, _i64, _p, _i32, _p, _i32, _i32, _u64, _u32,
                               _i32, _p, _p]),
+    "gq_decode_workers": (_i32, [_p, _p, _i32, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _p,
+                                 _p]),
     "gq_logquant": (_i32, [_p, _p, _i64, _i32, _d, _i32, _p, _p, _p, _p]),
     "gq_wire_lane_bytes": (_i32, [_i32, _i32, _i32]),
     "gq_quantize_wire": (_i32, [_p, _p, _i32, _i64, _p, _i32, _p, _i32, _i32, _u64, _u32, _u32,
@@ -300,6 +302,23 @@ def worker_mean(grads, scales, grid, levels, seed, out_dtype=F32, index_base=0, 
     ctx.check(_lib.gq_worker_mean(ctx.handle, _ptr_array(ptrs), len(grads), _elt(grads[0]), n,
                                   off, nseg, _dev(scales, "scales", torch.float32), grid, levels,
                                   seed, index_base, out_dtype, _dev(out, "out"), _stream()))
+    return out
+
+
+def decode_workers(codes, n, scales, grid, levels, bits, out_dtype=F32, offsets=None, out=None,
+                   ctx: Optional[Context] = None):
+    """Receiver's mean of K workers' packed codes (list of uint8 tensors), each decoded with
+    its own scale (scales: K x nseg fp32)."""
+    ctx = ctx or context()
+    off, nseg, keep = _offsets(offsets, n)
+    if scales.numel() != len(codes) * nseg:
+        raise ValueError("scales must hold K * nseg values")
+    if out is None:
+        out = torch.empty(n, dtype=_torch_dtype(out_dtype), device=codes[0].device)
+    cptr = _ptr_array([_dev(c, "codes[%d]" % k, torch.uint8) for k, c in enumerate(codes)])
+    ctx.check(_lib.gq_decode_workers(ctx.handle, cptr, len(codes), n, off, nseg,
+                                     _dev(scales, "scales", torch.float32), grid, levels, bits,
+                                     out_dtype, _dev(out, "out"), _stream()))
     return out
 
 

@@ -258,7 +258,15 @@ def rows_baselines(torch, gq, W, grads, w, row, it):
                                                       out=out), it)
         row("worker_mean_%s_1.3G_s127_K8" % tag, ms, K * n * 4 + n * 4,
             "each worker quantised and decoded with its own scale, fp32 mean out")
-    del out
+    # the receiver after an allgather of int8 codes (QSGD scales): K code streams in, fp32 out
+    Sq = gq.worker_scales(grads, gq.NORM_L2)
+    codes = [gq.quantize_pack(grads[k], Sq[k].clone(), w.grid, w.levels, w.bits, 1, k)
+             for k in range(K)]
+    ms = time_calls(torch, lambda: gq.decode_workers(codes, n, Sq, w.grid, w.levels, w.bits, 0,
+                                                     out=out), it)
+    row("decode_workers_int8_1.3G_K8", ms, K * n + n * 4,
+        "K int8 code streams in, each decoded with its worker's own scale, fp32 mean out")
+    del out, codes
     torch.cuda.empty_cache()
     w2 = W.get("resnet50-161t-f32-K8-exp7")
     g2 = W.gradients(w2, "cuda")

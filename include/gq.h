@@ -186,6 +186,18 @@ gq_status gq_worker_mean(gq_ctx *ctx, const void *const *grads, int32_t K, int32
                          int32_t grid, int32_t levels, uint64_t seed, uint32_t index_base,
                          int32_t out_dtype, void *out, void *stream);
 
+/* The receiver's side of these baselines after an allgather of the workers' b-bit codes:
+ *   acc = +0;  for k = 0..K-1 in order: acc = fma((float)lin(code_{k,i}), f_{k,g}, acc)
+ * with f_{k,g} as in gq_worker_mean; stored as fp32 or bf16.  Equal bit for bit to
+ * gq_worker_mean when code_k is gq_quantize_pack's output for worker k under scale row k.
+ *   codes   (host) array of K device pointers to packed codes of n elements (as
+ *           gq_quantize_pack writes them);  scales K*nseg fp32 (device), k-major
+ *   grid, levels, bits as in gq_quantize_pack;  out n elements of out_dtype */
+gq_status gq_decode_workers(gq_ctx *ctx, const uint8_t *const *codes, int32_t K, int64_t n,
+                            const int64_t *offsets, int32_t nseg, const float *scales,
+                            int32_t grid, int32_t levels, int32_t bits, int32_t out_dtype,
+                            void *out, void *stream);
+
 /* LQ-SGD log quantiser on each column of F (rows x r, row-major fp32; LQ-SGD review, Eq. 5
  * with the max-magnitude normalisation of referee major comment 1, decode by Eq. 6):
  *   m_c = max_i |F_ic|;  y = fp32(|F_ic| / m_c);

@@ -59,6 +59,28 @@ def _check_mean(orc, g, xs_np, scales, grid, levels, seed, offsets=None, out_dty
     return ref
 
 
+def _check_decode(orc, g, xs_np, scales, grid, levels, bits, seed, mean_ref, offsets=None,
+                  out_dtype=0):
+    """Receiver side: each worker's codes from gq_quantize_pack under its own scale row,
+    decoded by gq_decode_workers; equal to the oracle's decode of its own codes and to the
+    per-worker-scale mean."""
+    n = xs_np[0].size
+    off = offsets
+    codes_d, codes_h = [], []
+    for k, x in enumerate(xs_np):
+        row = np.ascontiguousarray(scales[k], np.float32)
+        cd = g.quantize_pack(dev(x), dev(row), grid, levels, bits, seed, k, 0, off)
+        ch = orc.pack(orc.quantize(x, row, grid, levels, seed, k, 0, off), grid, bits)
+        assert np.array_equal(host(cd), ch), first_diff(host(cd), ch)
+        codes_d.append(cd)
+        codes_h.append(ch)
+    ref = orc.decode_workers(codes_h, n, scales, grid, levels, bits, off, out_dtype)
+    got = host(g.decode_workers(codes_d, n, dev(np.ascontiguousarray(scales, np.float32)), grid,
+                                levels, bits, out_dtype, off))
+    assert np.array_equal(got, ref), first_diff(got, ref)
+    assert np.array_equal(ref, mean_ref), first_diff(ref, mean_ref)
+
+
 @pytest.mark.parametrize("name,norm,grid,levels", [
     ("flat-1.3G-f32-K8-uniform127", 0, U, 127),       # QSGD
     ("flat-1.3G-f32-K8-uniform127", 1, U, 127),       # QSGDinf
@@ -76,7 +98,8 @@ def test_workloads(orc, name, norm, grid, levels):
     off = w.offsets if w.nseg > 1 else None
     S = _check_scales(orc, g, xs, off, norm)
     out_dtype = 1 if w.out_dtype == "bf16" else 0
-    _check_mean(orc, g, xs, S, grid, levels, seed=41, offsets=off, out_dtype=out_dtype)
+    mean = _check_mean(orc, g, xs, S, grid, levels, seed=41, offsets=off, out_dtype=out_dtype)
+    _check_decode(orc, g, xs, S, grid, levels, w.bits, 41, mean, off, out_dtype)
 
 
 @pytest.mark.parametrize("K", [1, 3, 5, 8, 16, 17])
@@ -90,6 +113,9 @@ def test_worker_counts_and_ragged_tail(orc, K, grid, levels):
           for _ in range(K)]
     S = _check_scales(orc, g, xs, None, 0)
     _check_mean(orc, g, xs, S, grid, levels, seed=7, index_base=12345)
+    bits = 8 if levels > 7 else 4
+    mean = _check_mean(orc, g, xs, S, grid, levels, seed=7)
+    _check_decode(orc, g, xs, S, grid, levels, bits, 7, mean)
 
 
 def test_bf16_inputs_and_outputs(orc):
@@ -100,8 +126,10 @@ def test_bf16_inputs_and_outputs(orc):
     xs = [((rng.standard_t(3, n) * 1e-3).astype(np.float32).view(np.uint32) >> 16)
           .astype(np.uint16) for _ in range(6)]
     S = _check_scales(orc, g, xs, None, 1)
-    _check_mean(orc, g, xs, S, U, 7, seed=2, out_dtype=1)
-    _check_mean(orc, g, xs, S, X, 7, seed=2, out_dtype=0)
+    mean = _check_mean(orc, g, xs, S, U, 7, seed=2, out_dtype=1)
+    _check_decode(orc, g, xs, S, U, 7, 4, 2, mean, out_dtype=1)
+    mean = _check_mean(orc, g, xs, S, X, 7, seed=2, out_dtype=0)
+    _check_decode(orc, g, xs, S, X, 7, 4, 2, mean)
 
 
 def test_zero_and_unusable_workers(orc):
@@ -159,12 +187,15 @@ def test_empty_and_segments(orc):
     for norm in (0, 1):
         S = _check_scales(orc, g, xs, off, norm)
         assert np.all(S[:, [0, 2, 5]] == 0)
-        _check_mean(orc, g, xs, S, U, 15, seed=5, offsets=off)
+        mean = _check_mean(orc, g, xs, S, U, 15, seed=5, offsets=off)
+        _check_decode(orc, g, xs, S, U, 15, 8, 5, mean, off)
     x0 = torch.empty(0, dtype=torch.float32, device="cuda")
     S0 = g.worker_scales([x0, x0], 0)
     assert host(S0).tolist() == [[0.0], [0.0]]
     out = g.worker_mean([x0, x0], S0, U, 7, 1)
     assert out.numel() == 0
+    c0 = torch.empty(0, dtype=torch.uint8, device="cuda")
+    assert g.decode_workers([c0, c0], 0, S0, U, 7, 4).numel() == 0
 
 
 def test_host_checks():
@@ -186,4 +217,11 @@ def test_host_checks():
     assert e.value.code == g.EINVAL
     with pytest.raises(g.GQError) as e:
         g.worker_mean([x], S, U, 7, 1, index_base=2 ** 32 - 8)
+    assert e.value.code == g.EINVAL
+    c = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(g.GQError) as e:
+        g.decode_workers([c], 16, S, U, 8, 4)   # 8 levels do not fit 4-bit codes
+    assert e.value.code == g.EINVAL
+    with pytest.raises(g.GQError) as e:
+        g.decode_workers([c], 16, S, U, 7, 6)
     assert e.value.code == g.EINVAL
