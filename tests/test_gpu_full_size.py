@@ -13,6 +13,9 @@ The oracle cannot quantise 1e10 elements within a test, so at full size:
   elements (ragged end), both sides of segment boundaries (up to 40 of them), both sides of
   tile boundaries, elements past 2^31 and 2^32 bytes into a buffer, and seeded random
   positions.  The decoded means must match bit for bit.
+* The per-worker-scale baseline (each worker's own L2 scale, the oracle's norms rounded to
+  fp32) runs on the same buffers, as the one-pass gq_worker_mean and as gq_decode_workers of
+  the workers' packed codes; the same sampled runs must match the oracle's mean bit for bit.
 """
 from concurrent.futures import ThreadPoolExecutor
 
@@ -124,5 +127,28 @@ def test_full_size_norm_and_fused_sampled(orc, name):
         got = host(out[a:b])
         assert np.array_equal(got, ref["mean"]), "run [%d, %d) seg %d: %s" % (
             a, b, seg, first_diff(got, ref["mean"]))
-    del xs, out
+    del out
+
+    # the per-worker-scale baseline on the same buffers: each worker's own L2 scale (the
+    # oracle's norms rounded once to fp32), the one-pass mean and the receiver's decode of
+    # every worker's packed codes, sampled against the oracle's one-pass mean
+    Sw = norms_ref.astype(np.float32)
+    Sw_d = torch.from_numpy(np.ascontiguousarray(Sw)).to("cuda")
+    out_w = g.worker_mean(xs, Sw_d, w.grid, w.levels, SEED, out_dtype, offsets=w.offsets)
+    codes = [g.quantize_pack(xs[k], torch.from_numpy(np.ascontiguousarray(Sw[k])).to("cuda"),
+                             w.grid, w.levels, w.bits, SEED, k, 0, w.offsets)
+             for k in range(w.K)]
+    out_d = g.decode_workers(codes, w.n, Sw_d, w.grid, w.levels, w.bits, out_dtype,
+                             offsets=w.offsets)
+    torch.cuda.synchronize()
+    say("per-worker-scale mean and receiver decode done", name)
+    for a, b, seg in runs:
+        xs_run = [W.to_numpy(x[a:b]) for x in xs]
+        ref = orc.worker_mean(xs_run, np.ascontiguousarray(Sw[:, seg:seg + 1]), w.grid,
+                              w.levels, SEED, index_base=a, out_dtype=out_dtype)
+        for what, o in (("worker_mean", out_w), ("decode_workers", out_d)):
+            got = host(o[a:b])
+            assert np.array_equal(got, ref), "%s run [%d, %d) seg %d: %s" % (
+                what, a, b, seg, first_diff(got, ref))
+    del xs, out_w, out_d, codes
     torch.cuda.empty_cache()
