@@ -108,9 +108,24 @@ __device__ __forceinline__ void load_q_rows(const float *Q, int64_t j, float (&q
   }
 }
 
-__device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+// v of another lane by a DPP row operation (CTRL) in the rows ROW_MASK enables; 0 elsewhere.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF,
+                                                    false));
+}
+
+// Sum over the wave with DPP row operations only (no LDS traffic, fixed order); the total is
+// in lane 63.  Pairs and quads (quad_perm), half-rows (row_half_mirror), rows (row_mirror),
+// then row 0 into row 1 and row 2 into row 3 (row_bcast:15), then rows 0-1 into 2-3
+// (row_bcast:31).
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  v += dpp_f<0xB1, 0xF>(v);
+  v += dpp_f<0x4E, 0xF>(v);
+  v += dpp_f<0x141, 0xF>(v);
+  v += dpp_f<0x140, 0xF>(v);
+  v += dpp_f<0x142, 0xA>(v);
+  v += dpp_f<0x143, 0xC>(v);
   return v;
 }
 
@@ -187,8 +202,8 @@ __global__ __launch_bounds__(kBlockA) void k_lq_ef_mq(const float *__restrict__ 
   for (int rr = 0; rr < kRowsA; ++rr)
 #pragma unroll
     for (int c = 0; c < RANK; ++c) {
-      const float s = wave_sum_f(acc[rr][c]);
-      if (lane == 0) red[w][rr * RANK + c] = s;
+      const float s = wave_sum_to_lane63(acc[rr][c]);
+      if (lane == 63) red[w][rr * RANK + c] = s;
     }
   __syncthreads();
   if (threadIdx.x < kRowsA * RANK) {
