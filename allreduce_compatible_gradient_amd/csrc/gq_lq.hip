@@ -375,9 +375,9 @@ __global__ __launch_bounds__(solve_block<RANK>()) void k_lq_solve(const double *
 // of the first column tile also store them (Pt for the quantiser, the optional p_pre copy)
 // and take the column maxima of Pt: the bit patterns of non-negative floats order like
 // unsigned integers, so integer atomicMax (in LDS per block, then once per column in memory)
-// is the exact, order-independent maximum.  Wave w takes rows w, w + 8, ... of the chunk,
-// loaded 8 at a time; the 8 waves' sums are combined in LDS in wave order in one round and
-// written as contiguous (j, c) runs.
+// is the exact, order-independent maximum.  Wave w takes rows w, w + 8, ... of the chunk, in
+// batches of loads issued together; waves 4..7 hand their sums to waves 0..3 through LDS, and
+// the four pair sums are added in wave order and written as contiguous (j, c) runs.
 template <int RANK, int VEC, int ROWSC>
 __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict__ M,
                                                          const float *__restrict__ P,
@@ -388,10 +388,12 @@ __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict
                                                          float *__restrict__ part, int64_t n,
                                                          int64_t m) {
   constexpr int RW = ROWSC / kWavesC;   // rows per wave
-  constexpr int RB = (RANK <= 4 || RW < 8) ? RW : 8;  // rows per load batch (all of them at low rank)
+  // rows per load batch: all of them at low rank; 4 above, which with the half-size LDS
+  // reduction below lets a CU hold more blocks at once
+  constexpr int RB = RANK <= 4 ? RW : 4;
   static_assert(RW % RB == 0, "row batches must tile the wave's rows");
   constexpr int COLS = 64 * VEC;        // columns per block
-  __shared__ float red[kWavesC][COLS * RANK];
+  __shared__ float red[kWavesC / 2][COLS * RANK];
   __shared__ float ptile[ROWSC * RANK];
   __shared__ unsigned smax[RANK];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -468,17 +470,30 @@ __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict
       }
     }
   }
+  // waves 4..7 hand their sums to waves 0..3, which add them and leave the four sums in LDS
+  if (w >= kWavesC / 2) {
 #pragma unroll
-  for (int v = 0; v < VEC; ++v)
+    for (int v = 0; v < VEC; ++v)
 #pragma unroll
-    for (int c = 0; c < RANK; ++c) red[w][(lane * VEC + v) * RANK + c] = acc[v][c];
+      for (int c = 0; c < RANK; ++c) red[w - kWavesC / 2][(lane * VEC + v) * RANK + c] = acc[v][c];
+  }
+  __syncthreads();
+  if (w < kWavesC / 2) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v)
+#pragma unroll
+      for (int c = 0; c < RANK; ++c) {
+        float *slot = &red[w][(lane * VEC + v) * RANK + c];
+        *slot = acc[v][c] + *slot;
+      }
+  }
   __syncthreads();
   const int64_t ncols = m - j0 < COLS ? m - j0 : COLS;
   float *dst = part + ((int64_t)blockIdx.y * m + j0) * RANK;
   for (int o = threadIdx.x; o < ncols * RANK; o += kWavesC * 64) {
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kWavesC; ++i) s += red[i][o];
+    for (int i = 0; i < kWavesC / 2; ++i) s += red[i][o];
     dst[o] = s;
   }
 }
