@@ -234,24 +234,34 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
+// 1/sqrt(d) for a positive normal d (a pivot of a Gram matrix of fp32 vectors always is): the
+// hardware estimate refined by two Newton steps y <- y (3/2 - (d/2) y^2), each of which
+// squares the relative error, so the result is good to fp64 rounding.
+__device__ __forceinline__ double rsqrt_refined(double d) {
+  const double h = 0.5 * d;
+  double y = __builtin_amdgcn_rsq(d);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) y = fma(y, fma(-h * y, y, 0.5), y);
+  return y;
+}
+
 // Upper-triangular T with (P T)^T (P T) = I given G = P^T P, column by column as Gram-Schmidt
 // does it, through the Cholesky factor: G = R^T R (R upper triangular; a pivot below 2^-32 of
 // the column's squared norm marks a column with no remaining norm of its own -- zero, or a
 // combination of the earlier columns up to fp32 rounding -- whose row of R and column of T
-// are zero),
-// then T[:, c] = (e_c - sum_{k<c} R[k][c] T[:, k]) / R[c][c].
-// Spread over the lanes of one wave: lane j (< RANK) holds column j of G (g[k] = G[k][j]),
-// of R and of T; the entries a step needs from another column are read from its lane with
-// v_readlane (uniform values).  Every entry is formed with the same operations in the same
-// order as the one-thread form of these formulas.
+// are zero), and T = R^-1 from T R = I: T[a][c] = (delta_ac - sum_{k<c} T[a][k] R[k][c]) / R[c][c].
+// Spread over the lanes of one wave: lane j (< RANK) holds column j of G (g[k] = G[k][j]) and
+// of R, and row j of T.  Step c reads column c of R from lane c with v_readlane (uniform
+// values); with it every lane forms its own entries of row c of R and of column c of T, so T
+// needs no exchange at all.  Products accumulate by fused multiply-add in fp64.
 template <int RANK>
-__device__ __forceinline__ void lane_gram_schmidt_T(const double (&g)[RANK], int j,
-                                                    double (&tcol)[RANK]) {
+__device__ __forceinline__ void lane_cholqr_T(const double (&g)[RANK], int j,
+                                              double (&trow)[RANK]) {
   double rcol[RANK];  // R[k][j]
 #pragma unroll
   for (int k = 0; k < RANK; ++k) {
     rcol[k] = 0.0;
-    tcol[k] = 0.0;
+    trow[k] = 0.0;
   }
 #pragma unroll
   for (int c = 0; c < RANK; ++c) {
@@ -261,23 +271,20 @@ __device__ __forceinline__ void lane_gram_schmidt_T(const double (&g)[RANK], int
     const double gcc = readlane_d(g[c], c);  // G[c][c]: the column's squared norm
     double d = gcc;
 #pragma unroll
-    for (int k = 0; k < c; ++k) d -= rkc[k] * rkc[k];
+    for (int k = 0; k < c; ++k) d = fma(-rkc[k], rkc[k], d);
     // less than 2^-32 of the squared norm left: dependent on the earlier columns, set to zero
     if (d > 0x1p-32 * gcc) {  // the same value in every lane
-      const double rc = sqrt(d), inv = 1.0 / rc;
+      const double inv = rsqrt_refined(d), rc = d * inv;
       double v = g[c];  // G[c][j]
+      double u = j == c ? 1.0 : 0.0;
 #pragma unroll
-      for (int k = 0; k < c; ++k) v -= rkc[k] * rcol[k];
+      for (int k = 0; k < c; ++k) {
+        v = fma(-rkc[k], rcol[k], v);
+        u = fma(-trow[k], rkc[k], u);  // T[j][k] R[k][c]; T[j][k] = 0 for k < j
+      }
       if (j > c) rcol[c] = v * inv;
       if (j == c) rcol[c] = rc;
-      // column c of T (uniform values; lane c keeps them)
-#pragma unroll
-      for (int a = 0; a <= c; ++a) {
-        double u = a == c ? 1.0 : 0.0;
-#pragma unroll
-        for (int k = a; k < c; ++k) u -= rkc[k] * readlane_d(tcol[a], k);  // T[a][k], a <= k
-        if (j == c) tcol[a] = u * inv;
-      }
+      trow[c] = u * inv;
     }
   }
 }
@@ -291,6 +298,7 @@ __global__ __launch_bounds__(solve_block<RANK>()) void k_lq_solve(const double *
                                                           unsigned *__restrict__ cmax_bits) {
   constexpr int NG = RANK * (RANK + 1) / 2;
   __shared__ double Gs[RANK][RANK];
+  __shared__ double T1s[RANK][RANK], T2s[RANK][RANK];  // rows of T1 and of T2
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid < 2 * RANK) cmax_bits[tid] = 0u;  // column maxima of Pt and Q' start at +0
   // wave w sums entries t = w, w + NW, ...: lane l adds blocks l, l + 64, ... in order, UB
@@ -327,46 +335,59 @@ __global__ __launch_bounds__(solve_block<RANK>()) void k_lq_solve(const double *
     }
   }
   __syncthreads();
-  // r x r part in wave 0 (lane j < RANK owns column j; lanes beyond compute lane 0's values)
-  if (w != 0) return;
+  // r x r part in wave 0 (lane j < RANK owns column j of G and row j of T; lanes beyond
+  // compute lane 0's values); the other waves only take part in the barriers
   const int jc = lane < RANK ? lane : 0;
-  double g[RANK], t1[RANK], t2[RANK], gt[RANK];
+  if (w == 0) {
+    double g[RANK], t1[RANK];
 #pragma unroll
-  for (int k = 0; k < RANK; ++k) g[k] = Gs[k][jc];
-  lane_gram_schmidt_T<RANK>(g, jc, t1);
-  // column jc of G T1: entry x sums G[x][b] T1[b][jc] over b <= jc (G[x][b] = g[x] of lane b)
+    for (int k = 0; k < RANK; ++k) g[k] = Gs[k][jc];
+    lane_cholqr_T<RANK>(g, jc, t1);
+    if (lane < RANK)
 #pragma unroll
-  for (int x = 0; x < RANK; ++x) {
-    double sum = 0.0;
+      for (int k = 0; k < RANK; ++k) T1s[lane][k] = t1[k];
+  }
+  __syncthreads();
+  if (w == 0) {
+    // column jc of W = G T1 (T1[x][jc] = 0 for x > jc), then column jc of T1^T W, the Gram
+    // matrix of P T1; the entries of G and T1 are broadcast from LDS
+    double wcol[RANK];
 #pragma unroll
-    for (int b = 0; b < RANK; ++b) {
-      const double gxb = readlane_d(g[x], b);
-      if (b <= jc) sum += gxb * t1[b];
+    for (int b = 0; b < RANK; ++b) wcol[b] = 0.0;
+#pragma unroll 1
+    for (int x = 0; x < RANK; ++x) {
+      const double tx = T1s[x][jc];
+#pragma unroll
+      for (int b = 0; b < RANK; ++b) wcol[b] = fma(Gs[b][x], tx, wcol[b]);
     }
-    gt[x] = sum;
-  }
-  // column jc of T1^T G T1 (the Gram matrix of P T1): entry c sums T1[b][c] (G T1)[b][jc]
-  // over b <= c
+    double g[RANK];
 #pragma unroll
-  for (int c = 0; c < RANK; ++c) {
-    double sum = 0.0;
-#pragma unroll
-    for (int b = 0; b <= c; ++b) sum += readlane_d(t1[b], c) * gt[b];
-    g[c] = sum;
-  }
-  lane_gram_schmidt_T<RANK>(g, jc, t2);
-  // column jc of T = T1 T2: entry a sums T1[a][k] T2[k][jc] over a <= k <= jc
-  if (lane < RANK) {
-#pragma unroll
-    for (int a = 0; a < RANK; ++a) {
+    for (int c = 0; c < RANK; ++c) {
       double sum = 0.0;
 #pragma unroll
-      for (int k = a; k < RANK; ++k) {
-        const double t1ak = readlane_d(t1[a], k);
-        if (k <= jc) sum += t1ak * t2[k];
-      }
-      Tout[a * RANK + jc] = sum;
+      for (int b = 0; b <= c; ++b) sum = fma(T1s[b][c], wcol[b], sum);
+      g[c] = sum;
     }
+    double t2[RANK];
+    lane_cholqr_T<RANK>(g, jc, t2);
+    if (lane < RANK)
+#pragma unroll
+      for (int k = 0; k < RANK; ++k) T2s[lane][k] = t2[k];
+  }
+  __syncthreads();
+  // row jc of T = T1 T2: T[jc][c] sums T1[jc][k] T2[k][c] over k (T1[jc][k] = 0 for k < jc)
+  if (w == 0 && lane < RANK) {
+    double trow[RANK];
+#pragma unroll
+    for (int c = 0; c < RANK; ++c) trow[c] = 0.0;
+#pragma unroll 1
+    for (int k = 0; k < RANK; ++k) {
+      const double t1k = T1s[jc][k];
+#pragma unroll
+      for (int c = 0; c < RANK; ++c) trow[c] = fma(t1k, T2s[k][c], trow[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < RANK; ++c) Tout[jc * RANK + c] = trow[c];
   }
 }
 
