@@ -335,6 +335,10 @@ __device__ __forceinline__ float seg_decode(float S, double denom) {
 }
 
 // ---------------------------------------------------------------- element quantisers
+// The sign of a level: the uniform grid applies sign(x) as copysign does and the exponential
+// grid as the comparison x < 0; they differ only for a NaN element under a caller-given finite
+// scale (clamped to the top level), which keeps its sign bit on the uniform grid and counts
+// as positive on the exponential one -- each the form its kernel computes at no extra cost.
 // Uniform grid.  Returns the level magnitude m in [0, s] as a float (exact small integer);
 // the signed level is copysign(m, x).
 __device__ __forceinline__ float quant_uniform_mag(float x, float inv, float sf, uint32_t h) {
@@ -361,10 +365,6 @@ __device__ __forceinline__ uint32_t quant_exp_index(float x, float inv, int E, f
   return (low ? 0u : (uint32_t)jn) + (h < c ? 1u : 0u);
 }
 
-// Sign of an element: its sign bit, so a NaN under a caller-given finite scale (clamped to the
-// top level) keeps the sign its bits give it on both grids.
-__device__ __forceinline__ bool sign_of(float x) { return __float_as_int(x) < 0; }
-
 // Code field of a uniform level (signed, two's complement in `bits`).
 __device__ __forceinline__ uint32_t uniform_code(float m, float x, int bits) {
   return (uint32_t)(int32_t)copysignf(m, x) & ((1u << bits) - 1u);
@@ -372,7 +372,7 @@ __device__ __forceinline__ uint32_t uniform_code(float m, float x, int bits) {
 
 // Code field of an exponential index: sign bit above j (zero has no sign).
 __device__ __forceinline__ uint32_t exp_code(uint32_t j, float x, int bits) {
-  return ((sign_of(x) && j > 0) ? (1u << (bits - 1)) : 0u) | j;
+  return ((x < 0.0f && j > 0) ? (1u << (bits - 1)) : 0u) | j;
 }
 
 // Signed integer value on the common grid of an exponential index: sign * 2^(j-1), 0 for j = 0.
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
             if constexpr (GRID == 0)
               lin = (int32_t)copysignf(quant_uniform_mag(x[e], q.inv, sf, h), x[e]);
             else
-              lin = exp_lin(quant_exp_index(x[e], q.inv, a.levels, two_em1, h), sign_of(x[e]));
+              lin = exp_lin(quant_exp_index(x[e], q.inv, a.levels, two_em1, h), x[e] < 0.0f);
             v[e] = (uint32_t)(lin + a.offset);
           }
         } else {
@@ -797,7 +797,7 @@ __device__ __forceinline__ void fused_batch(const FusedArgs &a, int k0, int kn,
           if constexpr (STORE) c[e] = uniform_code(m, xv, a.bits);
         } else {
           const uint32_t jj = quant_exp_index(xv, q.inv, a.levels, two_em1, h);
-          acci[j][e] += exp_lin(jj, sign_of(xv));
+          acci[j][e] += exp_lin(jj, xv < 0.0f);
           if constexpr (STORE) c[e] = exp_code(jj, xv, a.bits);
         }
       }
@@ -1020,7 +1020,7 @@ __device__ __forceinline__ void worker_batch(const WorkerMeanArgs &a, int k0, in
         if constexpr (GRID == 0)
           l = copysignf(quant_uniform_mag(xv, inv, sf, h), xv);
         else
-          l = (float)exp_lin(quant_exp_index(xv, inv, a.levels, two_em1, h), sign_of(xv));
+          l = (float)exp_lin(quant_exp_index(xv, inv, a.levels, two_em1, h), xv < 0.0f);
         acc[j][e] = fmaf(l, fac, acc[j][e]);  // one rounding per worker, in worker order
       }
   }

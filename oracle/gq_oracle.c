@@ -199,7 +199,7 @@ static int32_t quant_exp(int32_t E, float x, float S, uint32_t key, uint32_t cou
     r = orc_uniform(key, counter);
     if (r < p)
         j += 1;
-    return (signbit(x) && j > 0) ? -j : j;
+    return (x < 0.0f && j > 0) ? -j : j; /* a NaN counts as positive here */
 }
 
 int32_t orc_quant_one(int32_t grid, int32_t levels, float x, float S, uint32_t key,

@@ -66,8 +66,8 @@ int32_t orc_global_norm(const void *const *xs, int32_t K, int32_t dtype, int64_t
 /* ---------------- stochastic quantisation ---------------- */
 /* Signed level of one element.  Uniform: value in [-s, s] (levels = s).
  * Exponential: sign * j with j in [0, E] (levels = E), level j>0 meaning 2^(j-E).
- * A NaN element (possible only under a caller-given finite scale) goes to the top level with
- * the sign of its sign bit. */
+ * A NaN element (possible only under a caller-given finite scale) goes to the top level, with
+ * the sign of its sign bit on the uniform grid and as positive on the exponential grid. */
 int32_t orc_quant_one(int32_t grid, int32_t levels, float x, float S, uint32_t key,
                       uint32_t counter);
 /* Quantise a segmented buffer of one worker; counter of element i is index_base + i. */

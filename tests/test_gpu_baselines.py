@@ -153,8 +153,9 @@ def test_zero_and_unusable_workers(orc):
 
 
 def test_nan_elements_under_a_given_scale(orc):
-    """With a finite scale given by the caller a NaN element takes the top level with its sign
-    bit's sign, in the baseline mean, the Global-QSGD codes and the fused pass alike."""
+    """With a finite scale given by the caller a NaN element takes the top level (sign bit's
+    sign on the uniform grid, positive on the exponential grid), in the baseline mean, the
+    Global-QSGD codes and the fused pass alike."""
     g = gq()
     say("baseline nan")
     n = 1000

@@ -460,9 +460,10 @@ def test_mean_is_unbiased_end_to_end(orc):
     assert np.all(np.abs(acc / N - true) < 5 * sd)
 
 
-def test_nan_goes_to_the_top_level_with_its_sign_bit(orc):
-    """Under a caller-given finite scale a NaN element is clamped to the top level; the
-    sign is the NaN's sign bit (the pages say nothing of NaN: a reading)."""
+def test_nan_goes_to_the_top_level(orc):
+    """Under a caller-given finite scale a NaN element is clamped to the top level, with its
+    sign bit's sign on the uniform grid and as positive on the exponential grid (the pages
+    say nothing of NaN: a reading)."""
     pos = np.float32(np.nan)
     neg = np.uint32(0xFFC00000).view(np.float32)
     x = np.array([pos, neg, 1.0, -1.0], np.float32)
@@ -470,4 +471,4 @@ def test_nan_goes_to_the_top_level_with_its_sign_bit(orc):
         q = _q(orc, x, 4.0, U, 31, seed)
         assert q[0] == 31 and q[1] == -31
         q = _q(orc, x, 4.0, X, 7, seed)
-        assert q[0] == 7 and q[1] == -7
+        assert q[0] == 7 and q[1] == 7
