@@ -519,28 +519,52 @@ __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict
   }
 }
 
-// Pass 2 (final): Q'[j][c] = sum over chunks, in chunk order (loads issued 32 chunks at a
-// time), and the column maxima of Q' (as for Pt in k_lq_mtp).
-template <int RANK>
+// Pass 2 (final): Q'[j][c] = sum over the chunks' partials and the column maxima of Q' (as for
+// Pt in k_lq_mtp).  Each output is summed by G threads -- group g takes chunks g, g + G, ...
+// in order, with a batch of loads in flight -- and the group sums are added in group order.
+// G = 1 normally; a short factor (at most kQsumShort outputs, e.g. rank 1 or 2 of 4096 rows)
+// takes G = 8 so that it still spreads over 128+ blocks.  Every block publishes its column
+// maxima once (r global atomics per block).
+constexpr int kQsumShort = 8192;
+
+template <int RANK, int G>
 __global__ __launch_bounds__(256) void k_lq_qsum(const float *__restrict__ part,
                                                  float *__restrict__ Qn, float *__restrict__ q_pre,
                                                  unsigned *__restrict__ cmax_bits, int64_t count,
                                                  int nchunks) {
+  constexpr int OUT = 256 / G, NB = 32 / G > 8 ? 32 / G : 8;  // outputs per block, loads per batch
+  __shared__ float ps[G][OUT];
   __shared__ unsigned smax[RANK];
+  const int il = threadIdx.x % OUT, g = threadIdx.x / OUT;
+  const int64_t i = (int64_t)blockIdx.x * OUT + il;
   if (threadIdx.x < RANK) smax[threadIdx.x] = 0u;
-  __syncthreads();
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  float s = 0.0f;
   if (i < count) {
-    float s = 0.0f;
-    for (int ch0 = 0; ch0 < nchunks; ch0 += 32) {
-      float v[32];
+    for (int ch0 = g; ch0 < nchunks; ch0 += NB * G) {
+      float v[NB];
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        v[u] = ch0 + u < nchunks ? part[(int64_t)(ch0 + u) * count + i] : 0.0f;
+      for (int u = 0; u < NB; ++u) {
+        const int ch = ch0 + u * G;
+        v[u] = ch < nchunks ? part[(int64_t)ch * count + i] : 0.0f;
+      }
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        if (ch0 + u < nchunks) s += v[u];
+      for (int u = 0; u < NB; ++u)
+        if (ch0 + u * G < nchunks) s += v[u];
     }
+  }
+  if constexpr (G > 1) {
+    ps[g][il] = s;
+    __syncthreads();
+    if (g == 0) {
+      float t = 0.0f;
+#pragma unroll
+      for (int k = 0; k < G; ++k) t += ps[k][il];
+      s = t;
+    }
+  } else {
+    __syncthreads();  // smax is initialised
+  }
+  if (g == 0 && i < count) {
     Qn[i] = s;
     if (q_pre) q_pre[i] = s;
     atomicMax(&smax[i % RANK], __float_as_uint(fabsf(s)));
@@ -781,8 +805,13 @@ void launch_step(const LqStepArgs &a, const StepBufs &b, const LqTables &tp, con
   else
     hipLaunchKernelGGL((k_lq_mtp<RANK, VEC, 128>), gcol, dim3(kWavesC * 64), 0, s, a.E, b.P,
                        b.T, b.Pt, a.p_pre, b.cmax_bits, b.part, n, m);
-  hipLaunchKernelGGL((k_lq_qsum<RANK>), dim3((unsigned)((m * RANK + 255) / 256)), dim3(256), 0,
-                     s, b.part, b.Qn, a.q_pre, b.cmax_bits + RANK, m * RANK, b.nchunks);
+  if (m * RANK <= kQsumShort)
+    hipLaunchKernelGGL((k_lq_qsum<RANK, 8>), dim3((unsigned)((m * RANK + 31) / 32)), dim3(256),
+                       0, s, b.part, b.Qn, a.q_pre, b.cmax_bits + RANK, m * RANK, b.nchunks);
+  else
+    hipLaunchKernelGGL((k_lq_qsum<RANK, 1>), dim3((unsigned)((m * RANK + 255) / 256)),
+                       dim3(256), 0, s, b.part, b.Qn, a.q_pre, b.cmax_bits + RANK, m * RANK,
+                       b.nchunks);
   ElemJob je{b.Pt, b.Qn, n, m, RANK, b.cmax_bits, a.p_codes, a.q_codes, a.p_colmax, a.q_colmax,
              b.Ph, a.p_hat, a.Q};
   hipLaunchKernelGGL(k_lq_quant_elems, dim3((unsigned)(((n + m) * RANK + 255) / 256)),
