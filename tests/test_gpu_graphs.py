@@ -125,3 +125,53 @@ def test_two_contexts_on_two_streams():
         assert torch.equal(outs[name], ref), name
     ca.close()
     cb.close()
+
+
+def test_baselines_in_a_graph(orc):
+    """Per-worker scales, the per-worker-scale mean and the receiver's decode of the codes,
+    captured once and replayed on new gradients: every replay equals the eager calls."""
+    g = gq()
+    say("graph: baselines")
+    w = W.reduced("resnet50-161t-f32-K8-exp7")
+    xs = [x.to("cuda") for x in W.gradients(w, "cpu")]
+    gctx, ectx = g.Context(), g.Context()
+    K, n = w.K, w.n
+    Sg = torch.empty(K, w.nseg, dtype=torch.float32, device="cuda")
+    Se = torch.empty_like(Sg)
+    outs = {c: torch.empty(n, dtype=torch.float32, device="cuda") for c in ("mg", "me", "dg", "de")}
+    codes_g = [torch.empty((n + 1) // 2, dtype=torch.uint8, device="cuda") for _ in range(K)]
+    codes_e = [torch.empty_like(c) for c in codes_g]
+    assert (w.nseg * 4) % 16 == 0  # each worker's row of scales is itself 16-byte aligned
+
+    def step(ctx, S, m_out, d_out, codes):
+        g.worker_scales(xs, g.NORM_L2, w.offsets, out=S, ctx=ctx)
+        g.worker_mean(xs, S, w.grid, w.levels, 5, 0, offsets=w.offsets, out=m_out, ctx=ctx)
+        for k in range(K):
+            g.quantize_pack(xs[k], S[k], w.grid, w.levels, w.bits, 5, k, 0, w.offsets,
+                            codes=codes[k], ctx=ctx)
+        g.decode_workers(codes, n, S, w.grid, w.levels, w.bits, 0, w.offsets, out=d_out,
+                         ctx=ctx)
+
+    step(gctx, Sg, outs["mg"], outs["dg"], codes_g)   # sizes the scratch
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(gctx, Sg, outs["mg"], outs["dg"], codes_g)
+    for rep in range(3):
+        for x in xs:
+            x.mul_(-1.5 if rep % 2 == 0 else 0.5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(ectx, Se, outs["me"], outs["de"], codes_e)
+        torch.cuda.synchronize()
+        assert torch.equal(Sg, Se), "replay %d: scales" % rep
+        assert torch.equal(outs["mg"], outs["me"]), "replay %d: mean" % rep
+        assert torch.equal(outs["dg"], outs["de"]), "replay %d: decode" % rep
+        assert torch.equal(outs["dg"], outs["mg"]), "replay %d: decode vs mean" % rep
+    ref = orc.worker_mean([host(x) for x in xs], host(Se), w.grid, w.levels, 5,
+                          offsets=w.offsets)
+    assert np.array_equal(host(outs["mg"]), ref), first_diff(host(outs["mg"]), ref)
+    del graph
+    gctx.close()
+    ectx.close()
