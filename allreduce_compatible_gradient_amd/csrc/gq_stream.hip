@@ -1,6 +1,8 @@
 // gq_stream.hip -- gfx950 kernels of the Global-QSGD path: global norm, stochastic
 // quantisation + packing, integer sum of codes, decode of the mean, the fused single pass,
-// and the summable wire payload (offset-binary lanes that a uint32 Allreduce adds exactly).
+// and the summable wire payload (offset-binary lanes that a uint32 Allreduce adds exactly);
+// and of the per-worker-scale baselines the NUQSGD abstract compares against (QSGD, QSGDinf,
+// NUQSGD): per-worker scales, their one-pass mean and the receiver's decode of their codes.
 //
 // Method (Global-QSGD / "Quantize Once, Train Fast", abstract): one global norm scales every
 // worker; unbiased stochastic rounding onto a grid all workers share; the integer codes are

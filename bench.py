@@ -38,7 +38,14 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(STREAM_SRC, "rb").read()).hexdigest()[:16]
+    """sha256 (16 hex digits) of the streaming kernels' source with comments and whitespace
+    removed: it changes when the code changes, not when a comment does."""
+    import re
+    src = open(STREAM_SRC).read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def measured_traffic(algo_bytes):
