@@ -102,13 +102,13 @@ def test_workloads(orc, name, norm, grid, levels):
     _check_decode(orc, g, xs, S, grid, levels, w.bits, 41, mean, off, out_dtype)
 
 
-@pytest.mark.parametrize("K", [1, 3, 5, 8, 16, 17])
+@pytest.mark.parametrize("K", [1, 3, 5, 8, 16, 17, 64])
 @pytest.mark.parametrize("grid,levels", [(U, 127), (U, 3), (X, 7), (X, 12)])
 def test_worker_counts_and_ragged_tail(orc, K, grid, levels):
     g = gq()
     say("baseline K", K, grid, levels)
     rng = np.random.default_rng(1000 * K + levels)
-    n = 3 * 8192 + 77
+    n = 3 * 8192 + 77 if K < 64 else 8192 + 77
     xs = [(rng.standard_normal(n) * 10.0 ** rng.uniform(-2, 1)).astype(np.float32)
           for _ in range(K)]
     S = _check_scales(orc, g, xs, None, 0)
