@@ -308,3 +308,28 @@ def test_step_fewer_rows_than_rank(orc, n, m, r):
     k = int((~dead).sum())
     assert np.abs(P_pre[:, ~dead].T @ P_pre[:, ~dead] - np.eye(k)).max() < 1e-5
     _check_step(ref, out, Eg, Qg, orthonormal=False)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_step_random_configurations(orc, i):
+    """Seeded random shapes (m not always a multiple of 4), ranks 1-8, alpha in {1, 10, 100}
+    and separate code widths b_p, b_q in 4..8; two steps each, within the step tolerances."""
+    g = gq()
+    rng = np.random.default_rng(70000 + i)
+    r = int(rng.integers(1, 9))
+    n = int(rng.integers(max(r, 8), 2500))
+    m = int(rng.integers(max(r, 8), 2500))
+    alpha = float(rng.choice([1.0, 10.0, 100.0]))
+    bp, bq = int(rng.integers(4, 9)), int(rng.integers(4, 9))
+    say("lq random", i, n, m, r, alpha, bp, bq)
+    E = np.zeros((n, m), np.float32)
+    Q = rng.standard_normal((m, r)).astype(np.float32)
+    U_ = rng.standard_normal((n, 8)) * 1e-3
+    V_ = rng.standard_normal((m, 8))
+    for t in range(2):
+        G = (rng.standard_normal((n, m)) * 1e-3 + U_ @ V_.T).astype(np.float32)
+        ref = orc.powersgd_logquant(G, E, Q, alpha, bp, bits_q=bq)
+        Ed, Qd = dev(E), dev(Q)
+        out = g.powersgd_logquant(dev(G), Ed, Qd, alpha, bp, want_pre=True, bits_q=bq)
+        _check_step(ref, out, host(Ed), host(Qd))
+        E, Q = ref["E"], ref["Q"]
