@@ -97,14 +97,15 @@ _tls = threading.local()
 
 
 def context() -> Context:
-    """Per-thread, per-device default context."""
-    dev = torch.cuda.current_device()
+    """The default context of this thread for the current device and stream (a context's
+    scratch must not be shared by two streams, so each stream gets its own)."""
+    key = (torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)
     ctxs = getattr(_tls, "ctxs", None)
     if ctxs is None:
         ctxs = _tls.ctxs = {}
-    if dev not in ctxs:
-        ctxs[dev] = Context()
-    return ctxs[dev]
+    if key not in ctxs:
+        ctxs[key] = Context()
+    return ctxs[key]
 
 
 def version() -> str:

@@ -175,3 +175,33 @@ def test_baselines_in_a_graph(orc):
     del graph
     gctx.close()
     ectx.close()
+
+
+def test_default_contexts_follow_the_stream():
+    """Without an explicit context each stream gets its own default one, so work issued on two
+    streams at once never shares scratch."""
+    g = gq()
+    say("default contexts per stream")
+    w = W.reduced("resnet50-161t-f32-K8-exp7")
+    xa = [x.to("cuda") for x in W.gradients(w, "cpu")]
+    xb = [(0.5 * x).contiguous() for x in xa]
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(sa):
+        ca = g.context()
+    with torch.cuda.stream(sb):
+        cb = g.context()
+    assert ca is not cb and g.context() is not ca
+    outs = {}
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for name, xs, st in (("a", xa, sa), ("b", xb, sb)):
+            with torch.cuda.stream(st):
+                S, _ = g.global_norm(xs, w.offsets)
+                outs[name] = g.fused_mean(xs, S, w.grid, w.levels, w.bits, 3, w.acc_bits,
+                                          offsets=w.offsets)
+    torch.cuda.synchronize()
+    for name, xs in (("a", xa), ("b", xb)):
+        S, _ = g.global_norm(xs, w.offsets)
+        ref = g.fused_mean(xs, S, w.grid, w.levels, w.bits, 3, w.acc_bits, offsets=w.offsets)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[name], ref), name
