@@ -97,15 +97,18 @@ _tls = threading.local()
 
 
 def context() -> Context:
-    """The default context of this thread for the current device and stream (a context's
-    scratch must not be shared by two streams, so each stream gets its own)."""
-    key = (torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)
+    """The default context of this thread for the current device.  It is shared by every
+    stream, which keeps the usual pattern working -- warm up eagerly, then capture the same
+    calls into a graph on another stream without allocating during capture; work issued on
+    two streams at the same time needs a Context for each (ctx=...), since a context's
+    scratch must not be used by two streams at once."""
+    dev = torch.cuda.current_device()
     ctxs = getattr(_tls, "ctxs", None)
     if ctxs is None:
         ctxs = _tls.ctxs = {}
-    if key not in ctxs:
-        ctxs[key] = Context()
-    return ctxs[key]
+    if dev not in ctxs:
+        ctxs[dev] = Context()
+    return ctxs[dev]
 
 
 def version() -> str:

@@ -177,31 +177,38 @@ def test_baselines_in_a_graph(orc):
     ectx.close()
 
 
-def test_default_contexts_follow_the_stream():
-    """Without an explicit context each stream gets its own default one, so work issued on two
-    streams at once never shares scratch."""
+
+def test_default_context_warm_up_then_capture(orc):
+    """The default context: calls made eagerly first can then be captured on torch's capture
+    stream without allocating, and the replays equal the eager results."""
     g = gq()
-    say("default contexts per stream")
-    w = W.reduced("resnet50-161t-f32-K8-exp7")
-    xa = [x.to("cuda") for x in W.gradients(w, "cpu")]
-    xb = [(0.5 * x).contiguous() for x in xa]
-    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
-    with torch.cuda.stream(sa):
-        ca = g.context()
-    with torch.cuda.stream(sb):
-        cb = g.context()
-    assert ca is not cb and g.context() is not ca
-    outs = {}
+    say("graph: default context")
+    w = W.reduced("gpt2s-148t-bf16-K16-uniform7")
+    xs = [x.to("cuda") for x in W.gradients(w, "cpu")]
+    S = torch.empty(w.nseg, dtype=torch.float32, device="cuda")
+    out = torch.empty(w.n, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        g.global_norm(xs, w.offsets, scale_out=S)
+        g.fused_mean(xs, S, w.grid, w.levels, w.bits, 2, w.acc_bits, 1, offsets=w.offsets,
+                     out=out)
+
+    step()
     torch.cuda.synchronize()
-    for _ in range(3):
-        for name, xs, st in (("a", xa, sa), ("b", xb, sb)):
-            with torch.cuda.stream(st):
-                S, _ = g.global_norm(xs, w.offsets)
-                outs[name] = g.fused_mean(xs, S, w.grid, w.levels, w.bits, 3, w.acc_bits,
-                                          offsets=w.offsets)
-    torch.cuda.synchronize()
-    for name, xs in (("a", xa), ("b", xb)):
-        S, _ = g.global_norm(xs, w.offsets)
-        ref = g.fused_mean(xs, S, w.grid, w.levels, w.bits, 3, w.acc_bits, offsets=w.offsets)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(2):
+        for x in xs:
+            x.mul_(2.0 if rep == 0 else -0.25)
         torch.cuda.synchronize()
-        assert torch.equal(outs[name], ref), name
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(got, out), "replay %d" % rep
+    ref = orc.allreduce_mean([host(x) for x in xs], w.grid, w.levels, w.bits, w.acc_bits, 2, 0,
+                             w.offsets, out_dtype=1, scale=host(S))
+    assert np.array_equal(host(out), ref["mean"]), first_diff(host(out), ref["mean"])
+    del graph
