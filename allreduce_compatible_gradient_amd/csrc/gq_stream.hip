@@ -354,15 +354,16 @@ __device__ __forceinline__ float quant_uniform_mag(float x, float inv, float sf,
 // Exponential grid: index j in [0, E] of the level (level j > 0 is 2^(j-E)).  Above the
 // lowest level u lies in the binade of level j = E + exponent(u), and the probability of
 // rounding up is u / 2^exponent - 1, whose 23 mantissa bits times 2^32 are the integer
-// mantissa << 9; below it, p = u / 2^(1-E) (both scalings exact).
-__device__ __forceinline__ uint32_t quant_exp_index(float x, float inv, int E, float two_em1,
+// mantissa << 9; below it, p = u / 2^(1-E), and p * 2^32 = u * 2^(E+31) is one exact
+// power-of-two scaling (lo_scale = 2^(E+31); u <= 1 keeps it far from overflow).
+__device__ __forceinline__ uint32_t quant_exp_index(float x, float inv, int E, float lo_scale,
                                                     uint32_t h) {
   const float u = fminf(fabsf(x) * inv, 1.0f);
   const uint32_t b = __float_as_uint(u);
   const int32_t jn = (int32_t)(b >> 23) - (127 - E);  // <= 0 below the lowest level
   const bool low = jn <= 0;
   const uint32_t c_hi = (b & 0x7FFFFFu) << 9;
-  const uint32_t c_lo = (uint32_t)ceilf((u * two_em1) * 4294967296.0f);
+  const uint32_t c_lo = (uint32_t)ceilf(u * lo_scale);
   const uint32_t c = low ? c_lo : c_hi;
   return (low ? 0u : (uint32_t)jn) + (h < c ? 1u : 0u);
 }
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
   constexpr int NP = kChunk / (64 * P);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float sf = (float)a.levels;
-  const float two_em1 = ldexpf(1.0f, a.levels - 1);
+  const float lo_scale = ldexpf(1.0f, a.levels + 31);
   for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
     int64_t begin;
     int len, seg;
@@ -520,7 +521,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
             if constexpr (GRID == 0)
               c[e] = uniform_code(quant_uniform_mag(x[e], q.inv, sf, h), x[e], a.bits);
             else
-              c[e] = exp_code(quant_exp_index(x[e], q.inv, a.levels, two_em1, h), x[e], a.bits);
+              c[e] = exp_code(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e], a.bits);
           }
         } else {
 #pragma unroll
@@ -695,7 +696,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
   constexpr int NP = kChunk / (64 * P);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float sf = (float)a.levels;
-  const float two_em1 = ldexpf(1.0f, a.levels - 1);
+  const float lo_scale = ldexpf(1.0f, a.levels + 31);
   for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
     int64_t begin;
     int len, seg;
@@ -721,7 +722,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
             if constexpr (GRID == 0)
               lin = (int32_t)copysignf(quant_uniform_mag(x[e], q.inv, sf, h), x[e]);
             else
-              lin = exp_lin(quant_exp_index(x[e], q.inv, a.levels, two_em1, h), x[e] < 0.0f);
+              lin = exp_lin(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e] < 0.0f);
             v[e] = (uint32_t)(lin + a.offset);
           }
         } else {
@@ -773,7 +774,7 @@ template <int DT, int GRID, int P, int NP, int KB, bool STORE>
 __device__ __forceinline__ void fused_batch(const FusedArgs &a, int k0, int kn,
                                             const int64_t (&e0)[NP], const int (&cnt)[NP],
                                             const uint32_t (&am)[NP][P], const SegQ &q,
-                                            float sf, float two_em1,
+                                            float sf, float lo_scale,
                                             float (&accf)[NP][P], int32_t (&acci)[NP][P]) {
   float x[KB][NP][P];
 #pragma unroll
@@ -798,7 +799,7 @@ __device__ __forceinline__ void fused_batch(const FusedArgs &a, int k0, int kn,
           accf[j][e] += copysignf(m, xv);
           if constexpr (STORE) c[e] = uniform_code(m, xv, a.bits);
         } else {
-          const uint32_t jj = quant_exp_index(xv, q.inv, a.levels, two_em1, h);
+          const uint32_t jj = quant_exp_index(xv, q.inv, a.levels, lo_scale, h);
           acci[j][e] += exp_lin(jj, xv < 0.0f);
           if constexpr (STORE) c[e] = exp_code(jj, xv, a.bits);
         }
@@ -822,7 +823,7 @@ void k_fused(FusedArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int K = KT > 0 ? KT : a.K;
   const float sf = (float)a.levels;
-  const float two_em1 = ldexpf(1.0f, a.levels - 1);
+  const float lo_scale = ldexpf(1.0f, a.levels + 31);
   for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
     int64_t begin;
     int len, seg;
@@ -854,13 +855,13 @@ void k_fused(FusedArgs a) {
         if constexpr (KT > 0) {
 #pragma unroll 1
           for (int k0 = 0; k0 < KT; k0 += KB)
-            fused_batch<DT, GRID, P, NP, KB, STORE>(a, k0, KB, e0, cnt, am, q, sf, two_em1,
+            fused_batch<DT, GRID, P, NP, KB, STORE>(a, k0, KB, e0, cnt, am, q, sf, lo_scale,
                                                     accf, acci);
         } else {
 #pragma unroll 1
           for (int k0 = 0; k0 < K; k0 += KB)
             fused_batch<DT, GRID, P, NP, KB, STORE>(a, k0, min(KB, K - k0), e0, cnt, am, q,
-                                                    sf, two_em1, accf, acci);
+                                                    sf, lo_scale, accf, acci);
         }
       } else if (STORE) {
         const uint32_t z[P] = {};
@@ -996,7 +997,7 @@ template <int DT, int GRID, int P, int NP, int KB>
 __device__ __forceinline__ void worker_batch(const WorkerMeanArgs &a, int k0, int kn,
                                              float2 fl, const int64_t (&e0)[NP],
                                              const int (&cnt)[NP], const uint32_t (&am)[NP][P],
-                                             float sf, float two_em1, float (&acc)[NP][P]) {
+                                             float sf, float lo_scale, float (&acc)[NP][P]) {
   float x[KB][NP][P];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
@@ -1022,7 +1023,7 @@ __device__ __forceinline__ void worker_batch(const WorkerMeanArgs &a, int k0, in
         if constexpr (GRID == 0)
           l = copysignf(quant_uniform_mag(xv, inv, sf, h), xv);
         else
-          l = (float)exp_lin(quant_exp_index(xv, inv, a.levels, two_em1, h), xv < 0.0f);
+          l = (float)exp_lin(quant_exp_index(xv, inv, a.levels, lo_scale, h), xv < 0.0f);
         acc[j][e] = fmaf(l, fac, acc[j][e]);  // one rounding per worker, in worker order
       }
   }
@@ -1040,7 +1041,7 @@ void k_worker_mean(WorkerMeanArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int K = KT > 0 ? KT : a.K;
   const float sf = (float)a.levels;
-  const float two_em1 = ldexpf(1.0f, a.levels - 1);
+  const float lo_scale = ldexpf(1.0f, a.levels + 31);
   for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
     int64_t begin;
     int len, seg;
@@ -1067,7 +1068,7 @@ void k_worker_mean(WorkerMeanArgs a) {
       }
 #pragma unroll 1
       for (int k0 = 0; k0 < K; k0 += KB)
-        worker_batch<DT, GRID, P, NP, KB>(a, k0, min(KB, K - k0), fl, e0, cnt, am, sf, two_em1,
+        worker_batch<DT, GRID, P, NP, KB>(a, k0, min(KB, K - k0), fl, e0, cnt, am, sf, lo_scale,
                                           acc);
 #pragma unroll
       for (int j = 0; j < NP; ++j)
