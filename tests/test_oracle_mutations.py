@@ -39,6 +39,10 @@ MUTATIONS = [
      "m = (int32_t)l + (r <= p ? 1 : 0);"),
     ("uniform: nearest level, not floor", "l = floor((double)u);", "l = floor((double)u + 0.5);"),
     ("uniform: sign dropped", "return signbit(x) ? -m : m;", "return m;"),
+    ("uniform: a NaN counted as positive", "return signbit(x) ? -m : m;",
+     "return x < 0.0f ? -m : m;"),
+    ("exponential: a NaN's sign bit kept", "return (x < 0.0f && j > 0) ? -j : j;",
+     "return (signbit(x) && j > 0) ? -j : j;"),
     ("uniform: counter without index base", "scale[g], key, index_base + (uint32_t)i);",
      "scale[g], key, (uint32_t)i);"),
     ("exponential: probability over the upper level", "p = ((double)u - lo) / (hi - lo);",
