@@ -373,7 +373,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the K data-parallel workers are simulated as K buffers "
-              "on it, and runs on more than one GPU are not part of this build (asked for %d)"
+              "on it; runs on more than one GPU are not supported (asked for %d)"
               % max(args.gpus, int(os.environ.get("WORLD_SIZE", "1"))), file=sys.stderr)
         sys.exit(2)
 
