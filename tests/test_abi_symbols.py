@@ -81,3 +81,21 @@ def test_wire_lane_width_rule_matches_the_oracle():
                 assert lib.gq_wire_lane_bytes(grid, levels, world) == \
                     oracle.wire_lane_bytes(grid, levels, world), (grid, levels, world)
     assert lib.gq_wire_lane_bytes(0, 128, 1) == 0 and lib.gq_wire_lane_bytes(0, 7, 0) == 0
+
+
+def test_header_is_plain_c99():
+    """include/gq.h and a C program using it compile as C99 with gcc (no C++ or HIP types in
+    the ABI), and the header alone also compiles with -pedantic."""
+    import subprocess
+    import tempfile
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    inc = os.path.join(ROOT, "include")
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
+                           "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(rocm, "include"),
+                           "-I" + inc, os.path.join(ROOT, "tests", "abi", "c_consumer.c")])
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "only_header.c")
+        with open(src, "w") as f:
+            f.write('#include "gq.h"\nint main(void) { return GQ_OK; }\n')
+        subprocess.check_call(["gcc", "-std=c99", "-pedantic", "-Wall", "-Werror",
+                               "-fsyntax-only", "-I" + inc, src])
