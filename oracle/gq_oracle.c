@@ -615,18 +615,17 @@ void orc_mgs(float *P, int64_t n, int32_t r)
     free(V);
 }
 
-/* [LQ] "What carries the argument": G ~ P Q^T with error feedback E_t = G'_t - Ghat_t;
- * "Core claim": Q warm-started from the previous iteration.  One worker, one power step. */
-void orc_powersgd_logquant(const float *G, float *E, float *Q, int64_t n, int64_t m,
-                           int32_t r, double alpha, int32_t bits_p, int32_t bits_q,
-                           int8_t *p_codes,
-                           float *p_colmax, int8_t *q_codes, float *q_colmax, float *p_hat,
-                           float *P_pre, float *Q_pre)
+/* [LQ] "Core claim": one worker's compressor.  M = G + E is left in E; P = M Q_prev is
+ * orthonormalised; Q' = M^T P; both factors are log-quantised (codes and maxima are the
+ * worker's message, Ph and Qh their decoded values); Q <- Qh is the warm start of the next
+ * step ("Q is warm-started from the previous iteration"). */
+static void lq_compress(const float *G, float *E, float *Q, int64_t n, int64_t m, int32_t r,
+                        double alpha, int32_t bits_p, int32_t bits_q, int8_t *p_codes,
+                        float *p_colmax, int8_t *q_codes, float *q_colmax, float *Ph, float *Qh,
+                        float *P_pre, float *Q_pre)
 {
     float *P = (float *)malloc((size_t)(n * r) * sizeof(float));
     float *Qn = (float *)malloc((size_t)(m * r) * sizeof(float));
-    float *Ph = (float *)malloc((size_t)(n * r) * sizeof(float));
-    float *Qh = (float *)malloc((size_t)(m * r) * sizeof(float));
     double *Qacc = (double *)malloc((size_t)(m * r) * sizeof(double));
     int64_t i, j;
     int32_t c;
@@ -662,7 +661,27 @@ void orc_powersgd_logquant(const float *G, float *E, float *Q, int64_t n, int64_
 
     orc_logquant(P, n, r, alpha, bits_p, p_codes, p_colmax, Ph);
     orc_logquant(Qn, m, r, alpha, bits_q, q_codes, q_colmax, Qh);
+    memcpy(Q, Qh, (size_t)(m * r) * sizeof(float));
+    free(P);
+    free(Qn);
+    free(Qacc);
+}
 
+/* [LQ] "What carries the argument": G ~ P Q^T with error feedback E_t = G'_t - Ghat_t.
+ * One worker, one power step: the compressor above, then E = M - Phat Qhat^T. */
+void orc_powersgd_logquant(const float *G, float *E, float *Q, int64_t n, int64_t m,
+                           int32_t r, double alpha, int32_t bits_p, int32_t bits_q,
+                           int8_t *p_codes,
+                           float *p_colmax, int8_t *q_codes, float *q_colmax, float *p_hat,
+                           float *P_pre, float *Q_pre)
+{
+    float *Ph = (float *)malloc((size_t)(n * r) * sizeof(float));
+    float *Qh = (float *)malloc((size_t)(m * r) * sizeof(float));
+    int64_t i, j;
+    int32_t c;
+
+    lq_compress(G, E, Q, n, m, r, alpha, bits_p, bits_q, p_codes, p_colmax, q_codes, q_colmax,
+                Ph, Qh, P_pre, Q_pre);
     /* E = M - Phat Qhat^T (fp64 products, one rounding) */
     for (i = 0; i < n; ++i)
         for (j = 0; j < m; ++j) {
@@ -671,12 +690,49 @@ void orc_powersgd_logquant(const float *G, float *E, float *Q, int64_t n, int64_
                 acc += (double)Ph[i * r + c] * (double)Qh[j * r + c];
             E[i * m + j] = (float)((double)E[i * m + j] - acc);
         }
-    memcpy(Q, Qh, (size_t)(m * r) * sizeof(float));
     if (p_hat)
         memcpy(p_hat, Ph, (size_t)(n * r) * sizeof(float));
-    free(P);
-    free(Qn);
     free(Ph);
     free(Qh);
-    free(Qacc);
+}
+
+/* [LQ] K workers, one step each.  Every worker runs the compressor above on its own
+ * M_w = G_w + E_w from its own warm start Q_w; the messages (codes and column maxima) are
+ * exchanged whole, since log codes cannot be summed.  Every worker then forms the same
+ * approximate global gradient (referee minor comment on Section III-A: Ghat_t stands for the
+ * global gradient) as the mean of the decoded messages,
+ *   Ghat = (1/K) sum_w Phat_w Qhat_w^T     (fp64 sum over w, then c; one rounding to fp32),
+ * and feeds back E_w = M_w - Ghat ("What carries the argument"), taken against the unrounded
+ * mean and rounded once, so that K = 1 is the single-worker step exactly.
+ * Codes and maxima are stacked by worker: p_codes K x n x r, p_colmax K x r, q_codes
+ * K x m x r, q_colmax K x r.  G_hat n x m. */
+void orc_lq_step_workers(const float *const *G, float *const *E, float *const *Q, int32_t K,
+                         int64_t n, int64_t m, int32_t r, double alpha, int32_t bits_p,
+                         int32_t bits_q, int8_t *p_codes, float *p_colmax, int8_t *q_codes,
+                         float *q_colmax, float *G_hat)
+{
+    float *Ph = (float *)malloc((size_t)K * (size_t)(n * r) * sizeof(float));
+    float *Qh = (float *)malloc((size_t)K * (size_t)(m * r) * sizeof(float));
+    int64_t i, j;
+    int32_t c, w;
+
+    for (w = 0; w < K; ++w)
+        lq_compress(G[w], E[w], Q[w], n, m, r, alpha, bits_p, bits_q, p_codes + w * n * r,
+                    p_colmax + w * r, q_codes + w * m * r, q_colmax + w * r, Ph + w * n * r,
+                    Qh + w * m * r, NULL, NULL);
+    for (i = 0; i < n; ++i)
+        for (j = 0; j < m; ++j) {
+            double acc = 0.0, mean;
+            for (w = 0; w < K; ++w) {
+                const float *pw = Ph + w * n * r, *qw = Qh + w * m * r;
+                for (c = 0; c < r; ++c)
+                    acc += (double)pw[i * r + c] * (double)qw[j * r + c];
+            }
+            mean = acc / (double)K;
+            G_hat[i * m + j] = (float)mean;
+            for (w = 0; w < K; ++w)
+                E[w][i * m + j] = (float)((double)E[w][i * m + j] - mean);
+        }
+    free(Ph);
+    free(Qh);
 }

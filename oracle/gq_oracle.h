@@ -19,7 +19,8 @@
  *          LQ-SGD Algorithm": "Core claim" (Eq. 5 log quantizer, 2^b bins, warm start),
  *          "What carries the argument" (G ~ P Q^T, error feedback E_t = G'_t - Ghat_t),
  *          referee major comment 1 (normalise by the maximum magnitude; Eq. 6 inverse;
- *          Q_t computed from the orthonormalised P_t).
+ *          Q_t computed from the orthonormalised P_t); referee minor comment on
+ *          Section III-A (Ghat_t is the approximate global gradient).
  *
  * Parity status of each function is given beside it; "parity unpinned" marks the parts
  * that only a second implementation of the same definition can check.
@@ -171,6 +172,14 @@ void orc_powersgd_logquant(const float *G, float *E, float *Q, int64_t n, int64_
                            int8_t *p_codes,
                            float *p_colmax, int8_t *q_codes, float *q_colmax, float *p_hat,
                            float *P_pre, float *Q_pre);
+/* K workers (1 <= K): each compresses its own M_w = G_w + E_w from its own warm start Q_w as
+ * above; Ghat = fp32((1/K) sum_w Phat_w Qhat_w^T) (fp64 sums); E_w <- fp32(M_w - that mean);
+ * Q_w <- Qhat_w.  Messages stacked by worker: p_codes K x n x r, p_colmax K x r,
+ * q_codes K x m x r, q_colmax K x r.  G_hat n x m. */
+void orc_lq_step_workers(const float *const *G, float *const *E, float *const *Q, int32_t K,
+                         int64_t n, int64_t m, int32_t r, double alpha, int32_t bits_p,
+                         int32_t bits_q, int8_t *p_codes, float *p_colmax, int8_t *q_codes,
+                         float *q_colmax, float *G_hat);
 
 #ifdef __cplusplus
 }

@@ -90,6 +90,8 @@ def lib():
             "orc_mgs": (None, [p, i64, i32]),
             "orc_powersgd_logquant": (None, [p, p, p, i64, i64, i32, d, i32, i32, p, p, p, p, p,
                                              p, p]),
+            "orc_lq_step_workers": (None, [p, p, p, i32, i64, i64, i32, d, i32, i32, p, p, p, p,
+                                           p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -375,3 +377,23 @@ def powersgd_logquant(G, E, Q, alpha, bits, bits_q=None):
                                 _ptr(pm), _ptr(qc), _ptr(qm), _ptr(ph), _ptr(ppre), _ptr(qpre))
     return dict(E=E, Q=Q, p_codes=pc, p_colmax=pm, q_codes=qc, q_colmax=qm, p_hat=ph,
                 P_pre=ppre, Q_pre=qpre)
+
+
+def lq_step_workers(Gs, Es, Qs, alpha, bits, bits_q=None):
+    """One step of K workers (lists of n x m gradients and errors, m x r warm starts).  Returns
+    a dict with the updated E and Q lists (new arrays), the stacked messages and G_hat."""
+    K = len(Gs)
+    Gs = [_c(G, np.float32) for G in Gs]
+    Es = [np.array(E, dtype=np.float32, order="C", copy=True) for E in Es]
+    Qs = [np.array(Q, dtype=np.float32, order="C", copy=True) for Q in Qs]
+    n, m = Gs[0].shape
+    r = Qs[0].shape[1]
+    pc = np.empty((K, n, r), np.int8)
+    qc = np.empty((K, m, r), np.int8)
+    pm = np.empty((K, r), np.float32)
+    qm = np.empty((K, r), np.float32)
+    gh = np.empty((n, m), np.float32)
+    lib().orc_lq_step_workers(_ptrs(Gs), _ptrs(Es), _ptrs(Qs), K, n, m, r, alpha, bits,
+                              bits if bits_q is None else bits_q, _ptr(pc), _ptr(pm), _ptr(qc),
+                              _ptr(qm), _ptr(gh))
+    return dict(E=Es, Q=Qs, p_codes=pc, p_colmax=pm, q_codes=qc, q_colmax=qm, G_hat=gh)

@@ -18,7 +18,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "gq_oracle.c")
 PIN_SUITES = ["tests/test_oracle_rng.py", "tests/test_oracle_quant.py", "tests/test_oracle_lq.py",
-              "tests/test_oracle_wire.py", "tests/test_oracle_baselines.py"]
+              "tests/test_oracle_wire.py", "tests/test_oracle_baselines.py",
+              "tests/test_oracle_lq_workers.py"]
 
 # (name, text in gq_oracle.c, replacement)
 MUTATIONS = [
@@ -112,6 +113,22 @@ MUTATIONS = [
      "int32_t q = orc_unpack_one(codes[0], i, grid, bits);"),
     ("worker mean: last worker left out", "            for (k = 0; k < K; ++k) {\n                float S",
      "            for (k = 0; k + 1 < K; ++k) {\n                float S"),
+    ("LQ workers: the sum of the messages, not their mean", "mean = acc / (double)K;",
+     "mean = acc;"),
+    ("LQ workers: last worker left out of the mean",
+     "            for (w = 0; w < K; ++w) {\n                const float *pw",
+     "            for (w = 0; w + 1 < K; ++w) {\n                const float *pw"),
+    ("LQ workers: worker 0's Q factor in every product", "*qw = Qh + w * m * r;", "*qw = Qh;"),
+    ("LQ workers: error against the sum, not the mean",
+     "E[w][i * m + j] = (float)((double)E[w][i * m + j] - mean);",
+     "E[w][i * m + j] = (float)((double)E[w][i * m + j] - acc);"),
+    ("LQ workers: error against the rounded mean",
+     "E[w][i * m + j] = (float)((double)E[w][i * m + j] - mean);",
+     "E[w][i * m + j] = E[w][i * m + j] - G_hat[i * m + j];"),
+    ("LQ workers: worker 0's warm start for every worker", "lq_compress(G[w], E[w], Q[w],",
+     "lq_compress(G[w], E[w], Q[0],"),
+    ("LQ workers: worker 0's gradient for every worker", "lq_compress(G[w], E[w], Q[w],",
+     "lq_compress(G[0], E[w], Q[w],"),
 ]
 
 
