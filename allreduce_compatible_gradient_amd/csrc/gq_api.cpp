@@ -635,7 +635,8 @@ GQ_EXPORT gq_status gq_powersgd_logquant(gq_ctx *c, const float *G, float *E, fl
   if (!c) return GQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (n < 1 || m < 1) return fail(c, GQ_EINVAL, "n = %lld, m = %lld must be >= 1", (long long)n, (long long)m);
-  if (n > (1ll << 30) || m > (1ll << 30)) return fail(c, GQ_EINVAL, "n or m too large");
+  if (n > gq::kLqMaxRows) return fail(c, GQ_EINVAL, "n = %lld above %lld rows", (long long)n, (long long)gq::kLqMaxRows);
+  if (m > (1ll << 30)) return fail(c, GQ_EINVAL, "m too large");
   if (r < 1 || r > gq::kLqMaxRank) return fail(c, GQ_EINVAL, "r = %d outside [1, %d]", r, gq::kLqMaxRank);
   if (!(alpha > 0.0) || !std::isfinite(alpha)) return fail(c, GQ_EINVAL, "alpha must be positive and finite");
   if (bits_p < 2 || bits_p > 8) return fail(c, GQ_EINVAL, "bits_p = %d outside [2, 8]", bits_p);
@@ -655,4 +656,58 @@ GQ_EXPORT gq_status gq_powersgd_logquant(gq_ctx *c, const float *G, float *E, fl
   hipError_t e = gq::lq_step(c->lq, a, s);
   if (e == hipErrorOutOfMemory) return fail(c, GQ_ENOMEM, "LQ scratch allocation failed");
   return e == hipSuccess ? GQ_OK : hip_fail(c, e, "powersgd_logquant launch");
+}
+
+GQ_EXPORT gq_status gq_lq_step_workers(gq_ctx *c, const float *const *G, float *const *E,
+                                       float *const *Q, int32_t K, int64_t n, int64_t m, int32_t r,
+                                       double alpha, int32_t bits_p, int32_t bits_q,
+                                       int8_t *p_codes, float *p_colmax, int8_t *q_codes,
+                                       float *q_colmax, float *G_hat, void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K < 1 || K > gq::kLqMaxWorkers) return fail(c, GQ_EINVAL, "K = %d outside [1, %d]", K, gq::kLqMaxWorkers);
+  if (!G || !E || !Q) return fail(c, GQ_EINVAL, "G, E and Q must be arrays of K pointers");
+  if (n < 1 || m < 1) return fail(c, GQ_EINVAL, "n = %lld, m = %lld must be >= 1", (long long)n, (long long)m);
+  if (n > gq::kLqMaxRows) return fail(c, GQ_EINVAL, "n = %lld above %lld rows", (long long)n, (long long)gq::kLqMaxRows);
+  if (m > (1ll << 30)) return fail(c, GQ_EINVAL, "m too large");
+  if (r < 1 || r > gq::kLqMaxRank) return fail(c, GQ_EINVAL, "r = %d outside [1, %d]", r, gq::kLqMaxRank);
+  if (!(alpha > 0.0) || !std::isfinite(alpha)) return fail(c, GQ_EINVAL, "alpha must be positive and finite");
+  if (bits_p < 2 || bits_p > 8) return fail(c, GQ_EINVAL, "bits_p = %d outside [2, 8]", bits_p);
+  if (bits_q < 2 || bits_q > 8) return fail(c, GQ_EINVAL, "bits_q = %d outside [2, 8]", bits_q);
+  for (int k = 0; k < K; ++k) {
+    TRY(check_ptr(c, G[k], "G[k]"));
+    TRY(check_ptr(c, E[k], "E[k]"));
+    TRY(check_ptr(c, Q[k], "Q[k]"));
+    if (E[k] == G_hat) return fail(c, GQ_EINVAL, "G_hat is E[%d]", k);
+    for (int l = 0; l < k; ++l)
+      if (E[l] == E[k] || Q[l] == Q[k])
+        return fail(c, GQ_EINVAL, "workers %d and %d share an E or a Q buffer", l, k);
+  }
+  TRY(check_ptr(c, p_codes, "p_codes"));
+  TRY(check_ptr(c, p_colmax, "p_colmax"));
+  TRY(check_ptr(c, q_codes, "q_codes"));
+  TRY(check_ptr(c, q_colmax, "q_colmax"));
+  TRY(check_ptr(c, G_hat, "G_hat"));
+  gq::LqWorkersStepArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int k = 0; k < K; ++k) {
+    a.W.G[k] = G[k];
+    a.W.E[k] = E[k];
+    a.W.Q[k] = Q[k];
+  }
+  a.K = K;
+  a.n = n;
+  a.m = m;
+  a.r = r;
+  a.alpha = alpha;
+  a.bits_p = bits_p;
+  a.bits_q = bits_q;
+  a.p_codes = p_codes;
+  a.p_colmax = p_colmax;
+  a.q_codes = q_codes;
+  a.q_colmax = q_colmax;
+  a.G_hat = G_hat;
+  hipError_t e = gq::lq_step_workers(c->lq, a, s);
+  if (e == hipErrorOutOfMemory) return fail(c, GQ_ENOMEM, "LQ scratch allocation failed");
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "lq_step_workers launch");
 }

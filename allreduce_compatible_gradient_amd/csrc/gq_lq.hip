@@ -1,4 +1,4 @@
-// gq_lq.hip -- gfx950 kernels of one LQ-SGD compressor step (one worker).
+// gq_lq.hip -- gfx950 kernels of one LQ-SGD compressor step, for one worker or for K workers.
 //
 // Method (review of "Trustworthy Efficient Communication for Distributed Learning using LQ-SGD
 // Algorithm"): PowerSGD's factorisation G ~ P Q^T with error feedback E_t = G'_t - Ghat_t
@@ -12,6 +12,12 @@
 //   pass 1  E <- G + E and P = E Q              (read G, E; write E)   k_lq_ef_mq
 //   pass 2  Q' = E^T Pt                         (read E)               k_lq_mtp + k_lq_qsum
 //   pass 3  E <- E - Phat Q'hat^T               (read E; write E)      k_lq_ef_update
+// With K workers (each its own G, E and warm start Q; the review's "Core claim" compresses each
+// worker's factors before the exchange) every per-worker kernel runs all K in one launch, the
+// worker taken from a grid dimension, and the last pass becomes k_lq_mean_ef: the mean of the
+// K decoded messages, Ghat = (1/K) sum_w Phat_w Qhat_w^T (the approximate global gradient of
+// the referee's comment on Section III-A), written once, and E_w <- M_w - Ghat for each worker
+// (read K E's; write K E's and Ghat).
 // Cache use: G and the incoming E are streamed once (non-temporal loads); the passes over M
 // read it with ordinary loads, so what the column pass brings in can still be cached when the
 // last pass reads it again.
@@ -155,14 +161,19 @@ __device__ __forceinline__ void tri_index(int t, int &a, int &b) {
 // Pass 1: E <- G + E (the gradient with the previous error fed back), P = E Q, and the block's
 // share of the Gram matrix P^T P (packed upper triangle, fp64, stored entry-major so that the
 // solve reads each entry's partials contiguously).
+// Worker blockIdx.y of the step: its own G, E and Q; its slices of the stacked P and partials.
 template <int RANK, int VEC>
-__global__ __launch_bounds__(kBlockA) void k_lq_ef_mq(const float *__restrict__ G,
-                                                      float *__restrict__ E,
-                                                      const float *__restrict__ Q,
-                                                      float *__restrict__ P,
-                                                      double *__restrict__ gpart, int64_t n,
+__global__ __launch_bounds__(kBlockA) void k_lq_ef_mq(const LqWorkerPtrs W,
+                                                      float *__restrict__ P_all,
+                                                      double *__restrict__ gpart_all, int64_t n,
                                                       int64_t m) {
   constexpr int NG = RANK * (RANK + 1) / 2;
+  const int wk = blockIdx.y;
+  const float *__restrict__ G = W.G[wk];
+  float *__restrict__ E = W.E[wk];
+  const float *__restrict__ Q = W.Q[wk];
+  float *__restrict__ P = P_all + (int64_t)wk * n * RANK;
+  double *__restrict__ gpart = gpart_all + (int64_t)wk * NG * gridDim.x;
   __shared__ float red[kBlockA / 64][kRowsA * RANK];
   __shared__ float pv[kRowsA * RANK];
   const int64_t row0 = (int64_t)blockIdx.x * kRowsA;
@@ -291,12 +302,17 @@ __device__ __forceinline__ void lane_cholqr_T(const double (&g)[RANK], int j,
 
 // Orthonormalise P (r x r part): fixed-order sum of the block Gram partials, then two
 // Cholesky-QR rounds in r x r space (lane-parallel in one wave) giving T = T1 T2.
+// One block per worker (blockIdx.x).
 template <int RANK>
-__global__ __launch_bounds__(solve_block<RANK>()) void k_lq_solve(const double *__restrict__ gpart,
+__global__ __launch_bounds__(solve_block<RANK>()) void k_lq_solve(const double *__restrict__ gpart_all,
                                                           int64_t nblocks,
-                                                          double *__restrict__ Tout,
-                                                          unsigned *__restrict__ cmax_bits) {
+                                                          double *__restrict__ T_all,
+                                                          unsigned *__restrict__ cmax_all) {
   constexpr int NG = RANK * (RANK + 1) / 2;
+  const int wk = blockIdx.x;
+  const double *__restrict__ gpart = gpart_all + (int64_t)wk * NG * nblocks;
+  double *__restrict__ Tout = T_all + wk * RANK * RANK;
+  unsigned *__restrict__ cmax_bits = cmax_all + wk * 2 * RANK;
   __shared__ double Gs[RANK][RANK];
   __shared__ double T1s[RANK][RANK], T2s[RANK][RANK];  // rows of T1 and of T2
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -399,15 +415,25 @@ __global__ __launch_bounds__(solve_block<RANK>()) void k_lq_solve(const double *
 // is the exact, order-independent maximum.  Wave w takes rows w, w + 8, ... of the chunk, in
 // batches of loads issued together; waves 4..7 hand their sums to waves 0..3 through LDS, and
 // the four pair sums are added in wave order and written as contiguous (j, c) runs.
+// Worker blockIdx.z: M is its E; P, T, Pt, p_pre (if any), the maxima and the partials are
+// its slices of the stacked buffers.
 template <int RANK, int VEC, int ROWSC>
-__global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict__ M,
-                                                         const float *__restrict__ P,
-                                                         const double *__restrict__ T,
-                                                         float *__restrict__ Pt,
-                                                         float *__restrict__ p_pre,
-                                                         unsigned *__restrict__ cmax_bits,
-                                                         float *__restrict__ part, int64_t n,
+__global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const LqWorkerPtrs W,
+                                                         const float *__restrict__ P_all,
+                                                         const double *__restrict__ T_all,
+                                                         float *__restrict__ Pt_all,
+                                                         float *__restrict__ p_pre_all,
+                                                         unsigned *__restrict__ cmax_all,
+                                                         float *__restrict__ part_all, int64_t n,
                                                          int64_t m) {
+  const int wk = blockIdx.z;
+  const float *__restrict__ M = W.E[wk];
+  const float *__restrict__ P = P_all + (int64_t)wk * n * RANK;
+  const double *__restrict__ T = T_all + wk * RANK * RANK;
+  float *__restrict__ Pt = Pt_all + (int64_t)wk * n * RANK;
+  float *__restrict__ p_pre = p_pre_all ? p_pre_all + (int64_t)wk * n * RANK : nullptr;
+  unsigned *__restrict__ cmax_bits = cmax_all + wk * 2 * RANK;
+  float *__restrict__ part = part_all + (int64_t)wk * gridDim.y * m * RANK;
   constexpr int RW = ROWSC / kWavesC;   // rows per wave
   // rows per load batch: all of them at low rank; 4 above, which with the half-size LDS
   // reduction below lets a CU hold more blocks at once
@@ -527,12 +553,20 @@ __global__ __launch_bounds__(kWavesC * 64) void k_lq_mtp(const float *__restrict
 // maxima once (r global atomics per block).
 constexpr int kQsumShort = 8192;
 
+// Worker blockIdx.y: its slices of the partials, of Q', of q_pre (if any) and of the maxima
+// (cmax_all holds 2 RANK words per worker; Q' takes the second RANK).
 template <int RANK, int G>
-__global__ __launch_bounds__(256) void k_lq_qsum(const float *__restrict__ part,
-                                                 float *__restrict__ Qn, float *__restrict__ q_pre,
-                                                 unsigned *__restrict__ cmax_bits, int64_t count,
+__global__ __launch_bounds__(256) void k_lq_qsum(const float *__restrict__ part_all,
+                                                 float *__restrict__ Qn_all,
+                                                 float *__restrict__ q_pre_all,
+                                                 unsigned *__restrict__ cmax_all, int64_t count,
                                                  int nchunks) {
   constexpr int OUT = 256 / G, NB = 32 / G > 8 ? 32 / G : 8;  // outputs per block, loads per batch
+  const int wk = blockIdx.y;
+  const float *__restrict__ part = part_all + (int64_t)wk * nchunks * count;
+  float *__restrict__ Qn = Qn_all + (int64_t)wk * count;
+  float *__restrict__ q_pre = q_pre_all ? q_pre_all + (int64_t)wk * count : nullptr;
+  unsigned *__restrict__ cmax_bits = cmax_all + wk * 2 * RANK + RANK;
   __shared__ float ps[G][OUT];
   __shared__ unsigned smax[RANK];
   const int il = threadIdx.x % OUT, g = threadIdx.x / OUT;
@@ -639,14 +673,32 @@ struct ElemJob {
   int8_t *p_codes, *q_codes;
   float *p_colmax, *q_colmax;
   float *Ph, *p_hat;     // decoded P (scratch) and the optional output copy
-  float *Qh;             // decoded Q (written into Q)
+  float *Qh;             // decoded Q (written into the worker's Q)
 };
 
-__global__ __launch_bounds__(256) void k_lq_quant_elems(ElemJob J, const float *tab_p, int Lp,
+// Worker blockIdx.y: every pointer of J0 is the base of a buffer stacked by worker (p_hat may
+// be null); the decoded Q goes into the worker's own Q.
+__global__ __launch_bounds__(256) void k_lq_quant_elems(const ElemJob J0, const LqWorkerPtrs W,
+                                                        const float *tab_p, int Lp,
                                                         const float *tab_q, int Lq) {
   __shared__ float thr[2][128];
   __shared__ float lvl[2][128];
   const int tid = threadIdx.x;
+  const int wk = blockIdx.y;
+  ElemJob J = J0;
+  {
+    const int64_t pn = J0.n * J0.r, qm = J0.m * J0.r;
+    J.Pt += wk * pn;
+    J.Qn += wk * qm;
+    J.cmax_bits += wk * 2 * J0.r;
+    J.p_codes += wk * pn;
+    J.q_codes += wk * qm;
+    J.p_colmax += wk * J0.r;
+    J.q_colmax += wk * J0.r;
+    J.Ph += wk * pn;
+    if (J0.p_hat) J.p_hat += wk * pn;
+    J.Qh = W.Q[wk];
+  }
   const int64_t np = J.n * J.r, nq = J.m * J.r;
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + tid;
   // the element and its column maximum are fetched while the tables are staged
@@ -729,6 +781,84 @@ __global__ __launch_bounds__(kBlockA) void k_lq_ef_update(float *__restrict__ E,
   }
 }
 
+// Last pass of a step of K workers: the approximate global gradient
+// Ghat = (1/K) sum_w Phat_w Qhat_w^T for 4 rows at a time (sums over workers, then columns of
+// the factors, by fused multiply-add), stored once, and E_w <- M_w - Ghat for every worker
+// (E_w holds M_w).  The 4 rows' decoded P entries of every worker are staged in LDS (at most
+// 16 x 4 x 8 floats); each worker's decoded Q rows are read from its own Q (m x r, L2-resident).
+// Two workers' rows are loaded before either is stored.  At K = 1 this is k_lq_ef_update with
+// Ghat also stored.
+template <int RANK, int VEC>
+__global__ __launch_bounds__(kBlockA) void k_lq_mean_ef(const LqWorkerPtrs W, int K,
+                                                        const float *__restrict__ Ph_all,
+                                                        float *__restrict__ Ghat, float invK,
+                                                        int64_t n, int64_t m) {
+  __shared__ float ps[kLqMaxWorkers * kRowsA * RANK];
+  const int64_t row0 = (int64_t)blockIdx.x * kRowsA;
+  const int nr = n - row0 < kRowsA ? (int)(n - row0) : kRowsA;
+  for (int t = threadIdx.x; t < K * kRowsA * RANK; t += kBlockA) {
+    const int wk = t / (kRowsA * RANK), rr = (t / RANK) % kRowsA, c = t % RANK;
+    ps[t] = rr < nr ? Ph_all[((int64_t)wk * n + row0 + rr) * RANK + c] : 0.0f;
+  }
+  __syncthreads();
+  for (int64_t j = (int64_t)threadIdx.x * VEC; j < m; j += (int64_t)kBlockA * VEC) {
+    float g[kRowsA][VEC];
+#pragma unroll
+    for (int rr = 0; rr < kRowsA; ++rr)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) g[rr][v] = 0.0f;
+#pragma unroll 1
+    for (int wk = 0; wk < K; ++wk) {
+      float q[RANK][VEC];
+      load_q_rows<RANK, VEC>(W.Q[wk], j, q);
+#pragma unroll
+      for (int rr = 0; rr < kRowsA; ++rr) {
+        float p[RANK];
+#pragma unroll
+        for (int c = 0; c < RANK; ++c) p[c] = ps[(wk * kRowsA + rr) * RANK + c];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+#pragma unroll
+          for (int c = 0; c < RANK; ++c) g[rr][v] = fmaf(p[c], q[c][v], g[rr][v]);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < kRowsA; ++rr)
+      if (rr < nr) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) g[rr][v] *= invK;
+        stv<VEC>(Ghat + (row0 + rr) * m + j, g[rr]);
+      }
+#pragma unroll 1
+    for (int wk = 0; wk < K; wk += 2) {
+      const bool two = wk + 1 < K;
+      float *E0 = W.E[wk];
+      float *E1 = two ? W.E[wk + 1] : E0;
+      float a[kRowsA][VEC], b[kRowsA][VEC];
+#pragma unroll
+      for (int rr = 0; rr < kRowsA; ++rr) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) b[rr][v] = 0.0f;
+        if (rr < nr) {
+          ldv<VEC>(E0 + (row0 + rr) * m + j, a[rr]);
+          if (two) ldv<VEC>(E1 + (row0 + rr) * m + j, b[rr]);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < kRowsA; ++rr)
+        if (rr < nr) {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            a[rr][v] -= g[rr][v];
+            b[rr][v] -= g[rr][v];
+          }
+          stv<VEC>(E0 + (row0 + rr) * m + j, a[rr]);
+          if (two) stv<VEC>(E1 + (row0 + rr) * m + j, b[rr]);
+        }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- host helpers
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -782,51 +912,70 @@ hipError_t tables(LqState &st, double alpha, int bits, hipStream_t s, const LqTa
   return hipSuccess;
 }
 
+// Scratch of a step, every buffer stacked by worker.
 struct StepBufs {
   float *P, *Pt, *part, *Qn, *Ph;
   double *gpart, *T;
-  unsigned *cmax_bits;
+  unsigned *cmax_bits;  // 2 RANK words per worker: Pt's column maxima, then Q''s
   int nchunks, rows_chunk;
   int64_t nblocks;
 };
 
+// One step of K workers (K = 1: the single-worker step).  Every per-worker kernel runs all
+// workers in one launch, the worker taken from a grid dimension.
+struct StepIO {
+  LqWorkerPtrs W;
+  int K;
+  int64_t n, m;
+  int8_t *p_codes, *q_codes;     // stacked by worker
+  float *p_colmax, *q_colmax;    // stacked by worker
+  float *p_hat, *p_pre, *q_pre;  // stacked by worker, or null
+  float *G_hat;                  // null: one worker, E <- M - Phat Qhat^T
+};
+
 template <int RANK, int VEC>
-void launch_step(const LqStepArgs &a, const StepBufs &b, const LqTables &tp, const LqTables &tq,
+void launch_step(const StepIO &io, const StepBufs &b, const LqTables &tp, const LqTables &tq,
                  hipStream_t s) {
-  const int64_t n = a.n, m = a.m;
-  hipLaunchKernelGGL((k_lq_ef_mq<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA), 0, s,
-                     a.G, a.E, a.Q, b.P, b.gpart, n, m);
-  hipLaunchKernelGGL((k_lq_solve<RANK>), dim3(1), dim3(solve_block<RANK>()), 0, s, b.gpart, b.nblocks,
-                     b.T, b.cmax_bits);
-  const dim3 gcol((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)b.nchunks);
+  const int64_t n = io.n, m = io.m;
+  const unsigned K = (unsigned)io.K;
+  hipLaunchKernelGGL((k_lq_ef_mq<RANK, VEC>), dim3((unsigned)b.nblocks, K), dim3(kBlockA), 0, s,
+                     io.W, b.P, b.gpart, n, m);
+  hipLaunchKernelGGL((k_lq_solve<RANK>), dim3(K), dim3(solve_block<RANK>()), 0, s, b.gpart,
+                     b.nblocks, b.T, b.cmax_bits);
+  const dim3 gcol((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)b.nchunks, K);
   if (b.rows_chunk == 64)
-    hipLaunchKernelGGL((k_lq_mtp<RANK, VEC, 64>), gcol, dim3(kWavesC * 64), 0, s, a.E, b.P, b.T,
-                       b.Pt, a.p_pre, b.cmax_bits, b.part, n, m);
+    hipLaunchKernelGGL((k_lq_mtp<RANK, VEC, 64>), gcol, dim3(kWavesC * 64), 0, s, io.W, b.P,
+                       b.T, b.Pt, io.p_pre, b.cmax_bits, b.part, n, m);
   else
-    hipLaunchKernelGGL((k_lq_mtp<RANK, VEC, 128>), gcol, dim3(kWavesC * 64), 0, s, a.E, b.P,
-                       b.T, b.Pt, a.p_pre, b.cmax_bits, b.part, n, m);
+    hipLaunchKernelGGL((k_lq_mtp<RANK, VEC, 128>), gcol, dim3(kWavesC * 64), 0, s, io.W, b.P,
+                       b.T, b.Pt, io.p_pre, b.cmax_bits, b.part, n, m);
   if (m * RANK <= kQsumShort)
-    hipLaunchKernelGGL((k_lq_qsum<RANK, 8>), dim3((unsigned)((m * RANK + 31) / 32)), dim3(256),
-                       0, s, b.part, b.Qn, a.q_pre, b.cmax_bits + RANK, m * RANK, b.nchunks);
-  else
-    hipLaunchKernelGGL((k_lq_qsum<RANK, 1>), dim3((unsigned)((m * RANK + 255) / 256)),
-                       dim3(256), 0, s, b.part, b.Qn, a.q_pre, b.cmax_bits + RANK, m * RANK,
+    hipLaunchKernelGGL((k_lq_qsum<RANK, 8>), dim3((unsigned)((m * RANK + 31) / 32), K),
+                       dim3(256), 0, s, b.part, b.Qn, io.q_pre, b.cmax_bits, m * RANK,
                        b.nchunks);
-  ElemJob je{b.Pt, b.Qn, n, m, RANK, b.cmax_bits, a.p_codes, a.q_codes, a.p_colmax, a.q_colmax,
-             b.Ph, a.p_hat, a.Q};
-  hipLaunchKernelGGL(k_lq_quant_elems, dim3((unsigned)(((n + m) * RANK + 255) / 256)),
-                     dim3(256), 0, s, je, tp.dev, tp.L, tq.dev, tq.L);
-  hipLaunchKernelGGL((k_lq_ef_update<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA), 0,
-                     s, a.E, b.Ph, a.Q, n, m);
+  else
+    hipLaunchKernelGGL((k_lq_qsum<RANK, 1>), dim3((unsigned)((m * RANK + 255) / 256), K),
+                       dim3(256), 0, s, b.part, b.Qn, io.q_pre, b.cmax_bits, m * RANK,
+                       b.nchunks);
+  ElemJob je{b.Pt, b.Qn, n, m, RANK, b.cmax_bits, io.p_codes, io.q_codes, io.p_colmax,
+             io.q_colmax, b.Ph, io.p_hat, nullptr};
+  hipLaunchKernelGGL(k_lq_quant_elems, dim3((unsigned)(((n + m) * RANK + 255) / 256), K),
+                     dim3(256), 0, s, je, io.W, tp.dev, tp.L, tq.dev, tq.L);
+  if (io.G_hat)
+    hipLaunchKernelGGL((k_lq_mean_ef<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA), 0,
+                       s, io.W, io.K, b.Ph, io.G_hat, 1.0f / (float)io.K, n, m);
+  else
+    hipLaunchKernelGGL((k_lq_ef_update<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA),
+                       0, s, io.W.E[0], b.Ph, io.W.Q[0], n, m);
 }
 
 template <int RANK>
-void launch_step_v(const LqStepArgs &a, bool vec4, const StepBufs &b, const LqTables &tp,
+void launch_step_v(const StepIO &io, bool vec4, const StepBufs &b, const LqTables &tp,
                    const LqTables &tq, hipStream_t s) {
   if (vec4)
-    launch_step<RANK, 4>(a, b, tp, tq, s);
+    launch_step<RANK, 4>(io, b, tp, tq, s);
   else
-    launch_step<RANK, 1>(a, b, tp, tq, s);
+    launch_step<RANK, 1>(io, b, tp, tq, s);
 }
 
 }  // namespace
@@ -841,29 +990,35 @@ hipError_t lq_logquant(LqState &st, const float *F, int64_t rows, int r, double 
   return hipGetLastError();
 }
 
-hipError_t lq_step(LqState &st, const LqStepArgs &a, hipStream_t s) {
+namespace {
+
+// Scratch for K workers, the launch shapes, and the launches.
+hipError_t run_step(LqState &st, const StepIO &io, int r, double alpha, int bits_p, int bits_q,
+                    hipStream_t s) {
   const LqTables *tp = nullptr, *tq = nullptr;
-  hipError_t e = tables(st, a.alpha, a.bits_p, s, &tp);
+  hipError_t e = tables(st, alpha, bits_p, s, &tp);
   if (e != hipSuccess) return e;
-  e = tables(st, a.alpha, a.bits_q, s, &tq);  // map insertion keeps tp valid
+  e = tables(st, alpha, bits_q, s, &tq);  // map insertion keeps tp valid
   if (e != hipSuccess) return e;
-  const int64_t n = a.n, m = a.m, r = a.r;
+  const int64_t n = io.n, m = io.m;
+  const size_t K = (size_t)io.K;
   StepBufs b;
   const bool vec4 = (m % 4) == 0;
   const int64_t col_tiles = vec4 ? (m + 255) / 256 : (m + 63) / 64;
-  b.rows_chunk = col_tiles * ((n + 127) / 128) < kColBlocksMin ? 64 : 128;
+  b.rows_chunk = col_tiles * ((n + 127) / 128) * (int64_t)K < kColBlocksMin ? 64 : 128;
   b.nchunks = (int)((n + b.rows_chunk - 1) / b.rows_chunk);
   b.nblocks = (n + kRowsA - 1) / kRowsA;
+  if (b.nchunks > 65535) return hipErrorInvalidValue;  // chunks are a grid dimension
   const int64_t ng = r * (r + 1) / 2;
   size_t off = 0;
-  const size_t oP = off; off += align256(sizeof(float) * n * r);
-  const size_t oG = off; off += align256(sizeof(double) * b.nblocks * ng);
-  const size_t oPt = off; off += align256(sizeof(float) * n * r);
-  const size_t oPart = off; off += align256(sizeof(float) * (size_t)b.nchunks * m * r);
-  const size_t oQn = off; off += align256(sizeof(float) * m * r);
-  const size_t oPh = off; off += align256(sizeof(float) * n * r);
-  const size_t oT = off; off += align256(sizeof(double) * r * r);
-  const size_t oC = off; off += align256(sizeof(unsigned) * 2 * r);
+  const size_t oP = off; off += align256(K * sizeof(float) * n * r);
+  const size_t oG = off; off += align256(K * sizeof(double) * b.nblocks * ng);
+  const size_t oPt = off; off += align256(K * sizeof(float) * n * r);
+  const size_t oPart = off; off += align256(K * sizeof(float) * (size_t)b.nchunks * m * r);
+  const size_t oQn = off; off += align256(K * sizeof(float) * m * r);
+  const size_t oPh = off; off += align256(K * sizeof(float) * n * r);
+  const size_t oT = off; off += align256(K * sizeof(double) * r * r);
+  const size_t oC = off; off += align256(K * sizeof(unsigned) * 2 * r);
   e = ensure(st, off, s);
   if (e != hipSuccess) return e;
   char *base = static_cast<char *>(st.scratch);
@@ -875,18 +1030,56 @@ hipError_t lq_step(LqState &st, const LqStepArgs &a, hipStream_t s) {
   b.Ph = reinterpret_cast<float *>(base + oPh);
   b.T = reinterpret_cast<double *>(base + oT);
   b.cmax_bits = reinterpret_cast<unsigned *>(base + oC);
-  switch (a.r) {
-    case 1: launch_step_v<1>(a, vec4, b, *tp, *tq, s); break;
-    case 2: launch_step_v<2>(a, vec4, b, *tp, *tq, s); break;
-    case 3: launch_step_v<3>(a, vec4, b, *tp, *tq, s); break;
-    case 4: launch_step_v<4>(a, vec4, b, *tp, *tq, s); break;
-    case 5: launch_step_v<5>(a, vec4, b, *tp, *tq, s); break;
-    case 6: launch_step_v<6>(a, vec4, b, *tp, *tq, s); break;
-    case 7: launch_step_v<7>(a, vec4, b, *tp, *tq, s); break;
-    case 8: launch_step_v<8>(a, vec4, b, *tp, *tq, s); break;
+  switch (r) {
+    case 1: launch_step_v<1>(io, vec4, b, *tp, *tq, s); break;
+    case 2: launch_step_v<2>(io, vec4, b, *tp, *tq, s); break;
+    case 3: launch_step_v<3>(io, vec4, b, *tp, *tq, s); break;
+    case 4: launch_step_v<4>(io, vec4, b, *tp, *tq, s); break;
+    case 5: launch_step_v<5>(io, vec4, b, *tp, *tq, s); break;
+    case 6: launch_step_v<6>(io, vec4, b, *tp, *tq, s); break;
+    case 7: launch_step_v<7>(io, vec4, b, *tp, *tq, s); break;
+    case 8: launch_step_v<8>(io, vec4, b, *tp, *tq, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t lq_step(LqState &st, const LqStepArgs &a, hipStream_t s) {
+  StepIO io;
+  std::memset(&io, 0, sizeof io);
+  io.W.G[0] = a.G;
+  io.W.E[0] = a.E;
+  io.W.Q[0] = a.Q;
+  io.K = 1;
+  io.n = a.n;
+  io.m = a.m;
+  io.p_codes = a.p_codes;
+  io.q_codes = a.q_codes;
+  io.p_colmax = a.p_colmax;
+  io.q_colmax = a.q_colmax;
+  io.p_hat = a.p_hat;
+  io.p_pre = a.p_pre;
+  io.q_pre = a.q_pre;
+  io.G_hat = nullptr;
+  return run_step(st, io, a.r, a.alpha, a.bits_p, a.bits_q, s);
+}
+
+hipError_t lq_step_workers(LqState &st, const LqWorkersStepArgs &a, hipStream_t s) {
+  if (a.K < 1 || a.K > kLqMaxWorkers) return hipErrorInvalidValue;
+  StepIO io;
+  std::memset(&io, 0, sizeof io);
+  io.W = a.W;
+  io.K = a.K;
+  io.n = a.n;
+  io.m = a.m;
+  io.p_codes = a.p_codes;
+  io.q_codes = a.q_codes;
+  io.p_colmax = a.p_colmax;
+  io.q_colmax = a.q_colmax;
+  io.G_hat = a.G_hat;
+  return run_step(st, io, a.r, a.alpha, a.bits_p, a.bits_q, s);
 }
 
 void lq_release(LqState &st) {

@@ -54,6 +54,8 @@ _SIGS = {
     "gq_dequantize_wire": (_i32, [_p, _p, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _p, _p]),
     "gq_powersgd_logquant": (_i32, [_p, _p, _p, _p, _i64, _i64, _i32, _d, _i32, _i32, _p, _p,
                                     _p, _p, _p, _p, _p, _p]),
+    "gq_lq_step_workers": (_i32, [_p, _p, _p, _p, _i32, _i64, _i64, _i32, _d, _i32, _i32, _p,
+                                  _p, _p, _p, _p, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -380,4 +382,39 @@ def powersgd_logquant(G, E, Q, alpha, bits, out=None, want_hat=True, want_pre=Fa
         _dev(o["p_codes"], "p_codes", torch.int8), _dev(o["p_colmax"], "p_colmax", torch.float32),
         _dev(o["q_codes"], "q_codes", torch.int8), _dev(o["q_colmax"], "q_colmax", torch.float32),
         opt("p_hat"), opt("p_pre"), opt("q_pre"), _stream()))
+    return o
+
+
+def lq_step_workers(Gs, Es, Qs, alpha, bits, bits_q=None, out=None,
+                    ctx: Optional[Context] = None):
+    """One LQ-SGD step of K workers (lists of n x m gradients, n x m errors and m x r warm
+    starts; E's and Q's are updated in place).  Returns a dict with every worker's message
+    stacked by worker (p_codes K x n x r, p_colmax K x r, q_codes K x m x r, q_colmax K x r)
+    and G_hat (n x m), the mean of the decoded messages."""
+    ctx = ctx or context()
+    K = len(Gs)
+    if not (len(Es) == K and len(Qs) == K):
+        raise ValueError("Gs, Es and Qs must have one entry per worker")
+    n, m = Gs[0].shape
+    r = Qs[0].shape[1]
+    for k in range(K):
+        if tuple(Gs[k].shape) != (n, m) or tuple(Es[k].shape) != (n, m):
+            raise ValueError("worker %d: G and E must be %d x %d" % (k, n, m))
+        if tuple(Qs[k].shape) != (m, r):
+            raise ValueError("worker %d: Q must be %d x %d" % (k, m, r))
+    dev = Gs[0].device
+    o = dict(out or {})
+    o.setdefault("p_codes", torch.empty(K, n, r, dtype=torch.int8, device=dev))
+    o.setdefault("p_colmax", torch.empty(K, r, dtype=torch.float32, device=dev))
+    o.setdefault("q_codes", torch.empty(K, m, r, dtype=torch.int8, device=dev))
+    o.setdefault("q_colmax", torch.empty(K, r, dtype=torch.float32, device=dev))
+    o.setdefault("G_hat", torch.empty(n, m, dtype=torch.float32, device=dev))
+    gp = _ptr_array([_dev(G, "G[k]", torch.float32) for G in Gs])
+    ep = _ptr_array([_dev(E, "E[k]", torch.float32) for E in Es])
+    qp = _ptr_array([_dev(Q, "Q[k]", torch.float32) for Q in Qs])
+    ctx.check(_lib.gq_lq_step_workers(
+        ctx.handle, gp, ep, qp, K, n, m, r, alpha, bits, bits if bits_q is None else bits_q,
+        _dev(o["p_codes"], "p_codes", torch.int8), _dev(o["p_colmax"], "p_colmax", torch.float32),
+        _dev(o["q_codes"], "q_codes", torch.int8), _dev(o["q_colmax"], "q_colmax", torch.float32),
+        _dev(o["G_hat"], "G_hat", torch.float32), _stream()))
     return o

@@ -177,6 +177,7 @@ LQ_SHAPES = ((4096, 4096), (4096, 11008))
 LQ_RANKS = (1, 4, 7)
 LQ_ALPHA = 10.0
 LQ_BITS = 8
+LQ_WORKERS = 8      # workers of the K-worker step (the flat Global-QSGD workload's count)
 
 
 # ----------------------------------------------------------------------------- drawing
@@ -258,6 +259,21 @@ def lq_problem(n: int, m: int, r: int, step: int, device="cpu"):
     U = torch.randn(n, 8, generator=g, device=device, dtype=torch.float64) * sig
     V = torch.randn(m, 8, generator=g, device=device, dtype=torch.float64) * sig
     gs = _gen(device, "lq", n, m, "noise", step)
+    G = (torch.randn(n, m, generator=gs, device=device, dtype=torch.float64) * 1e-3
+         + U @ V.T).to(torch.float32)
+    gq = _gen(device, "lq", n, m, r, "q0")
+    Q0 = torch.randn(m, r, generator=gq, device=device, dtype=torch.float32)
+    return G.contiguous(), Q0.contiguous()
+
+
+def lq_worker_problem(n: int, m: int, r: int, step: int, worker: int, device="cpu"):
+    """(G, Q_0) of one worker of the K-worker LQ-SGD workload: the shared rank-8 signal of
+    lq_problem plus the worker's own noise (std 1e-3); every worker starts from the same Q_0."""
+    g = _gen(device, "lq", n, m, "signal")
+    sig = (1e-3 / np.sqrt(8.0)) ** 0.5
+    U = torch.randn(n, 8, generator=g, device=device, dtype=torch.float64) * sig
+    V = torch.randn(m, 8, generator=g, device=device, dtype=torch.float64) * sig
+    gs = _gen(device, "lq", n, m, "noise", step, "worker", worker)
     G = (torch.randn(n, m, generator=gs, device=device, dtype=torch.float64) * 1e-3
          + U @ V.T).to(torch.float32)
     gq = _gen(device, "lq", n, m, r, "q0")

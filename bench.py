@@ -117,7 +117,7 @@ def time_calls(torch, fn, iters, warmup=1, median=True):
 
 
 ROW_GROUPS = ("flat-1.3G-steps", "resnet50", "gpt2", "lq-4096x4096", "lq-4096x11008",
-              "baselines")
+              "lq-workers", "baselines")
 FLAT_GROUPS = ("flat-1.3G-steps", "baselines")  # groups timed on the resident 1.3e9 buffers
 
 
@@ -143,6 +143,8 @@ def rows_breakdown(torch, gq, W, grads, S, w, args, groups=ROW_GROUPS):
     for shape in W.LQ_SHAPES:
         if "lq-%dx%d" % shape in groups:
             rows_lq(torch, gq, W, shape, row)
+    if "lq-workers" in groups:
+        rows_lq_workers(torch, gq, W, row)
     if "baselines" in groups:
         rows_baselines(torch, gq, W, grads, w, row, it)
     torch.cuda.empty_cache()
@@ -249,6 +251,25 @@ def rows_lq(torch, gq, W, shape, row):
         row("lq_step_%dx%d_r%d" % (n5, m5, r5), ms, 6 * n5 * m5 * 4,
             "G read, E read+write, E read, E read+write")
         del G, E, Q
+
+
+def rows_lq_workers(torch, gq, W, row):
+    """One LQ-SGD step of K = 8 workers: each worker's compressor, then the mean of the decoded
+    messages and every worker's error feedback."""
+    K = W.LQ_WORKERS
+    for (n5, m5), r5 in (((4096, 4096), 1), ((4096, 4096), 7), ((4096, 11008), 7)):
+        Gs, Es, Qs = [], [], []
+        for k in range(K):
+            G, Q0 = W.lq_worker_problem(n5, m5, r5, 0, k, "cuda")
+            Gs.append(G)
+            Es.append(torch.zeros_like(G))
+            Qs.append(Q0.clone())
+        o5 = gq.lq_step_workers(Gs, Es, Qs, W.LQ_ALPHA, W.LQ_BITS)
+        ms = time_calls(torch, lambda: gq.lq_step_workers(Gs, Es, Qs, W.LQ_ALPHA, W.LQ_BITS,
+                                                          out=o5), 11)
+        row("lq_workers_K%d_%dx%d_r%d" % (K, n5, m5, r5), ms, (6 * K + 1) * n5 * m5 * 4,
+            "per worker: G read, E read+write, E read, E read+write; G_hat written once")
+        del Gs, Es, Qs, o5
 
 
 def rows_baselines(torch, gq, W, grads, w, row, it):

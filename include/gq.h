@@ -226,6 +226,31 @@ gq_status gq_powersgd_logquant(gq_ctx *ctx, const float *G, float *E, float *Q, 
                                float *q_colmax, float *p_hat_or_null, float *p_pre_or_null,
                                float *q_pre_or_null, void *stream);
 
+/* One LQ-SGD step of K data-parallel workers whose buffers share this device (LQ-SGD review:
+ * "Core claim" -- each worker log-quantises its own factors before the exchange and sends
+ * r(n b_p + m b_q) bits of codes; "What carries the argument" -- error feedback against the
+ * approximate global gradient Ghat_t, which the referee's comment on Section III-A names as the
+ * stand-in for the global gradient).  Log codes cannot be summed, so the exchange is of whole
+ * messages, and every worker forms the same mean of the decoded messages:
+ *   for each worker w: the single-worker compressor of gq_powersgd_logquant on
+ *     M_w = G_w + E_w from its own warm start Q_w (codes and column maxima of P_w and Q'_w);
+ *   G_hat = (1/K) sum_w Phat_w Qhat_w^T;  E_w <- M_w - G_hat;  Q_w <- Qhat_w.
+ * K = 1 gives gq_powersgd_logquant's codes, maxima, E and Q (G_hat = Phat Qhat^T).
+ *   G, E, Q       (host) arrays of K device pointers: n x m fp32 gradients (read only; workers
+ *                 may share one), n x m fp32 errors (in/out) and m x r fp32 warm starts
+ *                 (in/out); the E's and Q's must be K distinct buffers
+ *   1 <= K <= 16, 1 <= r <= 8, 1 <= n <= 4,194,240, 1 <= m <= 2^30, alpha > 0, bits 2..8
+ *   p_codes K x n x r int8, p_colmax K x r fp32, q_codes K x m x r int8, q_colmax K x r fp32:
+ *                 every worker's message, stacked by worker
+ *   G_hat n x m fp32 (must not be one of the E's)
+ * Every device pointer 16-byte aligned.  Invalid arguments return GQ_EINVAL or GQ_EALIGN with
+ * nothing launched; scratch that cannot be allocated returns GQ_ENOMEM. */
+gq_status gq_lq_step_workers(gq_ctx *ctx, const float *const *G, float *const *E,
+                             float *const *Q, int32_t K, int64_t n, int64_t m, int32_t r,
+                             double alpha, int32_t bits_p, int32_t bits_q, int8_t *p_codes,
+                             float *p_colmax, int8_t *q_codes, float *q_colmax, float *G_hat,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif
