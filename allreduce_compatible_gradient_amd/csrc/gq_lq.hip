@@ -57,6 +57,8 @@ constexpr int kWavesC = 8;     // waves per column-pass block
 // Rows per column-pass chunk: 128, or 64 when 128-row chunks would give fewer than
 // kColBlocksMin blocks (the pass is then latency-bound and wants more of them).
 constexpr int kColBlocksMin = 1024;
+// MI355X's Infinity Cache (the last level before HBM)
+constexpr double kMallBytes = 256.0 * 1024 * 1024;
 // threads of the one-block solve: 16 waves, 8 at rank 8 (so that its r x r work fits in
 // registers)
 template <int RANK>
@@ -89,6 +91,16 @@ __device__ __forceinline__ void stv(float *p, const float (&v)[VEC]) {
     *reinterpret_cast<f32x4 *>(p) = t;
   } else {
     *p = v[0];
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void stv_nt(float *p, const float (&v)[VEC]) {
+  if constexpr (VEC == 4) {
+    f32x4 t = {v[0], v[1], v[2], v[3]};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(p));
+  } else {
+    __builtin_nontemporal_store(v[0], p);
   }
 }
 
@@ -162,7 +174,11 @@ __device__ __forceinline__ void tri_index(int t, int &a, int &b) {
 // share of the Gram matrix P^T P (packed upper triangle, fp64, stored entry-major so that the
 // solve reads each entry's partials contiguously).
 // Worker blockIdx.y of the step: its own G, E and Q; its slices of the stacked P and partials.
-template <int RANK, int VEC>
+// NT_M stores M non-temporally: when the step's M matrices together exceed the Infinity Cache,
+// dirty lines left there by this pass would be written back while the column pass reads M and
+// slow it (measured: 141 -> 96 us for 8 x 4096 x 4096 at r = 1); when they fit, the cached M
+// is what makes the next two passes fast, so ordinary stores are kept.
+template <int RANK, int VEC, bool NT_M>
 __global__ __launch_bounds__(kBlockA) void k_lq_ef_mq(const LqWorkerPtrs W,
                                                       float *__restrict__ P_all,
                                                       double *__restrict__ gpart_all, int64_t n,
@@ -200,7 +216,10 @@ __global__ __launch_bounds__(kBlockA) void k_lq_ef_mq(const LqWorkerPtrs W,
         float mv[VEC];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) mv[v] = g[rr][v] + e[rr][v];
-        stv<VEC>(E + (row0 + rr) * m + j, mv);
+        if constexpr (NT_M)
+          stv_nt<VEC>(E + (row0 + rr) * m + j, mv);
+        else
+          stv<VEC>(E + (row0 + rr) * m + j, mv);
 #pragma unroll
         for (int c = 0; c < RANK; ++c)
 #pragma unroll
@@ -938,8 +957,12 @@ void launch_step(const StepIO &io, const StepBufs &b, const LqTables &tp, const 
                  hipStream_t s) {
   const int64_t n = io.n, m = io.m;
   const unsigned K = (unsigned)io.K;
-  hipLaunchKernelGGL((k_lq_ef_mq<RANK, VEC>), dim3((unsigned)b.nblocks, K), dim3(kBlockA), 0, s,
-                     io.W, b.P, b.gpart, n, m);
+  if ((double)K * (double)n * (double)m * 4.0 > kMallBytes)
+    hipLaunchKernelGGL((k_lq_ef_mq<RANK, VEC, true>), dim3((unsigned)b.nblocks, K), dim3(kBlockA),
+                       0, s, io.W, b.P, b.gpart, n, m);
+  else
+    hipLaunchKernelGGL((k_lq_ef_mq<RANK, VEC, false>), dim3((unsigned)b.nblocks, K),
+                       dim3(kBlockA), 0, s, io.W, b.P, b.gpart, n, m);
   hipLaunchKernelGGL((k_lq_solve<RANK>), dim3(K), dim3(solve_block<RANK>()), 0, s, b.gpart,
                      b.nblocks, b.T, b.cmax_bits);
   const dim3 gcol((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)b.nchunks, K);
