@@ -100,6 +100,44 @@ def test_lq_step_in_a_graph():
     ectx.close()
 
 
+def test_lq_workers_step_in_a_graph():
+    """The K-worker LQ-SGD step captured after a warm-up call and replayed on fresh gradients:
+    every replay equals the eager step on a second context bit for bit."""
+    g = gq()
+    K, n, m, r = 3, 640, 512, 3
+    say("graph: lq workers step", K, n, m, r)
+    gen = torch.Generator(device="cuda").manual_seed(18)
+    Gs = [torch.randn(n, m, device="cuda", generator=gen) * 1e-3 for _ in range(K)]
+    E0 = [torch.randn(n, m, device="cuda", generator=gen) * 1e-4 for _ in range(K)]
+    Q0 = [torch.randn(m, r, device="cuda", generator=gen) for _ in range(K)]
+    gctx, ectx = g.Context(), g.Context()
+    Eg, Qg = [e.clone() for e in E0], [q.clone() for q in Q0]
+    Ee, Qe = [e.clone() for e in E0], [q.clone() for q in Q0]
+    og = g.lq_step_workers(Gs, Eg, Qg, W.LQ_ALPHA, W.LQ_BITS, ctx=gctx)   # warm-up: one step
+    oe = g.lq_step_workers(Gs, Ee, Qe, W.LQ_ALPHA, W.LQ_BITS, ctx=ectx)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        og = g.lq_step_workers(Gs, Eg, Qg, W.LQ_ALPHA, W.LQ_BITS, out=og, ctx=gctx)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for G in Gs:
+            G.mul_(-1.25)                      # new gradients every step, eagerly
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        oe = g.lq_step_workers(Gs, Ee, Qe, W.LQ_ALPHA, W.LQ_BITS, out=oe, ctx=ectx)
+        torch.cuda.synchronize()
+        for k in ("p_codes", "q_codes", "p_colmax", "q_colmax", "G_hat"):
+            assert torch.equal(og[k], oe[k]), "replay %d: %s" % (rep, k)
+        for w in range(K):
+            assert torch.equal(Eg[w], Ee[w]), "replay %d: E %d" % (rep, w)
+            assert torch.equal(Qg[w], Qe[w]), "replay %d: Q %d" % (rep, w)
+    del graph
+    gctx.close()
+    ectx.close()
+
+
 def test_two_contexts_on_two_streams():
     """Each context owns its scratch: two contexts driving two streams at once (default
     priority) give the same results as one after the other."""
