@@ -175,3 +175,33 @@ def test_argument_errors(case):
     with pytest.raises(g.GQError) as ei:
         g.lq_step_workers(Gs, Es, Qs, ALPHA, BITS, out=out)
     assert ei.value.code == 1  # GQ_EINVAL
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_workers_random_configurations(orc, i):
+    """Seeded random worker counts (1-16), shapes (m not always a multiple of 4), ranks 1-8,
+    alpha in {1, 10, 100} and code widths b_p, b_q in 4..8; workers share a low-rank signal
+    at their own scales; two steps each, within the step tolerances."""
+    g = gq()
+    rng = np.random.default_rng(80000 + i)
+    K = int(rng.integers(1, 17))
+    r = int(rng.integers(1, 9))
+    n = int(rng.integers(max(r, 8), 1200))
+    m = int(rng.integers(max(r, 8), 1200))
+    alpha = float(rng.choice([1.0, 10.0, 100.0]))
+    bp, bq = int(rng.integers(4, 9)), int(rng.integers(4, 9))
+    say("lq workers random", i, K, n, m, r, alpha, bp, bq)
+    U_ = rng.standard_normal((n, 8)) * 1e-3
+    V_ = rng.standard_normal((m, 8))
+    scale = 10.0 ** rng.uniform(-1, 1, K)
+    Es = [np.zeros((n, m), np.float32) for _ in range(K)]
+    Qs = [rng.standard_normal((m, r)).astype(np.float32) for _ in range(K)]
+    for t in range(2):
+        Gs = [((rng.standard_normal((n, m)) * 1e-3 + U_ @ V_.T) * scale[w]).astype(np.float32)
+              for w in range(K)]
+        ref = orc.lq_step_workers(Gs, Es, Qs, alpha, bp, bits_q=bq)
+        Ed = [dev(E) for E in Es]
+        Qd = [dev(Q) for Q in Qs]
+        out = g.lq_step_workers([dev(G) for G in Gs], Ed, Qd, alpha, bp, bits_q=bq)
+        _check(ref, out, [host(E) for E in Ed], [host(Q) for Q in Qd])
+        Es, Qs = ref["E"], ref["Q"]
