@@ -1,0 +1,105 @@
+"""The fused pass's fast path must give the general path's results bit for bit.
+
+On the exponential grid a worker's batch in which every |x| lies below the smallest value whose
+scaled magnitude reaches the lowest nonzero level 2^(1-E) is quantised without the clamp, the
+exponent split and the level selection.  These inputs are built around that threshold (and,
+as a control, the uniform grid's level 1, where the general path always runs), computed here
+in numpy's fp32 arithmetic from the scale the kernel is given: batches of small values, some
+holding the largest representable value below the threshold (the fast path at its edge), some
+holding the threshold itself or the next value above it in one worker and one lane (that batch
+falls back to the general path while the other workers' batches stay fast).  Sums and means
+are compared with the oracle bit for bit, for fp32 and bf16 elements and several worker counts.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_helpers import dev, first_diff, gq, host, say
+
+pytestmark = pytest.mark.gpu
+U, X = 0, 1
+
+
+@pytest.fixture(scope="module")
+def orc():
+    from oracle import oracle
+    oracle.lib()
+    return oracle
+
+
+def _threshold(inv, bound):
+    """Smallest fp32 a with fl(a * inv) >= bound (numpy fp32 products round to nearest even)."""
+    inv, bound = np.float32(inv), np.float32(bound)
+    a = np.float32(bound / inv)
+    while a > 0 and np.float32(np.nextafter(a, np.float32(0)) * inv) >= bound:
+        a = np.nextafter(a, np.float32(0))
+    while np.float32(a * inv) < bound:
+        a = np.nextafter(a, np.float32(np.inf))
+    return np.float32(a)
+
+
+def _bf16_below_at(a):
+    """Largest bf16 value below a and smallest bf16 value at or above a (as fp32)."""
+    bits = np.array([a], np.float32).view(np.uint32)[0]
+    lo = np.array([bits & 0xFFFF0000], np.uint32).view(np.float32)[0]
+    if lo >= a:
+        lo = np.array([(bits & 0xFFFF0000) - 0x10000], np.uint32).view(np.float32)[0]
+    hi = np.array([(np.array([lo], np.float32).view(np.uint32)[0]) + 0x10000],
+                  np.uint32).view(np.float32)[0]
+    assert lo < a <= hi
+    return np.float32(lo), np.float32(hi)
+
+
+def _to_bf16_bits(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+CASES = [(g, lv, b, K, dt) for (g, lv, b) in [(U, 7, 4), (U, 127, 8), (X, 7, 4)]
+         for K in (1, 3, 8, 16) for dt in ("f32", "bf16")]
+
+
+@pytest.mark.parametrize("grid,levels,bits,K,dt", CASES)
+def test_fast_path_matches_general_path(orc, grid, levels, bits, K, dt):
+    say("fast path", grid, levels, bits, K, dt)
+    g = gq()
+    rng = np.random.default_rng(1000 * grid + 10 * K + levels + (dt == "bf16"))
+    n = 2 * 8192 + 1000 + 5
+    S = np.float32(1.7)
+    if grid == U:
+        inv, bound = np.float32(np.float32(levels) / S), np.float32(1.0)
+    else:
+        inv, bound = np.float32(np.float32(1.0) / S), np.float32(2.0 ** (1 - levels))
+    thr = _threshold(inv, bound)
+    if dt == "bf16":
+        below, at = _bf16_below_at(thr)
+    else:
+        below, at = np.nextafter(thr, np.float32(0)), thr
+    above = np.nextafter(at, np.float32(np.inf)) if dt == "f32" else np.array(
+        [np.array([at], np.float32).view(np.uint32)[0] + 0x10000], np.uint32).view(np.float32)[0]
+    assert np.float32(below * inv) < bound <= np.float32(at * inv)
+    xs = []
+    for k in range(K):
+        x = (rng.standard_normal(n) * float(thr) * 0.05).astype(np.float32)
+        x[rng.random(n) < 0.02] = 0.0
+        # the edge of the fast path: the largest value below the threshold, either sign
+        for i in rng.choice(n, 40, replace=False):
+            x[i] = below if rng.random() < 0.5 else -below
+        # one worker, one lane: the threshold itself or the value above it
+        if k == K // 2:
+            for i in rng.choice(n, 12, replace=False):
+                x[i] = rng.choice([at, above, -at, -above])
+        if dt == "bf16":
+            x = _to_bf16_bits(x)
+        xs.append(x)
+    acc_bits = 16 if K * (levels if grid == U else 1 << (levels - 1)) < (1 << 15) else 32
+    ref = orc.allreduce_mean(xs, grid, levels, bits, acc_bits, 77, 0, scale=[S])
+    xd = [dev(x) for x in xs]
+    Sd = dev(np.array([S], np.float32))
+    mean = g.fused_mean(xd, Sd, grid, levels, bits, 77, acc_bits)
+    assert np.array_equal(host(mean), ref["mean"]), first_diff(host(mean), ref["mean"])
+    sd = torch.empty(n, dtype=torch.int16 if acc_bits == 16 else torch.int32, device="cuda")
+    mean2 = g.fused_mean(xd, Sd, grid, levels, bits, 77, acc_bits, sums=sd)
+    assert np.array_equal(host(sd), ref["sums"]), first_diff(host(sd), ref["sums"])
+    assert np.array_equal(host(mean2), ref["mean"])
+    # the planted values reach the levels they should: some sums are nonzero
+    assert np.any(ref["sums"] != 0)
