@@ -103,3 +103,49 @@ def test_fast_path_matches_general_path(orc, grid, levels, bits, K, dt):
     assert np.array_equal(host(mean2), ref["mean"])
     # the planted values reach the levels they should: some sums are nonzero
     assert np.any(ref["sums"] != 0)
+
+
+@pytest.mark.parametrize("K,dt", [(1, "f32"), (3, "f32"), (8, "f32"), (16, "bf16"), (5, "bf16")])
+@pytest.mark.parametrize("grid,levels", [(X, 7), (U, 7)])
+def test_worker_mean_fast_path(orc, grid, levels, K, dt):
+    """The per-worker-scale mean (QSGD / NUQSGD) at each worker's own lowest level: values just
+    below, at and above the threshold derived from that worker's scale, bit-exact means.  (The
+    fused pass's shortcut measured slower in this kernel and is not used there; these inputs
+    keep the level boundary under test for the baselines too.)"""
+    say("worker mean fast path", grid, levels, K, dt)
+    g = gq()
+    rng = np.random.default_rng(5000 + 10 * K + grid + (dt == "bf16"))
+    n = 2 * 8192 + 777
+    off = np.array([0, 8192, n], np.int64)
+    Sw = np.array([[np.float32(1.3 * (1.5 ** k) * (1 + 0.37 * s)) for s in range(2)]
+                   for k in range(K)], np.float32)
+    xs = []
+    for k in range(K):
+        x = np.empty(n, np.float32)
+        for s in range(2):
+            S = Sw[k, s]
+            if grid == U:
+                inv, bound = np.float32(np.float32(levels) / S), np.float32(1.0)
+            else:
+                inv, bound = np.float32(np.float32(1.0) / S), np.float32(2.0 ** (1 - levels))
+            thr = _threshold(inv, bound)
+            if dt == "bf16":
+                below, at = _bf16_below_at(thr)
+                above = np.array([np.array([at], np.float32).view(np.uint32)[0] + 0x10000],
+                                 np.uint32).view(np.float32)[0]
+            else:
+                below, at = np.nextafter(thr, np.float32(0)), thr
+                above = np.nextafter(at, np.float32(np.inf))
+            lo, hi = off[s], off[s + 1]
+            seg = (rng.standard_normal(hi - lo) * float(thr) * 0.05).astype(np.float32)
+            for i in rng.choice(hi - lo, 30, replace=False):
+                seg[i] = below if rng.random() < 0.5 else -below
+            if k == K // 2:
+                for i in rng.choice(hi - lo, 6, replace=False):
+                    seg[i] = rng.choice([at, above, -at, -above])
+            x[lo:hi] = seg
+        xs.append(_to_bf16_bits(x) if dt == "bf16" else x)
+    ref = orc.worker_mean(xs, Sw, grid, levels, 31, 0, off, 0)
+    got = g.worker_mean([dev(x) for x in xs], dev(np.ascontiguousarray(Sw)), grid, levels, 31,
+                        0, 0, off)
+    assert np.array_equal(host(got), ref), first_diff(host(got), ref)
