@@ -10,7 +10,7 @@ per second (K * n * 4 bytes per step).  ``roofline`` reports the dominant kernel
 pass) against the 8 TB/s HBM peak with its algorithmic bytes (K*n*4 in + n*4 out) and its
 average duration from HIP events recorded on the launch stream.  ``rows`` times each step of
 the path on its own (and the exponential-grid, bf16 and LQ-SGD workloads) for the same
-roofline.  ``cpu_baseline`` times the plain CPU oracle on the first 2^26 elements of every
+roofline.  ``cpu_baseline`` times the plain CPU oracle on the first 2^27 elements of every
 worker of the same data.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -384,7 +384,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 26)
+    ap.add_argument("--cpu-sample", type=int, default=1 << 27)
     ap.add_argument("--rows-only", choices=ROW_GROUPS, default=None,
                     help="time only this group of rows (no headline step, no CPU baseline): "
                          "one workload per rocprofv3 summary")
