@@ -125,10 +125,13 @@ def test_error_feedback_identity_on_gpu():
         assert torch.allclose(dec, Qs[w], rtol=2.5e-7, atol=0)
 
 
-@pytest.mark.parametrize("K,shape,r", [(4, (4096, 4096), 7), (8, (4096, 11008), 1)])
+@pytest.mark.parametrize("K,shape,r", [(4, (4096, 4096), 7), (8, (4096, 11008), 1),
+                                       (8, (4096, 4096), 1), (8, (4096, 4096), 7),
+                                       (8, (4096, 11008), 7)])
 def test_workers_full_shapes(orc, K, shape, r):
     """The LQ-SGD workload shapes with K workers (shared rank-8 signal, each worker's own noise),
-    one step from zero error and the common Q_0."""
+    one step from zero error and the common Q_0; the last three are the benchmark's
+    configurations, run through the same launches it times."""
     n, m = shape
     say("lq workers full", K, n, m, r)
     Gs, Qs = [], []
