@@ -152,3 +152,55 @@ def test_full_size_norm_and_fused_sampled(orc, name):
                 what, a, b, seg, first_diff(got, ref))
     del xs, out_w, out_d, codes
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,grid,levels,bits,acc_bits", [("f32", 0, 127, 8, 16),
+                                                             ("bf16", 0, 7, 4, 16)])
+def test_element_indices_beyond_2_31(orc, dtype, grid, levels, bits, acc_bits):
+    """Two workers of 2^31 + 24,581 elements (past the int32 range of element indices, and
+    past 2^32 bytes for bf16 too): the norm, the fused pass and the step-by-step path (codes,
+    integer sums, decode) over the whole buffers; runs around element 2^31, at the ragged end
+    and at random positions above 2^31 recomputed by the oracle, bit for bit."""
+    import dataclasses
+    n = (1 << 31) + 3 * TILE + 5
+    base = W.get("flat-1.3G-f32-K8-uniform127")
+    w = dataclasses.replace(base, name="flat-2^31+-%s" % dtype, K=2, n=n, dtype=dtype, grid=grid,
+                            levels=levels, bits=bits, acc_bits=acc_bits, out_dtype=dtype,
+                            offsets=np.array([0, n], np.int64))
+    say("beyond 2^31", w.name, "n", n, "GB", w.grad_bytes() / 1e9)
+    g = gq()
+    xs = W.gradients(w, "cuda")
+    torch.cuda.synchronize()
+    S_ref, norms_ref = _oracle_scale(orc, w, xs)
+    S_gpu, _ = g.global_norm(xs, w.offsets)
+    np.testing.assert_allclose(host(S_gpu), S_ref, rtol=1e-6, atol=0)
+    out_dtype = 1 if dtype == "bf16" else 0
+    scale = torch.from_numpy(S_ref).to("cuda")
+    out = g.fused_mean(xs, scale, grid, levels, bits, SEED, acc_bits, out_dtype)
+    codes = [g.quantize_pack(xs[k], scale, grid, levels, bits, SEED, k) for k in range(w.K)]
+    sums = g.accumulate_codes(codes, n, grid, levels, bits, acc_bits)
+    mean2 = g.dequantize(sums, scale, grid, levels, w.K, out_dtype)
+    torch.cuda.synchronize()
+    say("beyond 2^31: kernels done", w.name)
+    rng = np.random.default_rng(31)
+    t31 = 1 << 31
+    runs = [(0, RUN), (t31 - RUN // 2, t31 + RUN // 2), (t31 // TILE * TILE - RUN, t31 // TILE * TILE),
+            (n - RUN, n), (n - 5 - RUN // 2, n - 5 + RUN // 2)]
+    runs += [(int(i), int(i) + RUN) for i in rng.integers(t31, n - RUN, 8)]
+    # even starts keep 4-bit code pairs aligned; runs end at n at the latest
+    runs = [(a - a % 2, min(b, n)) for a, b in runs]
+    cb = (lambda i: i) if bits == 8 else (lambda i: (i + 1) // 2)
+    for a, b in runs:
+        xs_run = [W.to_numpy(x[a:b]) for x in xs]
+        ref = orc.allreduce_mean(xs_run, grid, levels, bits, acc_bits, SEED, index_base=a,
+                                 out_dtype=out_dtype, scale=S_ref)
+        for what, o in (("fused", out), ("composed", mean2)):
+            got = host(o[a:b])
+            assert np.array_equal(got, ref["mean"]), "%s run [%d, %d): %s" % (
+                what, a, b, first_diff(got, ref["mean"]))
+        assert np.array_equal(host(sums[a:b]), ref["sums"]), "sums run [%d, %d)" % (a, b)
+        for k in range(w.K):
+            got = host(codes[k][a if bits == 8 else a // 2:cb(b)])
+            assert np.array_equal(got, ref["codes"][k]), "codes %d run [%d, %d)" % (k, a, b)
+    del xs, out, codes, sums, mean2
+    torch.cuda.empty_cache()
