@@ -154,17 +154,19 @@ def test_full_size_norm_and_fused_sampled(orc, name):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("dtype,grid,levels,bits,acc_bits", [("f32", 0, 127, 8, 16),
-                                                             ("bf16", 0, 7, 4, 16)])
-def test_element_indices_beyond_2_31(orc, dtype, grid, levels, bits, acc_bits):
-    """Two workers of 2^31 + 24,581 elements (past the int32 range of element indices, and
-    past 2^32 bytes for bf16 too): the norm, the fused pass and the step-by-step path (codes,
-    integer sums, decode) over the whole buffers; runs around element 2^31, at the ragged end
-    and at random positions above 2^31 recomputed by the oracle, bit for bit."""
+@pytest.mark.parametrize("dtype,grid,levels,bits,acc_bits,K,n", [
+    ("f32", 0, 127, 8, 16, 2, (1 << 31) + 3 * TILE + 5),
+    ("bf16", 0, 7, 4, 16, 2, (1 << 31) + 3 * TILE + 5),
+    ("bf16", 1, 7, 4, 16, 1, (1 << 32) - 8)])
+def test_element_indices_beyond_2_31(orc, dtype, grid, levels, bits, acc_bits, K, n):
+    """Workers of 2^31 + 24,581 elements (past the int32 range of element indices, and past
+    2^32 bytes for bf16 too), and one worker of 2^32 - 8 elements (the largest buffer the
+    32-bit element counter allows): the norm, the fused pass and the step-by-step path (codes,
+    integer sums, decode) over the whole buffers; runs around element 2^31, at the end and at
+    random positions above 2^31 recomputed by the oracle, bit for bit."""
     import dataclasses
-    n = (1 << 31) + 3 * TILE + 5
     base = W.get("flat-1.3G-f32-K8-uniform127")
-    w = dataclasses.replace(base, name="flat-2^31+-%s" % dtype, K=2, n=n, dtype=dtype, grid=grid,
+    w = dataclasses.replace(base, name="flat-%d-%s" % (n, dtype), K=K, n=n, dtype=dtype, grid=grid,
                             levels=levels, bits=bits, acc_bits=acc_bits, out_dtype=dtype,
                             offsets=np.array([0, n], np.int64))
     say("beyond 2^31", w.name, "n", n, "GB", w.grad_bytes() / 1e9)
