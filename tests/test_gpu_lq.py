@@ -333,3 +333,29 @@ def test_step_random_configurations(orc, i):
         out = g.powersgd_logquant(dev(G), Ed, Qd, alpha, bp, want_pre=True, bits_q=bq)
         _check_step(ref, out, host(Ed), host(Qd))
         E, Q = ref["E"], ref["Q"]
+
+
+@pytest.mark.parametrize("n,m,r", [(65535 * 64, 12, 3), (4, 1 << 22, 2), (6, (1 << 22) + 3, 1)])
+def test_step_extreme_shapes(orc, n, m, r):
+    """The most rows the column pass's chunk grid allows (n = 65535 x 64), and very wide short
+    matrices (m = 2^22, and 2^22 + 3 so that no 4-column vector path applies): within the step
+    tolerances."""
+    say("lq step extreme", n, m, r)
+    rng = np.random.default_rng(n + m + r)
+    G = (rng.standard_normal((n, m)) * 1e-3).astype(np.float32)
+    E = np.zeros((n, m), np.float32)
+    Q = rng.standard_normal((m, r)).astype(np.float32)
+    ref, out, Eg, Qg = _step_both(orc, G, E, Q)
+    _check_step(ref, out, Eg, Qg)
+
+
+def test_step_rejects_too_many_rows():
+    """One row more than the chunk grid allows is refused on the host, nothing launched."""
+    g = gq()
+    n, m, r = 65535 * 64 + 1, 4, 1
+    G = torch.zeros(n, m, device="cuda")
+    E = torch.zeros(n, m, device="cuda")
+    Q = torch.zeros(m, r, device="cuda")
+    with pytest.raises(g.GQError) as ei:
+        g.powersgd_logquant(G, E, Q, ALPHA, BITS)
+    assert ei.value.code == 1
