@@ -128,6 +128,45 @@ __device__ __forceinline__ void load_part(const void *base, int64_t e0, int cnt,
   }
 }
 
+// One part of one worker as held between its load and its use: fp32 values, or bf16 elements
+// left in the words they were loaded in (element 2i in the low half of word i) and widened
+// where they are used, so that a buffer of bf16 parts takes half the registers.
+template <int DT, int P>
+struct PartBuf;
+template <int P>
+struct PartBuf<0, P> {
+  float v[P];
+  __device__ __forceinline__ void load(const void *base, int64_t e0, int cnt) {
+    load_part<0, P>(base, e0, cnt, v);
+  }
+  __device__ __forceinline__ float get(int e) const { return v[e]; }
+};
+template <int P>
+struct PartBuf<1, P> {
+  uint32_t w[P / 2];
+  __device__ __forceinline__ void load(const void *base, int64_t e0, int cnt) {
+    const uint16_t *b = static_cast<const uint16_t *>(base);
+    if (cnt == P) {
+      if constexpr (P == 8) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(b + e0));
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+      } else {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(b + e0));
+        w[0] = v.x; w[1] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < P / 2; ++i) w[i] = 0u;
+#pragma unroll
+      for (int e = 0; e < P; ++e)
+        if (e < cnt) w[e >> 1] |= (uint32_t)b[e0 + e] << ((e & 1) * 16);
+    }
+  }
+  __device__ __forceinline__ float get(int e) const {
+    return __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+  }
+};
+
 // Codes: c[e] holds the code field (bits wide) of element e0 + e.
 template <int P>
 __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t e0, int cnt, int bits,
@@ -788,39 +827,48 @@ __global__ __launch_bounds__(kBlock) void k_dequantize_wire(WireDequantArgs a) {
 // Workers are processed in batches of KB whose loads are all issued before any arithmetic.
 // KT > 0 fixes K at compile time; KT = 0 loops over a runtime K.
 //
-// Fast path (exponential grid, without code stores): when one worker's elements in every lane
-// of the wave have |x| below fast_below -- so that fl(|x| * inv) is below the lowest nonzero
-// level 2^(1-E), as for almost every element of a large tensor -- the index is 0 or 1 and the
-// round-up threshold is ceil(fl(|x| * inv) * 2^(E+31)), so the clamp, the exponent split and
-// the level selection of the general path drop out; the results are the general path's bit for
-// bit (ResNet-50's 161 tensors x 8 workers: 0.190 -> 0.184 ms).  The same shortcut on the
-// uniform grid (level 0 or 1 below u = 1) measured no faster for bf16 GPT-2 buckets, whose pass
-// is not limited by these instructions alone, and is not used there.
-template <int DT, int GRID, int P, int NP, int KB, bool STORE>
-__device__ __forceinline__ void fused_batch(const FusedArgs &a, int k0, int kn,
-                                            const int64_t (&e0)[NP], const int (&cnt)[NP],
-                                            const uint32_t (&am)[NP][P], const SegQ &q,
-                                            float sf, float lo_scale, float fast_below,
-                                            float (&accf)[NP][P], int32_t (&acci)[NP][P]) {
-  float x[KB][NP][P];
+// Fast path (FAST, without code stores): when one worker's elements in every lane of the wave
+// have |x| below fast_below -- so that fl(|x| * inv) is below the lowest nonzero level (1 on
+// the uniform grid, 2^(1-E) on the exponential one), as for almost every element of a large
+// tensor -- the level is 0 or 1 and the round-up threshold is ceil(fl(|x| * inv) * 2^32)
+// (uniform) or ceil(fl(|x| * inv) * 2^(E+31)) (exponential), so the clamp, floor, fraction,
+// exponent split and level selection of the general path drop out.  The results are the
+// general path's bit for bit (adding copysign(0, x) or +0 to a sum that starts at +0 gives the
+// same sum).  Used on the exponential grid (ResNet-50's 161 tensors x 8 workers: 0.190 ->
+// 0.184 ms) and in the double-buffered bf16 pass below; in the single-buffered bf16 pass the
+// uniform grid's shortcut saved instructions but no time (the waits for each batch's loads were
+// then exposed), so it is not used there.
+template <int DT, int P, int NP, int KB>
+__device__ __forceinline__ void fused_load(const FusedArgs &a, int k0, int kn,
+                                           const int64_t (&e0)[NP], const int (&cnt)[NP],
+                                           PartBuf<DT, P> (&x)[KB][NP]) {
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
     if (kb < kn)
 #pragma unroll
       for (int j = 0; j < NP; ++j)
-        if (cnt[j] > 0) load_part<DT, P>(a.grads[k0 + kb], e0[j], cnt[j], x[kb][j]);
+        if (cnt[j] > 0) x[kb][j].load(a.grads[k0 + kb], e0[j], cnt[j]);
+}
+
+template <int DT, int GRID, int P, int NP, int KB, bool STORE, bool FAST>
+__device__ __forceinline__ void fused_compute(const FusedArgs &a, int k0, int kn,
+                                              const PartBuf<DT, P> (&x)[KB][NP],
+                                              const int64_t (&e0)[NP], const int (&cnt)[NP],
+                                              const uint32_t (&am)[NP][P], const SegQ &q,
+                                              float sf, float lo_scale, float fast_below,
+                                              float (&accf)[NP][P], int32_t (&acci)[NP][P]) {
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     if (kb >= kn) break;
     const uint32_t km = a.key_mix[k0 + kb];
     bool fast = false;
-    if constexpr (!STORE && GRID == 1) {
+    if constexpr (!STORE && FAST) {
       bool lane_fast = true;
 #pragma unroll
       for (int j = 0; j < NP; ++j)
 #pragma unroll
         for (int e = 0; e < P; ++e)  // lanes past the end hold no elements: no condition
-          lane_fast &= cnt[j] <= 0 ? true : fabsf(x[kb][j][e]) < fast_below;
+          lane_fast &= cnt[j] <= 0 ? true : fabsf(x[kb][j].get(e)) < fast_below;
       fast = __all(lane_fast);
     }
     if (fast) {
@@ -828,11 +876,16 @@ __device__ __forceinline__ void fused_batch(const FusedArgs &a, int k0, int kn,
       for (int j = 0; j < NP; ++j)
 #pragma unroll
         for (int e = 0; e < P; ++e) {
-          const float xv = x[kb][j][e];
+          const float xv = x[kb][j].get(e);
           const uint32_t h = fmix32_tail(am[j][e] ^ km);
           const float tv = fabsf(xv) * q.inv;
-          const uint32_t c = (uint32_t)ceilf(tv * lo_scale);
-          acci[j][e] += h < c ? (xv < 0.0f ? -1 : 1) : 0;
+          if constexpr (GRID == 0) {
+            const uint32_t c = (uint32_t)ceilf(tv * 4294967296.0f);
+            accf[j][e] += h < c ? copysignf(1.0f, xv) : 0.0f;
+          } else {
+            const uint32_t c = (uint32_t)ceilf(tv * lo_scale);
+            acci[j][e] += h < c ? (xv < 0.0f ? -1 : 1) : 0;
+          }
         }
       continue;
     }
@@ -841,7 +894,7 @@ __device__ __forceinline__ void fused_batch(const FusedArgs &a, int k0, int kn,
       uint32_t c[P];
 #pragma unroll
       for (int e = 0; e < P; ++e) {
-        const float xv = x[kb][j][e];
+        const float xv = x[kb][j].get(e);
         const uint32_t h = fmix32_tail(am[j][e] ^ km);
         if constexpr (GRID == 0) {
           const float m = quant_uniform_mag(xv, q.inv, sf, h);
@@ -859,6 +912,18 @@ __device__ __forceinline__ void fused_batch(const FusedArgs &a, int k0, int kn,
   }
 }
 
+template <int DT, int GRID, int P, int NP, int KB, bool STORE>
+__device__ __forceinline__ void fused_batch(const FusedArgs &a, int k0, int kn,
+                                            const int64_t (&e0)[NP], const int (&cnt)[NP],
+                                            const uint32_t (&am)[NP][P], const SegQ &q,
+                                            float sf, float lo_scale, float fast_below,
+                                            float (&accf)[NP][P], int32_t (&acci)[NP][P]) {
+  PartBuf<DT, P> x[KB][NP];
+  fused_load<DT, P, NP, KB>(a, k0, kn, e0, cnt, x);
+  fused_compute<DT, GRID, P, NP, KB, STORE, GRID == 1>(a, k0, kn, x, e0, cnt, am, q, sf,
+                                                       lo_scale, fast_below, accf, acci);
+}
+
 // Without the code stores both grids fit in 128 VGPRs (4 waves per SIMD, enough loads in
 // flight per CU to cover HBM latency); the code-storing variants keep more values live and
 // get 256 (2 waves per SIMD) rather than spilling.
@@ -872,6 +937,11 @@ void k_fused(FusedArgs a) {
   // branch needs the registers (the exponential grid without code stores)
   constexpr bool FASTP = !STORE && GRID == 1;
   constexpr int KB = FASTP && (KT == 0 || KT > 4) ? 4 : (KT == 16 ? 8 : (KT > 0 ? KT : 4));
+  // bf16, 16 workers, no code stores: four batches of 4 workers, double-buffered so that the
+  // next batch's loads are in flight while the current one is quantised, with the fast path on
+  // both grids (GPT-2's buckets: 1.158 -> 0.946 ms from the double buffering, -> 0.875 ms with
+  // the uniform grid's fast path)
+  constexpr bool PIPE = !STORE && DT == 1 && KT == 16;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int K = KT > 0 ? KT : a.K;
   const float sf = (float)a.levels;
@@ -884,7 +954,9 @@ void k_fused(FusedArgs a) {
     const SegQ q = seg_quant<GRID>(S, a.levels);
     const float f = seg_decode(S, a.denom);
     const float fast_below =
-        GRID == 1 && q.valid ? below_bound(q.inv, ldexpf(1.0f, 1 - a.levels)) : 0.0f;
+        q.valid && (GRID == 1 || PIPE)
+            ? below_bound(q.inv, GRID == 1 ? ldexpf(1.0f, 1 - a.levels) : 1.0f)
+            : 0.0f;
     const int nch = (len + kChunk - 1) / kChunk;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
       int64_t e0[NP];
@@ -906,7 +978,21 @@ void k_fused(FusedArgs a) {
         }
       }
       if (q.valid) {
-        if constexpr (KT > 0) {
+        if constexpr (PIPE) {
+          PartBuf<DT, P> xa[4][NP], xb[4][NP];
+          fused_load<DT, P, NP, 4>(a, 0, 4, e0, cnt, xa);
+          fused_load<DT, P, NP, 4>(a, 4, 4, e0, cnt, xb);
+          fused_compute<DT, GRID, P, NP, 4, STORE, true>(a, 0, 4, xa, e0, cnt, am, q, sf,
+                                                               lo_scale, fast_below, accf, acci);
+          fused_load<DT, P, NP, 4>(a, 8, 4, e0, cnt, xa);
+          fused_compute<DT, GRID, P, NP, 4, STORE, true>(a, 4, 4, xb, e0, cnt, am, q, sf,
+                                                               lo_scale, fast_below, accf, acci);
+          fused_load<DT, P, NP, 4>(a, 12, 4, e0, cnt, xb);
+          fused_compute<DT, GRID, P, NP, 4, STORE, true>(a, 8, 4, xa, e0, cnt, am, q, sf,
+                                                               lo_scale, fast_below, accf, acci);
+          fused_compute<DT, GRID, P, NP, 4, STORE, true>(a, 12, 4, xb, e0, cnt, am, q, sf,
+                                                               lo_scale, fast_below, accf, acci);
+        } else if constexpr (KT > 0) {
 #pragma unroll 1
           for (int k0 = 0; k0 < KT; k0 += KB)
             fused_batch<DT, GRID, P, NP, KB, STORE>(a, k0, KB, e0, cnt, am, q, sf, lo_scale,
@@ -1047,18 +1133,23 @@ __global__ void k_worker_factors(const float *scales, int64_t count, int levels,
   fac[i] = make_float2(q.valid ? q.inv : 0.0f, seg_decode(S, denom));
 }
 
-template <int DT, int GRID, int P, int NP, int KB>
-__device__ __forceinline__ void worker_batch(const WorkerMeanArgs &a, int k0, int kn,
-                                             float2 fl, const int64_t (&e0)[NP],
-                                             const int (&cnt)[NP], const uint32_t (&am)[NP][P],
-                                             float sf, float lo_scale, float (&acc)[NP][P]) {
-  float x[KB][NP][P];
+template <int DT, int P, int NP, int KB>
+__device__ __forceinline__ void worker_load(const WorkerMeanArgs &a, int k0, int kn,
+                                            const int64_t (&e0)[NP], const int (&cnt)[NP],
+                                            PartBuf<DT, P> (&x)[KB][NP]) {
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
     if (kb < kn)
 #pragma unroll
       for (int j = 0; j < NP; ++j)
-        if (cnt[j] > 0) load_part<DT, P>(a.grads[k0 + kb], e0[j], cnt[j], x[kb][j]);
+        if (cnt[j] > 0) x[kb][j].load(a.grads[k0 + kb], e0[j], cnt[j]);
+}
+
+template <int DT, int GRID, int P, int NP, int KB>
+__device__ __forceinline__ void worker_compute(const WorkerMeanArgs &a, int k0, int kn,
+                                               const PartBuf<DT, P> (&x)[KB][NP], float2 fl,
+                                               const uint32_t (&am)[NP][P], float sf,
+                                               float lo_scale, float (&acc)[NP][P]) {
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     if (kb >= kn) break;
@@ -1071,7 +1162,7 @@ __device__ __forceinline__ void worker_batch(const WorkerMeanArgs &a, int k0, in
     for (int j = 0; j < NP; ++j)
 #pragma unroll
       for (int e = 0; e < P; ++e) {
-        const float xv = x[kb][j][e];
+        const float xv = x[kb][j].get(e);
         const uint32_t h = fmix32_tail(am[j][e] ^ km);
         float l;
         if constexpr (GRID == 0)
@@ -1081,6 +1172,16 @@ __device__ __forceinline__ void worker_batch(const WorkerMeanArgs &a, int k0, in
         acc[j][e] = fmaf(l, fac, acc[j][e]);  // one rounding per worker, in worker order
       }
   }
+}
+
+template <int DT, int GRID, int P, int NP, int KB>
+__device__ __forceinline__ void worker_batch(const WorkerMeanArgs &a, int k0, int kn,
+                                             float2 fl, const int64_t (&e0)[NP],
+                                             const int (&cnt)[NP], const uint32_t (&am)[NP][P],
+                                             float sf, float lo_scale, float (&acc)[NP][P]) {
+  PartBuf<DT, P> x[KB][NP];
+  worker_load<DT, P, NP, KB>(a, k0, kn, e0, cnt, x);
+  worker_compute<DT, GRID, P, NP, KB>(a, k0, kn, x, fl, am, sf, lo_scale, acc);
 }
 
 // For each element: every worker quantised with its own scale and decoded with its own factor,
@@ -1103,6 +1204,9 @@ void k_worker_mean(WorkerMeanArgs a) {
     const int nch = (len + kChunk - 1) / kChunk;
     // lane k holds worker k's (s/S or 1/S, decode factor) for this tile's segment (K <= 64)
     const float2 fl = a.fac[(int64_t)(lane < K ? lane : 0) * a.tv.nseg + seg];
+    // bf16, 16 workers: double-buffered batches of 4 as in k_fused (the fast path measured
+    // slower in this kernel: 0.985 against 0.948 ms on GPT-2's buckets, and is not used)
+    constexpr bool PIPE = KT == 16 && DT == 1;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
       int64_t e0[NP];
       int cnt[NP];
@@ -1120,10 +1224,22 @@ void k_worker_mean(WorkerMeanArgs a) {
           acc[j][e] = 0.0f;
         }
       }
+      if constexpr (PIPE) {
+        PartBuf<DT, P> xa[4][NP], xb[4][NP];
+        worker_load<DT, P, NP, 4>(a, 0, 4, e0, cnt, xa);
+        worker_load<DT, P, NP, 4>(a, 4, 4, e0, cnt, xb);
+        worker_compute<DT, GRID, P, NP, 4>(a, 0, 4, xa, fl, am, sf, lo_scale, acc);
+        worker_load<DT, P, NP, 4>(a, 8, 4, e0, cnt, xa);
+        worker_compute<DT, GRID, P, NP, 4>(a, 4, 4, xb, fl, am, sf, lo_scale, acc);
+        worker_load<DT, P, NP, 4>(a, 12, 4, e0, cnt, xb);
+        worker_compute<DT, GRID, P, NP, 4>(a, 8, 4, xa, fl, am, sf, lo_scale, acc);
+        worker_compute<DT, GRID, P, NP, 4>(a, 12, 4, xb, fl, am, sf, lo_scale, acc);
+      } else {
 #pragma unroll 1
-      for (int k0 = 0; k0 < K; k0 += KB)
-        worker_batch<DT, GRID, P, NP, KB>(a, k0, min(KB, K - k0), fl, e0, cnt, am, sf, lo_scale,
-                                          acc);
+        for (int k0 = 0; k0 < K; k0 += KB)
+          worker_batch<DT, GRID, P, NP, KB>(a, k0, min(KB, K - k0), fl, e0, cnt, am, sf,
+                                            lo_scale, acc);
+      }
 #pragma unroll
       for (int j = 0; j < NP; ++j)
         if (cnt[j] > 0) store_mean<P>(a.out, a.out_dtype, e0[j], cnt[j], acc[j]);

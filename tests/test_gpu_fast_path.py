@@ -1,14 +1,14 @@
 """The fused pass's fast path must give the general path's results bit for bit.
 
-On the exponential grid a worker's batch in which every |x| lies below the smallest value whose
-scaled magnitude reaches the lowest nonzero level 2^(1-E) is quantised without the clamp, the
-exponent split and the level selection.  These inputs are built around that threshold (and,
-as a control, the uniform grid's level 1, where the general path always runs), computed here
-in numpy's fp32 arithmetic from the scale the kernel is given: batches of small values, some
-holding the largest representable value below the threshold (the fast path at its edge), some
-holding the threshold itself or the next value above it in one worker and one lane (that batch
-falls back to the general path while the other workers' batches stay fast).  Sums and means
-are compared with the oracle bit for bit, for fp32 and bf16 elements and several worker counts.
+A worker's batch in which every |x| lies below the smallest value whose scaled magnitude
+reaches the lowest nonzero level (2^(1-E) on the exponential grid; 1 on the uniform grid, where
+the 16-worker bf16 pass uses the shortcut) is quantised without the clamp, floor and level
+selection.  These inputs are built around that threshold, computed here in numpy's fp32
+arithmetic from the scale the kernel is given: batches of small values, some holding the
+largest representable value below the threshold (the fast path at its edge), some holding the
+threshold itself or the next value above it in one worker and one lane (that batch falls back
+to the general path while the other workers' batches stay fast).  Sums and means are compared
+with the oracle bit for bit, for fp32 and bf16 elements, both grids and several worker counts.
 """
 import numpy as np
 import pytest
