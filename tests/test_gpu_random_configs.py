@@ -21,9 +21,9 @@ def orc():
     return oracle
 
 
-def _config(i):
+def _config(i, K=None, bf16=None):
     rng = np.random.default_rng(90000 + i)
-    K = int(rng.choice([1, 2, 3, 4, 5, 8, 11, 16, 23]))
+    K = int(rng.choice([1, 2, 3, 4, 5, 8, 11, 16, 23])) if K is None else K
     n = int(rng.integers(1, 40000))
     nseg = int(rng.integers(1, 6))
     cuts = sorted(int(c) // 8 * 8 for c in rng.integers(0, n + 1, nseg - 1))
@@ -34,7 +34,7 @@ def _config(i):
     levels = int(rng.integers(1, maxlv + 1)) if grid == U else int(rng.integers(1, min(maxlv, 12) + 1))
     maxlin = levels if grid == U else 1 << (levels - 1)
     acc_bits = 16 if K * maxlin < (1 << 15) and rng.random() < 0.6 else 32
-    bf16 = bool(rng.random() < 0.4)
+    bf16 = bool(rng.random() < 0.4) if bf16 is None else bf16
     out_dtype = int(rng.random() < 0.3)
     seed = int(rng.integers(0, 1 << 62))
     index_base = int(rng.integers(0, (1 << 32) - n))
@@ -52,8 +52,18 @@ def _config(i):
 
 @pytest.mark.parametrize("i", range(CASES))
 def test_random_configuration(orc, i):
+    _run(orc, i, _config(i))
+
+
+@pytest.mark.parametrize("i", range(CASES, CASES + 8))
+def test_random_configuration_bf16_16_workers(orc, i):
+    """The double-buffered 16-worker bf16 pass (with its fast path) on random lengths, segment
+    layouts, grids, levels and seeds."""
+    _run(orc, i, _config(i, K=16, bf16=True))
+
+
+def _run(orc, i, c):
     g = gq()
-    c = _config(i)
     K, n, off, grid, bits, levels = c["K"], c["n"], c["off"], c["grid"], c["bits"], c["levels"]
     say("random", i, {k: v for k, v in c.items() if k not in ("xs", "off")}, "nseg", off.size - 1)
     xs = c["xs"]
