@@ -758,6 +758,11 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
     int len, seg;
     tile_of(a.tv, t, kTile, begin, len, seg);
     const SegQ q = seg_quant<GRID>(a.scale[seg], a.levels);
+    // the fused pass's fast path: a part whose elements, in every active lane, lie below the
+    // lowest nonzero level has levels 0 and +-1 only (bit for bit the general path's)
+    const float bound = GRID == 0 ? 1.0f : ldexpf(1.0f, 1 - a.levels);
+    const float fast_below = q.valid ? below_bound(q.inv, bound) : 0.0f;
+    const float up_scale = GRID == 0 ? 4294967296.0f : lo_scale;
     const int nch = (len + kChunk - 1) / kChunk;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
 #pragma unroll
@@ -771,6 +776,20 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
           float x[P];
           load_part<DT, P>(a.grad, e0, cnt, x);
           const uint32_t ctr = a.index_base + (uint32_t)e0;
+          bool lane_fast = true;
+#pragma unroll
+          for (int e = 0; e < P; ++e) lane_fast &= fabsf(x[e]) < fast_below;
+          if (__all(lane_fast)) {
+#pragma unroll
+            for (int e = 0; e < P; ++e) {
+              const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+              const uint32_t c = (uint32_t)ceilf(fabsf(x[e]) * q.inv * up_scale);
+              const int32_t lin = h < c ? (x[e] < 0.0f ? -1 : 1) : 0;
+              v[e] = (uint32_t)(lin + a.offset);
+            }
+            store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
+            continue;
+          }
 #pragma unroll
           for (int e = 0; e < P; ++e) {
             const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);

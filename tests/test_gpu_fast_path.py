@@ -149,3 +149,38 @@ def test_worker_mean_fast_path(orc, grid, levels, K, dt):
     got = g.worker_mean([dev(x) for x in xs], dev(np.ascontiguousarray(Sw)), grid, levels, 31,
                         0, 0, off)
     assert np.array_equal(host(got), ref), first_diff(host(got), ref)
+
+
+@pytest.mark.parametrize("grid,levels,world,dt", [(U, 7, 16, "bf16"), (U, 127, 8, "f32"),
+                                                  (X, 7, 8, "f32"), (X, 7, 16, "bf16")])
+def test_wire_quantiser_fast_path(orc, grid, levels, world, dt):
+    """The wire payload's quantiser takes the same shortcut per part: payload bytes around the
+    threshold equal the oracle's encoding of its own levels."""
+    say("wire fast path", grid, levels, world, dt)
+    g = gq()
+    rng = np.random.default_rng(7000 + 10 * world + grid + levels)
+    n = 2 * 8192 + 999
+    S = np.float32(2.3)
+    if grid == U:
+        inv, bound = np.float32(np.float32(levels) / S), np.float32(1.0)
+    else:
+        inv, bound = np.float32(np.float32(1.0) / S), np.float32(2.0 ** (1 - levels))
+    thr = _threshold(inv, bound)
+    if dt == "bf16":
+        below, at = _bf16_below_at(thr)
+        above = np.array([np.array([at], np.float32).view(np.uint32)[0] + 0x10000],
+                         np.uint32).view(np.float32)[0]
+    else:
+        below, at = np.nextafter(thr, np.float32(0)), thr
+        above = np.nextafter(at, np.float32(np.inf))
+    x = (rng.standard_normal(n) * float(thr) * 0.05).astype(np.float32)
+    for i in rng.choice(n, 60, replace=False):
+        x[i] = below if rng.random() < 0.5 else -below
+    for i in rng.choice(n, 10, replace=False):
+        x[i] = rng.choice([at, above, -at, -above])
+    if dt == "bf16":
+        x = _to_bf16_bits(x)
+    q = orc.quantize(x, [S], grid, levels, 5, 3)
+    ref = orc.wire_encode(q, grid, levels, world)
+    got = g.quantize_wire(dev(x), dev(np.array([S], np.float32)), grid, levels, 5, 3, world)
+    assert np.array_equal(host(got), ref), first_diff(host(got), ref)
