@@ -379,6 +379,13 @@ __device__ __forceinline__ float seg_decode(float S, double denom) {
 // constant rounds monotonically, so every |x| below it has fl(|x| * inv) < bound.  Found from
 // the quotient by at most three one-ulp steps each way and verified at a and at the float
 // before it; 0 (which no |x| is below) if the verification fails.
+// The larger of m and |x| by IEEE 754-2019 maximum, which returns a NaN operand: a lane's largest
+// magnitude compared once against the threshold gives the same answer as comparing each
+// element (a NaN fails both ways), in one v_maximum3_f32 per two elements.
+__device__ __forceinline__ float max_abs(float m, float x) {
+  return __builtin_elementwise_maximum(m, fabsf(x));
+}
+
 __device__ __forceinline__ float below_bound(float inv, float bound) {
   uint32_t b = __float_as_uint(bound / inv);  // IEEE division, not negative
 #pragma unroll
@@ -776,10 +783,10 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
           float x[P];
           load_part<DT, P>(a.grad, e0, cnt, x);
           const uint32_t ctr = a.index_base + (uint32_t)e0;
-          bool lane_fast = true;
+          float big = 0.0f;  // a part's missing elements are loaded as zeros
 #pragma unroll
-          for (int e = 0; e < P; ++e) lane_fast &= fabsf(x[e]) < fast_below;
-          if (__all(lane_fast)) {
+          for (int e = 0; e < P; ++e) big = max_abs(big, x[e]);
+          if (__all(big < fast_below)) {
 #pragma unroll
             for (int e = 0; e < P; ++e) {
               const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
@@ -882,13 +889,15 @@ __device__ __forceinline__ void fused_compute(const FusedArgs &a, int k0, int kn
     const uint32_t km = a.key_mix[k0 + kb];
     bool fast = false;
     if constexpr (!STORE && FAST) {
-      bool lane_fast = true;
+      // parts past the end hold no elements and are left out; a part's missing elements
+      // are loaded as zeros
+      float big = 0.0f;
 #pragma unroll
       for (int j = 0; j < NP; ++j)
+        if (cnt[j] > 0)
 #pragma unroll
-        for (int e = 0; e < P; ++e)  // lanes past the end hold no elements: no condition
-          lane_fast &= cnt[j] <= 0 ? true : fabsf(x[kb][j].get(e)) < fast_below;
-      fast = __all(lane_fast);
+          for (int e = 0; e < P; ++e) big = max_abs(big, x[kb][j].get(e));
+      fast = __all(big < fast_below);
     }
     if (fast) {
 #pragma unroll
