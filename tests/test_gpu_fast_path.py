@@ -184,3 +184,75 @@ def test_wire_quantiser_fast_path(orc, grid, levels, world, dt):
     ref = orc.wire_encode(q, grid, levels, world)
     got = g.quantize_wire(dev(x), dev(np.array([S], np.float32)), grid, levels, 5, 3, world)
     assert np.array_equal(host(got), ref), first_diff(host(got), ref)
+
+
+
+# NaN (quiet and signalling patterns, either sign) and infinities; the NaN patterns keep their
+# mantissa bits in the upper half, so they stay NaN as bf16
+NONFINITE = np.array([0x7FC00000, 0xFFC00000, 0x7F810000, 0xFF810000, 0x7F800000, 0xFF800000],
+                     np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("grid,levels,bits,K,dt", [(U, 7, 4, 16, "bf16"), (X, 7, 4, 16, "bf16"),
+                                                   (X, 7, 4, 8, "f32"), (X, 7, 4, 3, "f32")])
+def test_nonfinite_element_in_a_small_batch(orc, grid, levels, bits, K, dt):
+    """Under a caller-given finite scale, a NaN or an infinity among values that all lie below
+    the threshold: the lane's largest magnitude must fail the threshold, so that its batch takes
+    the general path, which clamps the element to the top level as the oracle does; every other
+    batch stays on the fast path.  Sums and means bit-exact with the oracle."""
+    say("fast path non-finite", grid, levels, bits, K, dt)
+    g = gq()
+    rng = np.random.default_rng(9000 + 10 * K + grid)
+    n = 3 * 8192 + 77
+    S = np.float32(1.9)
+    inv = np.float32(np.float32(levels) / S) if grid == U else np.float32(np.float32(1.0) / S)
+    bound = np.float32(1.0) if grid == U else np.float32(2.0 ** (1 - levels))
+    thr = _threshold(inv, bound)
+    xs, xs0, planted = [], [], []
+    for k in range(K):
+        x = (rng.standard_normal(n) * float(thr) * 0.05).astype(np.float32)
+        x0 = x.copy()
+        if k % 2 == 1:  # three non-finite values in every other worker, in different chunks
+            for t, i in enumerate(rng.choice(n, 3, replace=False)):
+                x[i] = NONFINITE[(k + t) % len(NONFINITE)]
+                x0[i] = 0.0
+                planted.append(i)
+        xs.append(_to_bf16_bits(x) if dt == "bf16" else x)
+        xs0.append(_to_bf16_bits(x0) if dt == "bf16" else x0)
+    acc_bits = 16 if K * (levels if grid == U else 1 << (levels - 1)) < (1 << 15) else 32
+    ref = orc.allreduce_mean(xs, grid, levels, bits, acc_bits, 91, 0, scale=[S])
+    # each planted element takes the top level: its sum moves by s (or 2^(E-1)) against a zero
+    ref0 = orc.allreduce_mean(xs0, grid, levels, bits, acc_bits, 91, 0, scale=[S])
+    assert np.all(ref["sums"][planted] != ref0["sums"][planted])
+    xd = [dev(x) for x in xs]
+    Sd = dev(np.array([S], np.float32))
+    sd = torch.empty(n, dtype=torch.int16 if acc_bits == 16 else torch.int32, device="cuda")
+    g.fused_mean(xd, Sd, grid, levels, bits, 91, acc_bits, sums=sd)
+    assert np.array_equal(host(sd), ref["sums"]), first_diff(host(sd), ref["sums"])
+    mean = g.fused_mean(xd, Sd, grid, levels, bits, 91, acc_bits)
+    assert np.array_equal(host(mean), ref["mean"]), first_diff(host(mean), ref["mean"])
+
+
+@pytest.mark.parametrize("grid,world,dt", [(U, 16, "bf16"), (X, 8, "f32")])
+def test_wire_quantiser_nonfinite_element(orc, grid, world, dt):
+    """The wire payload's shortcut with a NaN or an infinity among small values (caller-given
+    finite scale): payload bytes equal the oracle's encoding of its levels."""
+    say("wire fast path non-finite", grid, world, dt)
+    g = gq()
+    levels = 7
+    rng = np.random.default_rng(9500 + world + grid)
+    n = 2 * 8192 + 333
+    S = np.float32(2.1)
+    inv = np.float32(np.float32(levels) / S) if grid == U else np.float32(np.float32(1.0) / S)
+    bound = np.float32(1.0) if grid == U else np.float32(2.0 ** (1 - levels))
+    thr = _threshold(inv, bound)
+    x = (rng.standard_normal(n) * float(thr) * 0.05).astype(np.float32)
+    pos = rng.choice(n, len(NONFINITE), replace=False)
+    x[pos] = NONFINITE
+    if dt == "bf16":
+        x = _to_bf16_bits(x)
+    q = orc.quantize(x, [S], grid, levels, 5, 3)
+    assert np.all(np.abs(q[pos]) == levels)  # the top level (index E on the exponential grid)
+    ref = orc.wire_encode(q, grid, levels, world)
+    got = g.quantize_wire(dev(x), dev(np.array([S], np.float32)), grid, levels, 5, 3, world)
+    assert np.array_equal(host(got), ref), first_diff(host(got), ref)
