@@ -876,13 +876,16 @@ __device__ __forceinline__ void fused_load(const FusedArgs &a, int k0, int kn,
         if (cnt[j] > 0) x[kb][j].load(a.grads[k0 + kb], e0[j], cnt[j]);
 }
 
-template <int DT, int GRID, int P, int NP, int KB, bool STORE, bool FAST>
+// FOLD: the fast path scales |x| by inv_up = inv * 2^32 (uniform) or inv * lo_scale
+// (exponential) in one product, which the caller has shown equal to scaling fl(|x| * inv).
+template <int DT, int GRID, int P, int NP, int KB, bool STORE, bool FAST, bool FOLD>
 __device__ __forceinline__ void fused_compute(const FusedArgs &a, int k0, int kn,
                                               const PartBuf<DT, P> (&x)[KB][NP],
                                               const int64_t (&e0)[NP], const int (&cnt)[NP],
                                               const uint32_t (&am)[NP][P], const SegQ &q,
                                               float sf, float lo_scale, float fast_below,
-                                              float (&accf)[NP][P], int32_t (&acci)[NP][P]) {
+                                              float inv_up, float (&accf)[NP][P],
+                                              int32_t (&acci)[NP][P]) {
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     if (kb >= kn) break;
@@ -906,14 +909,13 @@ __device__ __forceinline__ void fused_compute(const FusedArgs &a, int k0, int kn
         for (int e = 0; e < P; ++e) {
           const float xv = x[kb][j].get(e);
           const uint32_t h = fmix32_tail(am[j][e] ^ km);
-          const float tv = fabsf(xv) * q.inv;
-          if constexpr (GRID == 0) {
-            const uint32_t c = (uint32_t)ceilf(tv * 4294967296.0f);
+          const float up = FOLD ? fabsf(xv) * inv_up
+                                : fabsf(xv) * q.inv * (GRID == 0 ? 4294967296.0f : lo_scale);
+          const uint32_t c = (uint32_t)ceilf(up);
+          if constexpr (GRID == 0)
             accf[j][e] += h < c ? copysignf(1.0f, xv) : 0.0f;
-          } else {
-            const uint32_t c = (uint32_t)ceilf(tv * lo_scale);
+          else
             acci[j][e] += h < c ? (xv < 0.0f ? -1 : 1) : 0;
-          }
         }
       continue;
     }
@@ -948,8 +950,9 @@ __device__ __forceinline__ void fused_batch(const FusedArgs &a, int k0, int kn,
                                             float (&accf)[NP][P], int32_t (&acci)[NP][P]) {
   PartBuf<DT, P> x[KB][NP];
   fused_load<DT, P, NP, KB>(a, k0, kn, e0, cnt, x);
-  fused_compute<DT, GRID, P, NP, KB, STORE, GRID == 1>(a, k0, kn, x, e0, cnt, am, q, sf,
-                                                       lo_scale, fast_below, accf, acci);
+  fused_compute<DT, GRID, P, NP, KB, STORE, GRID == 1, false>(a, k0, kn, x, e0, cnt, am, q, sf,
+                                                              lo_scale, fast_below, 0.0f, accf,
+                                                              acci);
 }
 
 // Without the code stores both grids fit in 128 VGPRs (4 waves per SIMD, enough loads in
@@ -981,8 +984,17 @@ void k_fused(FusedArgs a) {
     const float S = a.scale[seg];
     const SegQ q = seg_quant<GRID>(S, a.levels);
     const float f = seg_decode(S, a.denom);
+    // In the double-buffered pass the fast path scales |x| by inv_up = inv * 2^32 (or
+    // inv * lo_scale) in one product.  Below the threshold fl(|x| * inv) < 1, and scaling it by
+    // that power of two is exact, so the one product equals it whenever fl(|x| * inv) is a
+    // normal number; when it is subnormal both ceilings are 1 (products below 2^-126 * 2^(E+31)
+    // <= 1, hence E <= 95), and they differ only if fl(|x| * inv) underflows to zero for a
+    // nonzero x, which inv >= 2^-16 rules out for bf16 (whose smallest magnitude is 2^-133).
+    // A tile whose scale fails these conditions takes the general path throughout.
+    const float inv_up = q.inv * (GRID == 0 ? 4294967296.0f : lo_scale);
+    const bool fold_ok = q.inv >= 0x1p-16f && inv_up < 0x1p127f && (GRID == 0 || a.levels <= 95);
     const float fast_below =
-        q.valid && (GRID == 1 || PIPE)
+        q.valid && (GRID == 1 || PIPE) && (!PIPE || fold_ok)
             ? below_bound(q.inv, GRID == 1 ? ldexpf(1.0f, 1 - a.levels) : 1.0f)
             : 0.0f;
     const int nch = (len + kChunk - 1) / kChunk;
@@ -1010,16 +1022,20 @@ void k_fused(FusedArgs a) {
           PartBuf<DT, P> xa[4][NP], xb[4][NP];
           fused_load<DT, P, NP, 4>(a, 0, 4, e0, cnt, xa);
           fused_load<DT, P, NP, 4>(a, 4, 4, e0, cnt, xb);
-          fused_compute<DT, GRID, P, NP, 4, STORE, true>(a, 0, 4, xa, e0, cnt, am, q, sf,
-                                                               lo_scale, fast_below, accf, acci);
+          fused_compute<DT, GRID, P, NP, 4, STORE, true, true>(a, 0, 4, xa, e0, cnt, am, q,
+                                                                     sf, lo_scale, fast_below,
+                                                                     inv_up, accf, acci);
           fused_load<DT, P, NP, 4>(a, 8, 4, e0, cnt, xa);
-          fused_compute<DT, GRID, P, NP, 4, STORE, true>(a, 4, 4, xb, e0, cnt, am, q, sf,
-                                                               lo_scale, fast_below, accf, acci);
+          fused_compute<DT, GRID, P, NP, 4, STORE, true, true>(a, 4, 4, xb, e0, cnt, am, q,
+                                                                     sf, lo_scale, fast_below,
+                                                                     inv_up, accf, acci);
           fused_load<DT, P, NP, 4>(a, 12, 4, e0, cnt, xb);
-          fused_compute<DT, GRID, P, NP, 4, STORE, true>(a, 8, 4, xa, e0, cnt, am, q, sf,
-                                                               lo_scale, fast_below, accf, acci);
-          fused_compute<DT, GRID, P, NP, 4, STORE, true>(a, 12, 4, xb, e0, cnt, am, q, sf,
-                                                               lo_scale, fast_below, accf, acci);
+          fused_compute<DT, GRID, P, NP, 4, STORE, true, true>(a, 8, 4, xa, e0, cnt, am, q,
+                                                                     sf, lo_scale, fast_below,
+                                                                     inv_up, accf, acci);
+          fused_compute<DT, GRID, P, NP, 4, STORE, true, true>(a, 12, 4, xb, e0, cnt, am, q,
+                                                                     sf, lo_scale, fast_below,
+                                                                     inv_up, accf, acci);
         } else if constexpr (KT > 0) {
 #pragma unroll 1
           for (int k0 = 0; k0 < KT; k0 += KB)

@@ -256,3 +256,42 @@ def test_wire_quantiser_nonfinite_element(orc, grid, world, dt):
     ref = orc.wire_encode(q, grid, levels, world)
     got = g.quantize_wire(dev(x), dev(np.array([S], np.float32)), grid, levels, 5, 3, world)
     assert np.array_equal(host(got), ref), first_diff(host(got), ref)
+
+
+@pytest.mark.parametrize("grid,levels,bits", [(U, 7, 4), (X, 7, 4)])
+@pytest.mark.parametrize("side", ["above", "below"])
+def test_folded_product_at_its_scale_limit(orc, grid, levels, bits, side):
+    """The 16-worker bf16 pass multiplies |x| once by the scaled inverse (inv * 2^32, or
+    inv * 2^(E+31)) on the fast path, which it takes only while inv >= 2^-16, so that no
+    nonzero bf16 value (the smallest is 2^-133) has a product fl(|x| * inv) that underflows to
+    zero.  Scales that put inv just above that limit (fast path with subnormal products for the
+    bf16 subnormals planted here) and just below it (general path) give the oracle's sums and
+    means bit for bit."""
+    say("folded product limit", grid, levels, side)
+    g = gq()
+    K = 16
+    rng = np.random.default_rng(9900 + grid + (side == "below"))
+    n = 2 * 8192 + 4099
+    num = np.float32(levels if grid == U else 1.0)
+    S = np.float32(num * np.float32(2.0 ** 16))  # inv = num / S = 2^-16 exactly
+    S = np.nextafter(S, np.float32(0)) if side == "above" else np.nextafter(S, np.float32(np.inf))
+    inv = np.float32(num / S)
+    assert (inv >= np.float32(2.0 ** -16)) == (side == "above")
+    xs = []
+    for k in range(K):
+        x = (rng.standard_normal(n) * float(S) * 1e-3).astype(np.float32)
+        x[rng.random(n) < 0.05] = 0.0
+        bits16 = (x.view(np.uint32) >> 16).astype(np.uint16)
+        sub = rng.random(n) < 0.05  # bf16 subnormals of either sign, down to 2^-133
+        bits16[sub] = (rng.integers(1, 0x80, sub.sum()) | (rng.integers(0, 2, sub.sum()) << 15))
+        xs.append(bits16.astype(np.uint16))
+    acc_bits = 16 if K * (levels if grid == U else 1 << (levels - 1)) < (1 << 15) else 32
+    ref = orc.allreduce_mean(xs, grid, levels, bits, acc_bits, 123, 5, scale=[S])
+    assert np.any(ref["sums"] != 0)
+    xd = [dev(x) for x in xs]
+    Sd = dev(np.array([S], np.float32))
+    sd = torch.empty(n, dtype=torch.int16 if acc_bits == 16 else torch.int32, device="cuda")
+    g.fused_mean(xd, Sd, grid, levels, bits, 123, acc_bits, index_base=5, sums=sd)
+    assert np.array_equal(host(sd), ref["sums"]), first_diff(host(sd), ref["sums"])
+    mean = g.fused_mean(xd, Sd, grid, levels, bits, 123, acc_bits, index_base=5)
+    assert np.array_equal(host(mean), ref["mean"]), first_diff(host(mean), ref["mean"])
