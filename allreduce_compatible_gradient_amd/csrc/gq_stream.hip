@@ -768,8 +768,13 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
     // the fused pass's fast path: a part whose elements, in every active lane, lie below the
     // lowest nonzero level has levels 0 and +-1 only (bit for bit the general path's)
     const float bound = GRID == 0 ? 1.0f : ldexpf(1.0f, 1 - a.levels);
-    const float fast_below = q.valid ? below_bound(q.inv, bound) : 0.0f;
     const float up_scale = GRID == 0 ? 4294967296.0f : lo_scale;
+    // bf16: |x| scaled by inv_up = inv * up_scale in one product, exact under the conditions
+    // k_fused's double-buffered pass states (a tile outside them takes the general path)
+    const float inv_up = q.inv * up_scale;
+    const bool fold_ok =
+        DT == 0 || (q.inv >= 0x1p-16f && inv_up < 0x1p127f && (GRID == 0 || a.levels <= 95));
+    const float fast_below = q.valid && fold_ok ? below_bound(q.inv, bound) : 0.0f;
     const int nch = (len + kChunk - 1) / kChunk;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
 #pragma unroll
@@ -790,7 +795,8 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
 #pragma unroll
             for (int e = 0; e < P; ++e) {
               const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
-              const uint32_t c = (uint32_t)ceilf(fabsf(x[e]) * q.inv * up_scale);
+              const float up = DT == 1 ? fabsf(x[e]) * inv_up : fabsf(x[e]) * q.inv * up_scale;
+              const uint32_t c = (uint32_t)ceilf(up);
               const int32_t lin = h < c ? (x[e] < 0.0f ? -1 : 1) : 0;
               v[e] = (uint32_t)(lin + a.offset);
             }

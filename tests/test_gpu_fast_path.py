@@ -295,3 +295,8 @@ def test_folded_product_at_its_scale_limit(orc, grid, levels, bits, side):
     assert np.array_equal(host(sd), ref["sums"]), first_diff(host(sd), ref["sums"])
     mean = g.fused_mean(xd, Sd, grid, levels, bits, 123, acc_bits, index_base=5)
     assert np.array_equal(host(mean), ref["mean"]), first_diff(host(mean), ref["mean"])
+    # the wire payload's quantiser takes the same one-product scaling for bf16 under the same limit
+    q = orc.quantize(xs[3], [S], grid, levels, 123, 3, index_base=5)
+    wref = orc.wire_encode(q, grid, levels, K)
+    wgot = g.quantize_wire(xd[3], Sd, grid, levels, 123, 3, K, index_base=5)
+    assert np.array_equal(host(wgot), wref), first_diff(host(wgot), wref)
