@@ -976,8 +976,8 @@ void k_fused(FusedArgs a) {
   constexpr int KB = FASTP && (KT == 0 || KT > 4) ? 4 : (KT == 16 ? 8 : (KT > 0 ? KT : 4));
   // bf16, 16 workers, no code stores: four batches of 4 workers, double-buffered so that the
   // next batch's loads are in flight while the current one is quantised, with the fast path on
-  // both grids (GPT-2's buckets: 1.158 -> 0.946 ms from the double buffering, -> 0.875 ms with
-  // the uniform grid's fast path)
+  // both grids (GPT-2's buckets: 1.158 -> 0.946 ms from the double buffering, -> 0.84 ms with
+  // the uniform grid's fast path, its per-lane maximum vote and one-product scaling)
   constexpr bool PIPE = !STORE && DT == 1 && KT == 16;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int K = KT > 0 ? KT : a.K;
