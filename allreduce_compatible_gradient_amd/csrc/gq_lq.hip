@@ -276,23 +276,32 @@ __device__ __forceinline__ double rsqrt_refined(double d) {
 }
 
 // Upper-triangular T with (P T)^T (P T) = I given G = P^T P, column by column as Gram-Schmidt
-// does it, through the Cholesky factor: G = R^T R (R upper triangular; a pivot below 2^-32 of
-// the column's squared norm marks a column with no remaining norm of its own -- zero, or a
-// combination of the earlier columns up to fp32 rounding -- whose row of R and column of T
-// are zero), and T = R^-1 from T R = I: T[a][c] = (delta_ac - sum_{k<c} T[a][k] R[k][c]) / R[c][c].
+// does it, through the Cholesky factor G = R^T R (R upper triangular), and T = R^-1 from
+// T R = I: T[a][c] = (delta_ac - sum_{k<c} T[a][k] R[k][c]) / R[c][c].
+// Dependent columns: R[c][c] is the norm column c keeps after the projections, and
+// a_j = sum_{k<c} T[j][k] R[k][c] are its coefficients on the earlier columns.  If rounding
+// moved every column by a relative amount rho, that remainder would move by at most
+// rho (|p_c| + sum_j |a_j| |p_j|); with rho = sqrt(m) 2^-24, the rounding of an fp32 sum of
+// m products (the entries of P = M Q), a column whose R[c][c] is within that bound has no
+// direction of its own that fp32 resolves, and its row of R and column of T are zero.
+// rho2 = rho^2 is compared with the squares (R[c][c]^2 against rho2 * bound^2).
 // Spread over the lanes of one wave: lane j (< RANK) holds column j of G (g[k] = G[k][j]) and
 // of R, and row j of T.  Step c reads column c of R from lane c with v_readlane (uniform
 // values); with it every lane forms its own entries of row c of R and of column c of T, so T
-// needs no exchange at all.  Products accumulate by fused multiply-add in fp64.
+// needs no exchange at all; the c terms |a_j| |p_j| of the bound are read from lanes 0..c-1.
+// Products accumulate by fused multiply-add in fp64.
 template <int RANK>
-__device__ __forceinline__ void lane_cholqr_T(const double (&g)[RANK], int j,
+__device__ __forceinline__ void lane_cholqr_T(const double (&g)[RANK], int j, double rho2,
                                               double (&trow)[RANK]) {
   double rcol[RANK];  // R[k][j]
+  double gjj = 0.0;   // G[j][j]
 #pragma unroll
   for (int k = 0; k < RANK; ++k) {
     rcol[k] = 0.0;
     trow[k] = 0.0;
+    if (k == j) gjj = g[k];
   }
+  const double pj = sqrt(gjj);  // |p_j|
 #pragma unroll
   for (int c = 0; c < RANK; ++c) {
     double rkc[RANK > 1 ? RANK - 1 : 1];  // R[k][c], k < c
@@ -302,16 +311,20 @@ __device__ __forceinline__ void lane_cholqr_T(const double (&g)[RANK], int j,
     double d = gcc;
 #pragma unroll
     for (int k = 0; k < c; ++k) d = fma(-rkc[k], rkc[k], d);
-    // less than 2^-32 of the squared norm left: dependent on the earlier columns, set to zero
-    if (d > 0x1p-32 * gcc) {  // the same value in every lane
-      const double inv = rsqrt_refined(d), rc = d * inv;
-      double v = g[c];  // G[c][j]
-      double u = j == c ? 1.0 : 0.0;
+    double v = g[c];  // G[c][j]
+    double u = j == c ? 1.0 : 0.0;
 #pragma unroll
-      for (int k = 0; k < c; ++k) {
-        v = fma(-rkc[k], rcol[k], v);
-        u = fma(-trow[k], rkc[k], u);  // T[j][k] R[k][c]; T[j][k] = 0 for k < j
-      }
+    for (int k = 0; k < c; ++k) {
+      v = fma(-rkc[k], rcol[k], v);
+      u = fma(-trow[k], rkc[k], u);  // T[j][k] R[k][c]; T[j][k] = 0 for k < j
+    }
+    // lane j < c: u = -a_j; the bound |p_c| + sum_{j<c} |a_j| |p_j| in lane order
+    const double term = fabs(u) * pj;
+    double bound = sqrt(gcc);
+#pragma unroll
+    for (int k = 0; k < c; ++k) bound += readlane_d(term, k);
+    if (d > rho2 * bound * bound) {  // the same value in every lane
+      const double inv = rsqrt_refined(d), rc = d * inv;
       if (j > c) rcol[c] = v * inv;
       if (j == c) rcol[c] = rc;
       trow[c] = u * inv;
@@ -326,7 +339,8 @@ template <int RANK>
 __global__ __launch_bounds__(solve_block<RANK>()) void k_lq_solve(const double *__restrict__ gpart_all,
                                                           int64_t nblocks,
                                                           double *__restrict__ T_all,
-                                                          unsigned *__restrict__ cmax_all) {
+                                                          unsigned *__restrict__ cmax_all,
+                                                          double rho2) {
   constexpr int NG = RANK * (RANK + 1) / 2;
   const int wk = blockIdx.x;
   const double *__restrict__ gpart = gpart_all + (int64_t)wk * NG * nblocks;
@@ -377,7 +391,7 @@ __global__ __launch_bounds__(solve_block<RANK>()) void k_lq_solve(const double *
     double g[RANK], t1[RANK];
 #pragma unroll
     for (int k = 0; k < RANK; ++k) g[k] = Gs[k][jc];
-    lane_cholqr_T<RANK>(g, jc, t1);
+    lane_cholqr_T<RANK>(g, jc, rho2, t1);
     if (lane < RANK)
 #pragma unroll
       for (int k = 0; k < RANK; ++k) T1s[lane][k] = t1[k];
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(solve_block<RANK>()) void k_lq_solve(const double *
       g[c] = sum;
     }
     double t2[RANK];
-    lane_cholqr_T<RANK>(g, jc, t2);
+    lane_cholqr_T<RANK>(g, jc, rho2, t2);
     if (lane < RANK)
 #pragma unroll
       for (int k = 0; k < RANK; ++k) T2s[lane][k] = t2[k];
@@ -964,7 +978,7 @@ void launch_step(const StepIO &io, const StepBufs &b, const LqTables &tp, const 
     hipLaunchKernelGGL((k_lq_ef_mq<RANK, VEC, false>), dim3((unsigned)b.nblocks, K),
                        dim3(kBlockA), 0, s, io.W, b.P, b.gpart, n, m);
   hipLaunchKernelGGL((k_lq_solve<RANK>), dim3(K), dim3(solve_block<RANK>()), 0, s, b.gpart,
-                     b.nblocks, b.T, b.cmax_bits);
+                     b.nblocks, b.T, b.cmax_bits, (double)m * 0x1p-48);
   const dim3 gcol((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)b.nchunks, K);
   if (b.rows_chunk == 64)
     hipLaunchKernelGGL((k_lq_mtp<RANK, VEC, 64>), gcol, dim3(kWavesC * 64), 0, s, io.W, b.P,

@@ -400,10 +400,9 @@ __device__ __forceinline__ float below_bound(float inv, float bound) {
 }
 
 // ---------------------------------------------------------------- element quantisers
-// The sign of a level: the uniform grid applies sign(x) as copysign does and the exponential
-// grid as the comparison x < 0; they differ only for a NaN element under a caller-given finite
-// scale (clamped to the top level), which keeps its sign bit on the uniform grid and counts
-// as positive on the exponential one -- each the form its kernel computes at no extra cost.
+// The sign of a level is the sign bit of x on both grids (IEEE 754's signBit, the sign that
+// copysign transfers): a NaN element under a caller-given finite scale, clamped to the top
+// level, keeps the sign its bit gives it, and -0 has level 0, which carries no sign.
 // Uniform grid.  Returns the level magnitude m in [0, s] as a float (exact small integer);
 // the signed level is copysign(m, x).
 __device__ __forceinline__ float quant_uniform_mag(float x, float inv, float sf, uint32_t h) {
@@ -436,15 +435,24 @@ __device__ __forceinline__ uint32_t uniform_code(float m, float x, int bits) {
   return (uint32_t)(int32_t)copysignf(m, x) & ((1u << bits) - 1u);
 }
 
-// Code field of an exponential index: sign bit above j (zero has no sign).
+// x's sign bit as a condition (an integer comparison of the bit pattern, so a NaN or -0 keeps
+// the sign its bit gives it).
+__device__ __forceinline__ bool sign_bit(float x) { return (int32_t)__float_as_uint(x) < 0; }
+
+// Code field of an exponential index: x's sign bit above j (zero has no sign).
 __device__ __forceinline__ uint32_t exp_code(uint32_t j, float x, int bits) {
-  return ((x < 0.0f && j > 0) ? (1u << (bits - 1)) : 0u) | j;
+  return ((sign_bit(x) && j > 0) ? (1u << (bits - 1)) : 0u) | j;
 }
 
 // Signed integer value on the common grid of an exponential index: sign * 2^(j-1), 0 for j = 0.
 __device__ __forceinline__ int32_t exp_lin(uint32_t j, bool neg) {
   const int32_t v = (int32_t)((1u << j) >> 1);
   return neg ? -v : v;
+}
+
+// The same with the sign taken from x's sign bit.
+__device__ __forceinline__ int32_t exp_lin_of(uint32_t j, float x) {
+  return exp_lin(j, sign_bit(x));
 }
 
 template <int GRID>
@@ -810,7 +818,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
             if constexpr (GRID == 0)
               lin = (int32_t)copysignf(quant_uniform_mag(x[e], q.inv, sf, h), x[e]);
             else
-              lin = exp_lin(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e] < 0.0f);
+              lin = exp_lin_of(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e]);
             v[e] = (uint32_t)(lin + a.offset);
           }
         } else {
@@ -938,7 +946,7 @@ __device__ __forceinline__ void fused_compute(const FusedArgs &a, int k0, int kn
           if constexpr (STORE) c[e] = uniform_code(m, xv, a.bits);
         } else {
           const uint32_t jj = quant_exp_index(xv, q.inv, a.levels, lo_scale, h);
-          acci[j][e] += exp_lin(jj, xv < 0.0f);
+          acci[j][e] += exp_lin_of(jj, xv);
           if constexpr (STORE) c[e] = exp_code(jj, xv, a.bits);
         }
       }
@@ -1218,7 +1226,7 @@ __device__ __forceinline__ void worker_compute(const WorkerMeanArgs &a, int k0, 
         if constexpr (GRID == 0)
           l = copysignf(quant_uniform_mag(xv, inv, sf, h), xv);
         else
-          l = (float)exp_lin(quant_exp_index(xv, inv, a.levels, lo_scale, h), xv < 0.0f);
+          l = (float)exp_lin_of(quant_exp_index(xv, inv, a.levels, lo_scale, h), xv);
         acc[j][e] = fmaf(l, fac, acc[j][e]);  // one rounding per worker, in worker order
       }
   }

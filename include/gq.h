@@ -91,8 +91,10 @@ gq_status gq_global_norm(gq_ctx *ctx, const void *const *grads, int32_t K, int32
  *                level_j <= u (level_0 = 0, level_j = 2^(j-E)); p = (u - level_j) /
  *                (level_{j+1} - level_j); j <- j + [r < p]; code = sign bit << (bits-1) | j
  * where r = fmix32((index_base + i) XOR key_k) * 2^-32 and key_k is the low 32 bits of
- * SplitMix64 output k+1 from state `seed`.  A segment whose scale is not a positive finite
- * number (or whose inv_g overflows) gets all-zero codes.  Element 2t of a 4-bit buffer sits in
+ * SplitMix64 output k+1 from state `seed`; sign(x) is x's sign bit on both grids, so a NaN
+ * element (possible only under a caller-given finite scale) takes the top level with the sign
+ * its bit gives it.  A segment whose scale is not a positive finite number (or whose inv_g
+ * overflows) gets all-zero codes.  Element 2t of a 4-bit buffer sits in
  * the low nibble of byte t; an odd tail leaves the high nibble 0.
  *   grad    n elements of `dtype`;  scale nseg fp32 (device);  worker = k
  *   codes   n bytes (bits = 8) or ceil(n/2) bytes (bits = 4)

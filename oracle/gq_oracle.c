@@ -199,7 +199,7 @@ static int32_t quant_exp(int32_t E, float x, float S, uint32_t key, uint32_t cou
     r = orc_uniform(key, counter);
     if (r < p)
         j += 1;
-    return (x < 0.0f && j > 0) ? -j : j; /* a NaN counts as positive here */
+    return (signbit(x) && j > 0) ? -j : j; /* the sign bit, as on the uniform grid */
 }
 
 int32_t orc_quant_one(int32_t grid, int32_t levels, float x, float S, uint32_t key,
@@ -580,33 +580,67 @@ void orc_logquant(const float *F, int64_t rows, int32_t r, double alpha, int32_t
 }
 
 /* [LQ] referee major comment 1: Q is computed from P after P is orthonormalised.  Modified
- * Gram-Schmidt over columns 0..r-1 in order, all arithmetic in fp64.  The pages give no rule
- * for a column that depends on the earlier ones; reading: if the projections leave less than
- * 2^-16 of its norm (squared: 2^-32), what is left is rounding of the fp32 factor, not a
- * direction, and the column is set to zero (as one with no norm at all). */
-void orc_mgs(float *P, int64_t n, int32_t r)
+ * Gram-Schmidt over columns 0..r-1 in order, all arithmetic in fp64.
+ *
+ * The pages give no rule for a column that depends on the earlier ones.  Reading, from fp32
+ * arithmetic alone: column c keeps, after the projections, the part p_c - sum_j a_j p_j with
+ * a the coefficients of its projection on the earlier columns (a = R^-1 times column c of
+ * R, over the live earlier columns).  If every column were moved by a relative amount rho
+ * through rounding, that part would move by at most rho (|p_c| + sum_j |a_j| |p_j|) (triangle
+ * inequality), so a column exactly dependent in exact arithmetic can keep that much.  Each
+ * entry of P = M Q_prev is a sum of m products of fp32 values, whose rounding is of relative
+ * size sqrt(m) u for mixed signs (u = 2^-24, fp32's unit roundoff); so rho = sqrt(m) u, and a
+ * column whose remaining norm is at most rho (|p_c| + sum_j |a_j| |p_j|) has no direction of
+ * its own that fp32 resolves: it is set to zero like a column with no norm at all. */
+double orc_mgs_rho(int64_t m)
+{
+    return sqrt((double)m) * 0x1p-24;
+}
+
+void orc_mgs(float *P, int64_t n, int32_t r, int64_t m)
 {
     double *V = (double *)malloc((size_t)(n * r) * sizeof(double));
-    int32_t c, j;
+    double R[8][8], nrm0[8], a[8];
+    const double rho = orc_mgs_rho(m);
+    int32_t c, j, k;
     int64_t i;
     for (i = 0; i < n * r; ++i)
         V[i] = (double)P[i];
     for (c = 0; c < r; ++c) {
-        double nrm = 0.0, nrm0 = 0.0;
+        double nrm = 0.0, bound;
+        for (j = 0; j < r; ++j)
+            R[j][c] = 0.0;
+        nrm0[c] = 0.0;
         for (i = 0; i < n; ++i)
-            nrm0 += V[i * r + c] * V[i * r + c];
+            nrm0[c] += V[i * r + c] * V[i * r + c];
+        nrm0[c] = sqrt(nrm0[c]);
         for (j = 0; j < c; ++j) {
             double d = 0.0;
             for (i = 0; i < n; ++i)
                 d += V[i * r + j] * V[i * r + c];
             for (i = 0; i < n; ++i)
                 V[i * r + c] -= d * V[i * r + j];
+            R[j][c] = d;
         }
         for (i = 0; i < n; ++i)
             nrm += V[i * r + c] * V[i * r + c];
-        if (!(nrm > 0x1p-32 * nrm0))
-            nrm = 0.0;
         nrm = sqrt(nrm);
+        /* a = R[<c][<c]^-1 R[<c][c] by back substitution; a dead column (R[j][j] = 0) has
+         * a zero row in R and takes no part */
+        bound = nrm0[c];
+        for (j = c - 1; j >= 0; --j) {
+            a[j] = 0.0;
+            if (R[j][j] > 0.0) {
+                double t = R[j][c];
+                for (k = j + 1; k < c; ++k)
+                    t -= R[j][k] * a[k];
+                a[j] = t / R[j][j];
+            }
+            bound += fabs(a[j]) * nrm0[j];
+        }
+        if (!(nrm > rho * bound))
+            nrm = 0.0;
+        R[c][c] = nrm;
         for (i = 0; i < n; ++i)
             V[i * r + c] = nrm > 0.0 ? V[i * r + c] / nrm : 0.0;
     }
@@ -617,8 +651,8 @@ void orc_mgs(float *P, int64_t n, int32_t r)
 
 /* [LQ] "Core claim": one worker's compressor.  M = G + E is left in E; P = M Q_prev is
  * orthonormalised; Q' = M^T P; both factors are log-quantised (codes and maxima are the
- * worker's message, Ph and Qh their decoded values); Q <- Qh is the warm start of the next
- * step ("Q is warm-started from the previous iteration"). */
+ * worker's message, Ph and Qh their decoded values); Q <- Qh, the decoded Q, starts the next
+ * step's power iteration (the warm start of the "Core claim"). */
 static void lq_compress(const float *G, float *E, float *Q, int64_t n, int64_t m, int32_t r,
                         double alpha, int32_t bits_p, int32_t bits_q, int8_t *p_codes,
                         float *p_colmax, int8_t *q_codes, float *q_colmax, float *Ph, float *Qh,
@@ -642,7 +676,7 @@ static void lq_compress(const float *G, float *E, float *Q, int64_t n, int64_t m
                 acc += (double)E[i * m + j] * (double)Q[j * r + c];
             P[i * r + c] = (float)acc;
         }
-    orc_mgs(P, n, r);
+    orc_mgs(P, n, r, m);
 
     /* Q = M^T P: every Q[j][c] sums over i = 0..n-1 in order (rows outermost so that M is
      * read along its rows) */

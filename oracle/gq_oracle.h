@@ -68,7 +68,7 @@ int32_t orc_global_norm(const void *const *xs, int32_t K, int32_t dtype, int64_t
 /* Signed level of one element.  Uniform: value in [-s, s] (levels = s).
  * Exponential: sign * j with j in [0, E] (levels = E), level j>0 meaning 2^(j-E).
  * A NaN element (possible only under a caller-given finite scale) goes to the top level, with
- * the sign of its sign bit on the uniform grid and as positive on the exponential grid. */
+ * the sign of its sign bit (both grids). */
 int32_t orc_quant_one(int32_t grid, int32_t levels, float x, float S, uint32_t key,
                       uint32_t counter);
 /* Quantise a segmented buffer of one worker; counter of element i is index_base + i. */
@@ -158,11 +158,15 @@ float orc_logq_level(int32_t k, double alpha, int32_t L);
  * codes rows x r int8; colmax r fp32; Fhat rows x r (may be NULL). */
 void orc_logquant(const float *F, int64_t rows, int32_t r, double alpha, int32_t bits,
                   int8_t *codes, float *colmax, float *Fhat);
-/* Modified Gram-Schmidt on the columns of P (n x r, row-major, fp32 in and out), fp64 math.
- * A column whose norm after the projections is below 2^-16 of its norm before them is
- * numerically dependent on the earlier columns (the fp32 factor cannot resolve the
- * difference) and is set to zero, like a column that is exactly zero. */
-void orc_mgs(float *P, int64_t n, int32_t r);
+/* Relative rounding rho = sqrt(m) 2^-24 of an entry of P = M Q_prev that sums m products of
+ * fp32 values (the reading in gq_oracle.c). */
+double orc_mgs_rho(int64_t m);
+/* Modified Gram-Schmidt on the columns of P (n x r, r <= 8, row-major, fp32 in and out), fp64
+ * math; m is the number of products summed in each entry of P.  Column c is numerically
+ * dependent on the earlier ones, and set to zero like a column that is exactly zero, when the
+ * norm it keeps after the projections is at most rho (|p_c| + sum_j |a_j| |p_j|), rho =
+ * orc_mgs_rho(m), a the coefficients of its projection on the earlier columns. */
+void orc_mgs(float *P, int64_t n, int32_t r, int64_t m);
 /* One compressor step: M = G + E; P = M Qprev; P <- MGS(P); Q = M^T P; quantise P with
  * bits_p and Q with bits_q (the review's referee comment on Section V names b_p and b_q as
  * separate settings); E <- M - Phat Qhat^T; Qprev <- Qhat.  E and Q are updated in place.

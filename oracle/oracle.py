@@ -87,7 +87,8 @@ def lib():
             "orc_logq_index": (i32, [f, d, i32]),
             "orc_logq_level": (f, [i32, d, i32]),
             "orc_logquant": (None, [p, i64, i32, d, i32, p, p, p]),
-            "orc_mgs": (None, [p, i64, i32]),
+            "orc_mgs": (None, [p, i64, i32, i64]),
+            "orc_mgs_rho": (d, [i64]),
             "orc_powersgd_logquant": (None, [p, p, p, i64, i64, i32, d, i32, i32, p, p, p, p, p,
                                              p, p]),
             "orc_lq_step_workers": (None, [p, p, p, i32, i64, i64, i32, d, i32, i32, p, p, p, p,
@@ -351,10 +352,17 @@ def logquant(F, alpha, bits):
     return codes, colmax, Fhat
 
 
-def mgs(P):
+def mgs(P, m):
+    """Modified Gram-Schmidt of the oracle; m = the number of products summed in each entry
+    of P (the inner dimension of P = M Q_prev), which sets the dependent-column cut."""
     P = np.array(P, dtype=np.float32, order="C", copy=True)
-    lib().orc_mgs(_ptr(P), P.shape[0], P.shape[1])
+    lib().orc_mgs(_ptr(P), P.shape[0], P.shape[1], int(m))
     return P
+
+
+def mgs_rho(m):
+    """Relative rounding rho of an entry of P that sums m products: sqrt(m) 2^-24."""
+    return lib().orc_mgs_rho(int(m))
 
 
 def powersgd_logquant(G, E, Q, alpha, bits, bits_q=None):

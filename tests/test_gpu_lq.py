@@ -291,6 +291,56 @@ def test_step_rank_deficient_gradient(orc, n, m, r, rank):
     _check_step(ref, out, Eg, Qg, orthonormal=False)
 
 
+@pytest.mark.parametrize("ill", [False, True])
+def test_step_dependent_column_cut(orc, ill):
+    """The dependent-column rule on the GPU: with Q_prev = [I; 0] the factor P = M Q_prev is the
+    first three columns of M exactly, and the third is set to its neighbours' combination
+    (coefficients (1, 0.5), or (-49, 50) on nearly parallel neighbours) plus a part of its own
+    at 1.15, 0.87, 2 and 0.5 times the cut rho (|p_c| + sum_j |a_j| |p_j|), rho = sqrt(m) 2^-24:
+    kept (unit norm, orthogonal to the others) above the cut and zero below it, on both
+    sides."""
+    n, m, r = 400, 1024, 3
+    say("lq dependent column cut", ill)
+    rho = np.sqrt(m) * 2.0 ** -24
+    rng = np.random.default_rng(77 + ill)
+    coef = np.array((-49.0, 50.0) if ill else (1.0, 0.5))
+    Q = np.zeros((m, r), np.float32)
+    Q[:r, :r] = np.eye(r, dtype=np.float32)
+    for frac, kept in ((1.15, True), (0.87, False), (2.0, True), (0.5, False)):
+        A = rng.standard_normal((n, 2))
+        if ill:
+            A[:, 1] = A[:, 0] + 0.01 * rng.standard_normal(n)
+        A = A.astype(np.float32).astype(np.float64)
+        w = rng.standard_normal(n)
+        qa, _ = np.linalg.qr(A)
+        w -= qa @ (qa.T @ w)
+        w /= np.linalg.norm(w)
+        base = A @ coef
+        bound = np.linalg.norm(base) + np.sum(np.abs(coef) * np.linalg.norm(A, axis=0))
+        G = (rng.standard_normal((n, m)) * 1e-3).astype(np.float32)
+        G[:, :2] = A
+        G[:, 2] = base + frac * rho * bound * w
+        P = G[:, :3].astype(np.float64)
+        a, *_ = np.linalg.lstsq(P[:, :2], P[:, 2], rcond=None)
+        got_frac = np.linalg.norm(P[:, 2] - P[:, :2] @ a) / rho / (
+            np.linalg.norm(P[:, 2]) + np.sum(np.abs(a) * np.linalg.norm(P[:, :2], axis=0)))
+        assert abs(got_frac / frac - 1.0) < 0.04, got_frac
+        E = np.zeros((n, m), np.float32)
+        ref, out, Eg, Qg = _step_both(orc, G, E, Q)
+        P_pre = host(out["p_pre"]).astype(np.float64)
+        # the orthonormal factor of nearly parallel columns amplifies fp32 rounding by their
+        # condition number (about 100 here)
+        tol = 1e-5 * max(1.0, np.linalg.cond(P[:, :2]) / 10.0)
+        if kept:
+            assert ref["P_pre"][:, 2].any()
+            assert np.abs(P_pre.T @ P_pre - np.eye(3)).max() < tol
+        else:
+            assert not ref["P_pre"][:, 2].any()
+            assert not P_pre[:, 2].any()
+            assert np.abs(P_pre[:, :2].T @ P_pre[:, :2] - np.eye(2)).max() < tol
+        assert _rel(P_pre, ref["P_pre"]) < tol
+
+
 @pytest.mark.parametrize("n,m,r", [(5, 6, 7), (3, 9, 4), (9, 2, 3), (1, 1, 1)])
 def test_step_fewer_rows_than_rank(orc, n, m, r):
     """n or m below r: at most min(n, m) columns of P can be independent; the others are

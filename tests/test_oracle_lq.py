@@ -98,7 +98,7 @@ def test_mgs_matches_householder_qr(orc):
     rng = np.random.default_rng(2)
     for n, r in ((64, 1), (500, 4), (1000, 7)):
         P = rng.standard_normal((n, r)).astype(np.float32)
-        got = orc.mgs(P)
+        got = orc.mgs(P, 1000)
         q, R = np.linalg.qr(P.astype(np.float64))
         q = q * np.sign(np.diag(R))
         assert np.abs(got - q).max() < 1e-6
@@ -109,7 +109,7 @@ def test_mgs_zero_column_stays_zero(orc):
     rng = np.random.default_rng(3)
     P = rng.standard_normal((50, 3)).astype(np.float32)
     P[:, 1] = 0
-    got = orc.mgs(P)
+    got = orc.mgs(P, 1000)
     assert not got[:, 1].any()
     assert abs(np.linalg.norm(got[:, 2].astype(np.float64)) - 1) < 1e-6
 
@@ -126,13 +126,71 @@ def test_mgs_dependent_columns_are_zero(orc):
     P[:, 3] = (P[:, 0] + P[:, 2]).astype(np.float32)  # dependent up to fp32 rounding
     W = rng.standard_normal(n)
     P[:, 4] = (P[:, 2] + 1e-3 * W).astype(np.float32)  # a small part of its own
-    got = orc.mgs(P).astype(np.float64)
+    got = orc.mgs(P, 1000).astype(np.float64)
     assert not got[:, 1].any() and not got[:, 3].any()
     live = [0, 2, 4, 5]
     assert np.abs(got[:, live].T @ got[:, live] - np.eye(4)).max() < 1e-6
     # the live columns span what the original ones span
     q, _ = np.linalg.qr(P[:, live].astype(np.float64))
     assert np.abs(got[:, live] - q @ (q.T @ got[:, live])).max() < 1e-6
+
+
+def _bound_and_rest(P):
+    """For the last column of an fp32 P (taken exactly in fp64): the norm it keeps after
+    projecting out the earlier columns, and |p_c| + sum_j |a_j| |p_j| with a its coefficients
+    on the earlier columns."""
+    P64 = P.astype(np.float64)
+    A, c = P64[:, :-1], P64[:, -1]
+    a, *_ = np.linalg.lstsq(A, c, rcond=None)
+    rest = np.linalg.norm(c - A @ a)
+    bound = np.linalg.norm(c) + np.sum(np.abs(a) * np.linalg.norm(A, axis=0))
+    return rest, bound
+
+
+def _column_at(rng, n, coef, frac, rho, ill=False):
+    """fp32 columns p_0, p_1 and p_2 = coef_0 p_0 + coef_1 p_1 + t w, w orthogonal to p_0 and
+    p_1, with t = frac * rho * (|p_2| + |coef_0| |p_0| + |coef_1| |p_1|).  ill: p_1 = p_0 plus
+    1/100 of a direction of its own (nearly parallel earlier columns)."""
+    A = rng.standard_normal((n, 2))
+    if ill:
+        A[:, 1] = A[:, 0] + 0.01 * rng.standard_normal(n)
+    A = A.astype(np.float32).astype(np.float64)
+    w = rng.standard_normal(n)
+    qa, _ = np.linalg.qr(A)
+    w -= qa @ (qa.T @ w)
+    w /= np.linalg.norm(w)
+    base = A @ np.asarray(coef, np.float64)
+    bound = np.linalg.norm(base) + np.sum(np.abs(coef) * np.linalg.norm(A, axis=0))
+    P = np.empty((n, 3), np.float32)
+    P[:, :2] = A
+    P[:, 2] = base + frac * rho * bound * w
+    rest, bound = _bound_and_rest(P)
+    return P, rest / (rho * bound)
+
+
+@pytest.mark.parametrize("m", [1024, 11008])
+@pytest.mark.parametrize("ill", [False, True])
+def test_mgs_cut_from_fp32_rounding(orc, m, ill):
+    """The dependent-column cut follows from fp32 arithmetic alone: a column whose remaining
+    norm is at most rho (|p_c| + sum_j |a_j| |p_j|), rho = sqrt(m) 2^-24, is set to zero and one
+    with a little more is kept -- with well-separated earlier columns (coefficients (1, 0.5))
+    and with nearly parallel ones (coefficients (-49, 50), where the bound is ~90 times the
+    column's own norm: a cut without the coefficient term would keep the column that must
+    go)."""
+    rho = np.sqrt(m) * 2.0 ** -24
+    assert orc.mgs_rho(m) == rho
+    rng = np.random.default_rng(m + ill)
+    coef = (-49.0, 50.0) if ill else (1.0, 0.5)
+    for frac, kept in ((1.15, True), (0.87, False), (2.0, True), (0.5, False)):
+        P, ratio = _column_at(rng, 400, coef, frac, rho, ill)
+        assert abs(ratio / frac - 1.0) < 0.04, (ratio, frac)
+        got = orc.mgs(P, m).astype(np.float64)
+        if kept:
+            assert abs(np.linalg.norm(got[:, 2]) - 1.0) < 1e-6
+            assert np.abs(got.T @ got - np.eye(3)).max() < 1e-6
+        else:
+            assert not got[:, 2].any()
+            assert np.abs(got[:, :2].T @ got[:, :2] - np.eye(2)).max() < 1e-6
 
 
 def _step(orc, G, E, Q):

@@ -42,8 +42,8 @@ MUTATIONS = [
     ("uniform: sign dropped", "return signbit(x) ? -m : m;", "return m;"),
     ("uniform: a NaN counted as positive", "return signbit(x) ? -m : m;",
      "return x < 0.0f ? -m : m;"),
-    ("exponential: a NaN's sign bit kept", "return (x < 0.0f && j > 0) ? -j : j;",
-     "return (signbit(x) && j > 0) ? -j : j;"),
+    ("exponential: a NaN counted as positive", "return (signbit(x) && j > 0) ? -j : j;",
+     "return (x < 0.0f && j > 0) ? -j : j;"),
     ("uniform: counter without index base", "scale[g], key, index_base + (uint32_t)i);",
      "scale[g], key, (uint32_t)i);"),
     ("exponential: probability over the upper level", "p = ((double)u - lo) / (hi - lo);",
@@ -84,9 +84,15 @@ MUTATIONS = [
      "V[i * r + c] += d * V[i * r + j];"),
     ("Gram-Schmidt: no normalisation", "V[i * r + c] = nrm > 0.0 ? V[i * r + c] / nrm : 0.0;",
      "V[i * r + c] = V[i * r + c];"),
-    ("Gram-Schmidt: dependent columns kept", "        if (!(nrm > 0x1p-32 * nrm0))\n            nrm = 0.0;\n",
+    ("Gram-Schmidt: dependent columns kept", "        if (!(nrm > rho * bound))\n            nrm = 0.0;\n",
      "\n"),
-    ("power step: P not orthonormalised", "    orc_mgs(P, n, r);\n", "\n"),
+    ("Gram-Schmidt: one fixed cut for every product length", "return sqrt((double)m) * 0x1p-24;",
+     "return 0x1p-16;"),
+    ("Gram-Schmidt: cut without the earlier columns' coefficients",
+     "            bound += fabs(a[j]) * nrm0[j];\n", "\n"),
+    ("Gram-Schmidt: coefficients from the wrong row of R", "t -= R[j][k] * a[k];",
+     "t -= R[k][j] * a[k];"),
+    ("power step: P not orthonormalised", "    orc_mgs(P, n, r, m);\n", "\n"),
     ("power step: no error fed back", "E[i] = G[i] + E[i];", "E[i] = G[i];"),
     ("power step: error of the wrong sign", "E[i * m + j] = (float)((double)E[i * m + j] - acc);",
      "E[i * m + j] = (float)((double)E[i * m + j] + acc);"),

@@ -461,9 +461,9 @@ def test_mean_is_unbiased_end_to_end(orc):
 
 
 def test_nan_goes_to_the_top_level(orc):
-    """Under a caller-given finite scale a NaN element is clamped to the top level, with its
-    sign bit's sign on the uniform grid and as positive on the exponential grid (the pages
-    say nothing of NaN: a reading)."""
+    """Under a caller-given finite scale a NaN element is clamped to the top level with the
+    sign its sign bit gives it, on both grids (the pages say nothing of NaN: a reading; the
+    sign bit is IEEE 754's sign of every value, NaN included)."""
     pos = np.float32(np.nan)
     neg = np.uint32(0xFFC00000).view(np.float32)
     x = np.array([pos, neg, 1.0, -1.0], np.float32)
@@ -471,4 +471,4 @@ def test_nan_goes_to_the_top_level(orc):
         q = _q(orc, x, 4.0, U, 31, seed)
         assert q[0] == 31 and q[1] == -31
         q = _q(orc, x, 4.0, X, 7, seed)
-        assert q[0] == 7 and q[1] == 7
+        assert q[0] == 7 and q[1] == -7
