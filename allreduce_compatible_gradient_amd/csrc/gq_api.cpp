@@ -3,8 +3,10 @@
 // Every call validates its arguments on the host first (nothing is enqueued on failure),
 // resolves the segment layout to a cached device tile table, derives the per-worker random
 // keys, and enqueues the kernels on the caller's stream.  No call synchronises except
-// gq_read_status and the rare scratch growth, which waits for the stream before freeing
-// the buffer it replaces.
+// gq_read_status, gq_trim and gq_destroy.  Device buffers a call has used (scratch, tables)
+// are never freed while the context lives unless the caller asks (gq_trim): a buffer replaced
+// by a larger one, or a table evicted from the cache, is retired, so that work still queued
+// and graphs captured from earlier calls keep valid pointers.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -40,6 +42,7 @@ struct gq_ctx {
   std::string err;
   void *scratch = nullptr;
   size_t scratch_bytes = 0;
+  std::vector<SegTable> retired;    // replaced scratch (dev only) and evicted tables
   unsigned *status = nullptr;       // device word: bit 0 = non-finite norm
   unsigned *status_host = nullptr;  // pinned
   std::map<std::pair<std::vector<int64_t>, int>, SegTable> segcache;  // (offsets, tile size)
@@ -83,20 +86,18 @@ uint32_t worker_key(uint64_t seed, uint32_t worker) {
 // the XOR of counter and key), so the kernels mix the counter once for all workers.
 uint32_t key_mix(uint32_t key) { return key ^ (key >> 16); }
 
-gq_status ensure_scratch(gq_ctx *c, size_t bytes, hipStream_t s) {
+gq_status ensure_scratch(gq_ctx *c, size_t bytes, hipStream_t) {
   if (bytes <= c->scratch_bytes) return GQ_OK;
-  if (c->scratch) {
-    hipError_t e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
-    (void)hipFree(c->scratch);
-    c->scratch = nullptr;
-    c->scratch_bytes = 0;
-  }
   size_t want = bytes < (1u << 20) ? (1u << 20) : bytes + bytes / 4;
-  if (hipMalloc(&c->scratch, want) != hipSuccess) {
-    c->scratch = nullptr;
+  void *fresh = nullptr;
+  if (hipMalloc(&fresh, want) != hipSuccess)
     return fail(c, GQ_ENOMEM, "scratch allocation of %zu bytes failed", want);
+  if (c->scratch) {
+    SegTable old;
+    old.dev = c->scratch;
+    c->retired.push_back(std::move(old));
   }
+  c->scratch = fresh;
   c->scratch_bytes = want;
   return GQ_OK;
 }
@@ -135,9 +136,7 @@ gq_status resolve_segments(gq_ctx *c, int64_t n, const int64_t *offsets, int32_t
   auto it = c->segcache.find(key);
   if (it == c->segcache.end()) {
     if (c->segcache.size() >= 64) {
-      hipError_t e = hipStreamSynchronize(s);
-      if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
-      for (auto &kv : c->segcache) (void)hipFree(kv.second.dev);
+      for (auto &kv : c->segcache) c->retired.push_back(std::move(kv.second));
       c->segcache.clear();
     }
     SegTable t;
@@ -252,9 +251,20 @@ GQ_EXPORT gq_status gq_create(gq_ctx **out) {
   return GQ_OK;
 }
 
+GQ_EXPORT gq_status gq_trim(gq_ctx *c) {
+  if (!c) return GQ_EINVAL;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(c, e, "hipDeviceSynchronize");
+  for (auto &t : c->retired) (void)hipFree(t.dev);
+  c->retired.clear();
+  gq::lq_trim(c->lq);
+  return GQ_OK;
+}
+
 GQ_EXPORT void gq_destroy(gq_ctx *c) {
   if (!c) return;
   (void)hipDeviceSynchronize();
+  for (auto &t : c->retired) (void)hipFree(t.dev);
   if (c->scratch) (void)hipFree(c->scratch);
   if (c->status) (void)hipFree(c->status);
   if (c->status_host) (void)hipHostFree(c->status_host);
@@ -662,7 +672,8 @@ GQ_EXPORT gq_status gq_lq_step_workers(gq_ctx *c, const float *const *G, float *
                                        float *const *Q, int32_t K, int64_t n, int64_t m, int32_t r,
                                        double alpha, int32_t bits_p, int32_t bits_q,
                                        int8_t *p_codes, float *p_colmax, int8_t *q_codes,
-                                       float *q_colmax, float *G_hat, void *stream) {
+                                       float *q_colmax, float *G_hat, float *p_pre_or_null,
+                                       float *q_pre_or_null, void *stream) {
   if (!c) return GQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K < 1 || K > gq::kLqMaxWorkers) return fail(c, GQ_EINVAL, "K = %d outside [1, %d]", K, gq::kLqMaxWorkers);
@@ -688,6 +699,8 @@ GQ_EXPORT gq_status gq_lq_step_workers(gq_ctx *c, const float *const *G, float *
   TRY(check_ptr(c, q_codes, "q_codes"));
   TRY(check_ptr(c, q_colmax, "q_colmax"));
   TRY(check_ptr(c, G_hat, "G_hat"));
+  if (p_pre_or_null) TRY(check_ptr(c, p_pre_or_null, "p_pre"));
+  if (q_pre_or_null) TRY(check_ptr(c, q_pre_or_null, "q_pre"));
   gq::LqWorkersStepArgs a;
   std::memset(&a, 0, sizeof a);
   for (int k = 0; k < K; ++k) {
@@ -707,6 +720,8 @@ GQ_EXPORT gq_status gq_lq_step_workers(gq_ctx *c, const float *const *G, float *
   a.q_codes = q_codes;
   a.q_colmax = q_colmax;
   a.G_hat = G_hat;
+  a.p_pre = p_pre_or_null;
+  a.q_pre = q_pre_or_null;
   hipError_t e = gq::lq_step_workers(c->lq, a, s);
   if (e == hipErrorOutOfMemory) return fail(c, GQ_ENOMEM, "LQ scratch allocation failed");
   return e == hipSuccess ? GQ_OK : hip_fail(c, e, "lq_step_workers launch");

@@ -29,9 +29,12 @@ struct LqTables {
   int L = 0;
 };
 
+// Scratch of the steps.  A buffer replaced by a larger one is retired, not freed: a captured
+// graph may still hold it; lq_trim frees the retired buffers.
 struct LqState {
   void *scratch = nullptr;
   size_t bytes = 0;
+  std::vector<void *> retired;
   std::map<std::pair<double, int>, LqTables> tables;
 };
 
@@ -66,12 +69,15 @@ struct LqWorkersStepArgs {
   int8_t *q_codes;   // K x m x r
   float *q_colmax;   // K x r
   float *G_hat;      // n x m
+  float *p_pre;      // K x n x r, or null: the orthonormalised P of every worker
+  float *q_pre;      // K x m x r, or null: every worker's Q' before quantisation
 };
 
 hipError_t lq_logquant(LqState &st, const float *F, int64_t rows, int r, double alpha, int bits,
                        int8_t *codes, float *colmax, float *Fhat, hipStream_t s);
 hipError_t lq_step(LqState &st, const LqStepArgs &a, hipStream_t s);
 hipError_t lq_step_workers(LqState &st, const LqWorkersStepArgs &a, hipStream_t s);
+void lq_trim(LqState &st);
 void lq_release(LqState &st);
 
 }  // namespace gq

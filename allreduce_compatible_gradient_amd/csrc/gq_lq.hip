@@ -895,21 +895,15 @@ __global__ __launch_bounds__(kBlockA) void k_lq_mean_ef(const LqWorkerPtrs W, in
 // ---------------------------------------------------------------- host helpers
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-hipError_t ensure(LqState &st, size_t bytes, hipStream_t s) {
+// Grow the scratch.  The buffer it replaces is retired, not freed: work already enqueued, or
+// a captured graph, may still use it (it is freed by lq_trim or lq_release).
+hipError_t ensure(LqState &st, size_t bytes, hipStream_t) {
   if (bytes <= st.bytes) return hipSuccess;
-  if (st.scratch) {
-    hipError_t e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return e;
-    (void)hipFree(st.scratch);
-    st.scratch = nullptr;
-    st.bytes = 0;
-  }
   const size_t want = bytes + bytes / 4;
-  hipError_t e = hipMalloc(&st.scratch, want);
-  if (e != hipSuccess) {
-    st.scratch = nullptr;
-    return hipErrorOutOfMemory;
-  }
+  void *fresh = nullptr;
+  if (hipMalloc(&fresh, want) != hipSuccess) return hipErrorOutOfMemory;
+  if (st.scratch) st.retired.push_back(st.scratch);
+  st.scratch = fresh;
   st.bytes = want;
   return hipSuccess;
 }
@@ -1116,10 +1110,18 @@ hipError_t lq_step_workers(LqState &st, const LqWorkersStepArgs &a, hipStream_t 
   io.p_colmax = a.p_colmax;
   io.q_colmax = a.q_colmax;
   io.G_hat = a.G_hat;
+  io.p_pre = a.p_pre;
+  io.q_pre = a.q_pre;
   return run_step(st, io, a.r, a.alpha, a.bits_p, a.bits_q, s);
 }
 
+void lq_trim(LqState &st) {
+  for (void *p : st.retired) (void)hipFree(p);
+  st.retired.clear();
+}
+
 void lq_release(LqState &st) {
+  lq_trim(st);
   if (st.scratch) (void)hipFree(st.scratch);
   st.scratch = nullptr;
   st.bytes = 0;

@@ -55,7 +55,8 @@ _SIGS = {
     "gq_powersgd_logquant": (_i32, [_p, _p, _p, _p, _i64, _i64, _i32, _d, _i32, _i32, _p, _p,
                                     _p, _p, _p, _p, _p, _p]),
     "gq_lq_step_workers": (_i32, [_p, _p, _p, _p, _i32, _i64, _i64, _i32, _d, _i32, _i32, _p,
-                                  _p, _p, _p, _p, _p]),
+                                  _p, _p, _p, _p, _p, _p, _p]),
+    "gq_trim": (_i32, [_p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -385,12 +386,13 @@ def powersgd_logquant(G, E, Q, alpha, bits, out=None, want_hat=True, want_pre=Fa
     return o
 
 
-def lq_step_workers(Gs, Es, Qs, alpha, bits, bits_q=None, out=None,
+def lq_step_workers(Gs, Es, Qs, alpha, bits, bits_q=None, out=None, want_pre=False,
                     ctx: Optional[Context] = None):
     """One LQ-SGD step of K workers (lists of n x m gradients, n x m errors and m x r warm
     starts; E's and Q's are updated in place).  Returns a dict with every worker's message
     stacked by worker (p_codes K x n x r, p_colmax K x r, q_codes K x m x r, q_colmax K x r)
-    and G_hat (n x m), the mean of the decoded messages."""
+    and G_hat (n x m), the mean of the decoded messages; with want_pre also every worker's
+    factors before quantisation (p_pre K x n x r, q_pre K x m x r)."""
     ctx = ctx or context()
     K = len(Gs)
     if not (len(Es) == K and len(Qs) == K):
@@ -409,6 +411,13 @@ def lq_step_workers(Gs, Es, Qs, alpha, bits, bits_q=None, out=None,
     o.setdefault("q_codes", torch.empty(K, m, r, dtype=torch.int8, device=dev))
     o.setdefault("q_colmax", torch.empty(K, r, dtype=torch.float32, device=dev))
     o.setdefault("G_hat", torch.empty(n, m, dtype=torch.float32, device=dev))
+    if want_pre:
+        o.setdefault("p_pre", torch.empty(K, n, r, dtype=torch.float32, device=dev))
+        o.setdefault("q_pre", torch.empty(K, m, r, dtype=torch.float32, device=dev))
+
+    def opt(k):
+        return None if o.get(k) is None else _dev(o[k], k, torch.float32)
+
     gp = _ptr_array([_dev(G, "G[k]", torch.float32) for G in Gs])
     ep = _ptr_array([_dev(E, "E[k]", torch.float32) for E in Es])
     qp = _ptr_array([_dev(Q, "Q[k]", torch.float32) for Q in Qs])
@@ -416,5 +425,11 @@ def lq_step_workers(Gs, Es, Qs, alpha, bits, bits_q=None, out=None,
         ctx.handle, gp, ep, qp, K, n, m, r, alpha, bits, bits if bits_q is None else bits_q,
         _dev(o["p_codes"], "p_codes", torch.int8), _dev(o["p_colmax"], "p_colmax", torch.float32),
         _dev(o["q_codes"], "q_codes", torch.int8), _dev(o["q_colmax"], "q_colmax", torch.float32),
-        _dev(o["G_hat"], "G_hat", torch.float32), _stream()))
+        _dev(o["G_hat"], "G_hat", torch.float32), opt("p_pre"), opt("q_pre"), _stream()))
     return o
+
+
+def trim(ctx: Optional[Context] = None) -> None:
+    """Wait for the device and free the buffers the context has retired (see gq_trim)."""
+    ctx = ctx or context()
+    ctx.check(_lib.gq_trim(ctx.handle))

@@ -21,11 +21,21 @@
  *  - Pointers are device memory unless marked (host).  Device pointers must be 16-byte
  *    aligned.  The caller owns every buffer and keeps it alive until the stream has finished.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work on it and
- *    return before the GPU finishes; none synchronises except gq_read_status.
+ *    return before the GPU finishes; none synchronises except gq_read_status, gq_trim and
+ *    gq_destroy.
  *  - Every argument is checked on the host before anything is enqueued.  On failure nothing
  *    is launched, the call returns the error code and gq_last_error(ctx) says why.
- *  - A context is not thread-safe; use one context per stream.  The library allocates device
- *    memory only inside a context (scratch that grows on demand, cached segment tables).
+ *  - A context is not thread-safe.  The library allocates device memory only inside a context
+ *    (scratch that grows on demand, cached segment tables), and every call made on a context
+ *    uses its one scratch: calls that may run at the same time (on streams the caller does not
+ *    order) need a context each; calls on one stream, or on streams the caller orders, may
+ *    share one.
+ *  - Lifetime (HIP graph capture): once a call has sized a context's scratch and cached its
+ *    segment layout, repeating it only launches kernels, so it can be captured into a graph.
+ *    Device buffers a call used stay valid as long as the context lives: scratch replaced by a
+ *    larger one and tables evicted from the cache (more than 64 layouts) are retired, not
+ *    freed.  Retired buffers are freed by gq_trim (call it only when no captured graph that
+ *    used the context will be replayed again) and by gq_destroy.
  *  - Segments: `offsets` (host) has nseg+1 int64 entries, offsets[0] = 0, offsets[nseg] = n,
  *    non-decreasing; every interior offset is a multiple of 8 (GQ_EALIGN otherwise).  Passing
  *    offsets = NULL with nseg = 1 means one segment [0, n).  Empty segments are allowed.
@@ -60,9 +70,14 @@ typedef int32_t gq_status;
 
 typedef struct gq_ctx gq_ctx;
 
-/* Create / destroy a context on the current HIP device. */
+/* Create / destroy a context on the current HIP device.  gq_destroy waits for the device and
+ * frees everything the context holds. */
 gq_status gq_create(gq_ctx **out);
 void gq_destroy(gq_ctx *ctx);
+/* Wait for the device, then free the buffers the context has retired (scratch replaced by a
+ * larger one, evicted segment tables).  Graphs captured from calls on ctx before this call
+ * must not be replayed afterwards.  The current scratch and cached tables are kept. */
+gq_status gq_trim(gq_ctx *ctx);
 /* Text of the last error on ctx (valid until the next call on ctx). */
 const char *gq_last_error(const gq_ctx *ctx);
 /* Library version string. */
@@ -113,18 +128,25 @@ gq_status gq_accumulate_codes(gq_ctx *ctx, const uint8_t *const *codes, int32_t 
                               int32_t grid, int32_t levels, int32_t bits, int32_t acc_bits,
                               void *sums, void *stream);
 
-/* Decode of the mean: mean_i = fp32(sums_i) * f_g, f_g = fp32(S_g / D) with the division in
+/* Decode of the mean (Global-QSGD abstract: the summed codes of the shared grid stand for the
+ * sum of the workers' quantised gradients, so one scale turns them into the mean):
+ *   mean_i = fp32(sums_i) * f_g, f_g = fp32(S_g / D) with the division in
  * fp64, D = s*K (uniform) or K*2^(E-1) (exponential); f_g = 0 for a scale that is not a
- * positive finite number.  out: n fp32, or bf16 rounded to nearest even (out_dtype). */
+ * positive finite number.  out: n fp32, or bf16 rounded to nearest even (out_dtype).
+ *   sums n int16/int32 (acc_bits);  scale nseg fp32 (device) */
 gq_status gq_dequantize(gq_ctx *ctx, const void *sums, int32_t acc_bits, int64_t n,
                         const int64_t *offsets, int32_t nseg, const float *scale, int32_t grid,
                         int32_t levels, int32_t K, int32_t out_dtype, void *out,
                         void *stream);
 
-/* One streaming pass equal, bit for bit, to gq_quantize_pack for every worker k (worker = k),
- * then gq_accumulate_codes, then gq_dequantize, without materialising codes or sums unless
- * asked: codes_or_null is NULL or a (host) array of K device pointers; sums_or_null is NULL or
- * n int16/int32. */
+/* The whole Global-QSGD aggregation in one streaming pass (Global-QSGD abstract: quantise
+ * with the shared scale, sum the codes as Allreduce does, decode the mean; "Quantize Once,
+ * Train Fast", title): equal, bit for bit, to gq_quantize_pack for every worker k
+ * (worker = k), then gq_accumulate_codes, then gq_dequantize, without materialising codes or
+ * sums unless asked: codes_or_null is NULL or a (host) array of K device pointers;
+ * sums_or_null is NULL or n int16/int32.
+ *   grads (host) array of K device pointers, n elements of `dtype` each;  scale nseg fp32
+ *   (device);  out n elements of out_dtype. */
 gq_status gq_fused_mean(gq_ctx *ctx, const void *const *grads, int32_t K, int32_t dtype,
                         int64_t n, const int64_t *offsets, int32_t nseg, const float *scale,
                         int32_t grid, int32_t levels, int32_t bits, uint64_t seed,
@@ -245,13 +267,15 @@ gq_status gq_powersgd_logquant(gq_ctx *ctx, const float *G, float *E, float *Q, 
  *   p_codes K x n x r int8, p_colmax K x r fp32, q_codes K x m x r int8, q_colmax K x r fp32:
  *                 every worker's message, stacked by worker
  *   G_hat n x m fp32 (must not be one of the E's)
+ *   p_pre_or_null K x n x r fp32 or NULL (every worker's orthonormalised P before quantisation)
+ *   q_pre_or_null K x m x r fp32 or NULL (every worker's Q' = M_w^T P_w before quantisation)
  * Every device pointer 16-byte aligned.  Invalid arguments return GQ_EINVAL or GQ_EALIGN with
  * nothing launched; scratch that cannot be allocated returns GQ_ENOMEM. */
 gq_status gq_lq_step_workers(gq_ctx *ctx, const float *const *G, float *const *E,
                              float *const *Q, int32_t K, int64_t n, int64_t m, int32_t r,
                              double alpha, int32_t bits_p, int32_t bits_q, int8_t *p_codes,
                              float *p_colmax, int8_t *q_codes, float *q_colmax, float *G_hat,
-                             void *stream);
+                             float *p_pre_or_null, float *q_pre_or_null, void *stream);
 
 #ifdef __cplusplus
 }

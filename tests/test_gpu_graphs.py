@@ -250,3 +250,102 @@ def test_default_context_warm_up_then_capture(orc):
                              w.offsets, out_dtype=1, scale=host(S))
     assert np.array_equal(host(out), ref["mean"]), first_diff(host(out), ref["mean"])
     del graph
+
+
+def test_replay_after_scratch_growth_and_table_eviction(orc):
+    """A graph keeps the scratch and segment table of the calls it captured.  Later eager calls
+    on the same context that grow its scratch (a much longer buffer) and evict its cached
+    layouts (65 new ones) retire those buffers instead of freeing them, so the replays still
+    match the eager calls; gq_trim then frees what was retired and eager calls go on."""
+    g = gq()
+    say("graph: replay after growth and eviction")
+    w = W.reduced("resnet50-161t-f32-K8-exp7")
+    xs = [x.to("cuda") for x in W.gradients(w, "cpu")]
+    gctx, ectx = g.Context(), g.Context()
+    S = torch.empty(w.nseg, dtype=torch.float32, device="cuda")
+    out = torch.empty(w.n, dtype=torch.float32, device="cuda")
+
+    def step(ctx, S_, out_):
+        g.global_norm(xs, w.offsets, scale_out=S_, ctx=ctx)
+        g.fused_mean(xs, S_, w.grid, w.levels, w.bits, 5, w.acc_bits, 0, offsets=w.offsets,
+                     out=out_, ctx=ctx)
+
+    step(gctx, S, out)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(gctx, S, out)
+    torch.cuda.synchronize()
+    # grow the norm scratch: 8 workers of 2^26 elements need far more tile partials
+    big = [torch.randn(1 << 26, device="cuda") for _ in range(8)]
+    g.global_norm(big, None, ctx=gctx)
+    # evict the cached layouts: 65 distinct two-segment layouts
+    y = torch.randn(65 * 8 + 64, device="cuda")
+    s1 = torch.ones(2, dtype=torch.float32, device="cuda")
+    for t in range(65):
+        g.quantize_pack(y, s1, 0, 7, 8, 1, 0, offsets=[0, 8 * (t + 1), y.numel()], ctx=gctx)
+    torch.cuda.synchronize()
+    del big
+    S_e, out_e = torch.empty_like(S), torch.empty_like(out)
+    for rep in range(3):
+        for x in xs:
+            x.mul_(-1.25)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(ectx, S_e, out_e)
+        torch.cuda.synchronize()
+        assert torch.equal(S, S_e), "replay %d: scale" % rep
+        assert torch.equal(out, out_e), "replay %d: %s" % (rep, first_diff(host(out), host(out_e)))
+    ref = orc.allreduce_mean([host(x) for x in xs], w.grid, w.levels, w.bits, w.acc_bits, 5, 0,
+                             w.offsets, scale=host(S))
+    assert np.array_equal(host(out), ref["mean"]), first_diff(host(out), ref["mean"])
+    del graph
+    g.trim(ctx=gctx)
+    step(gctx, S, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_e)
+    gctx.close()
+    ectx.close()
+
+
+def test_lq_replay_after_scratch_growth():
+    """The LQ-SGD step captured on a context whose scratch a larger eager step then replaces:
+    the replays still equal the eager step on a second context bit for bit."""
+    g = gq()
+    n, m, r = 512, 384, 3
+    say("graph: lq replay after growth", n, m, r)
+    gen = torch.Generator(device="cuda").manual_seed(23)
+    G = torch.randn(n, m, device="cuda", generator=gen) * 1e-3
+    E0 = torch.randn(n, m, device="cuda", generator=gen) * 1e-4
+    Q0 = torch.randn(m, r, device="cuda", generator=gen)
+    gctx, ectx = g.Context(), g.Context()
+    Eg, Qg, Ee, Qe = E0.clone(), Q0.clone(), E0.clone(), Q0.clone()
+    og = g.powersgd_logquant(G, Eg, Qg, W.LQ_ALPHA, W.LQ_BITS, ctx=gctx)
+    oe = g.powersgd_logquant(G, Ee, Qe, W.LQ_ALPHA, W.LQ_BITS, ctx=ectx)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        og = g.powersgd_logquant(G, Eg, Qg, W.LQ_ALPHA, W.LQ_BITS, out=og, ctx=gctx)
+    torch.cuda.synchronize()
+    # a much larger step on the capturing context replaces its scratch
+    Gb = torch.randn(4096, 4096, device="cuda", generator=gen)
+    g.powersgd_logquant(Gb, torch.zeros_like(Gb), torch.randn(4096, 8, device="cuda",
+                                                              generator=gen),
+                        W.LQ_ALPHA, W.LQ_BITS, ctx=gctx)
+    torch.cuda.synchronize()
+    del Gb
+    for rep in range(3):
+        G.mul_(-1.5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        oe = g.powersgd_logquant(G, Ee, Qe, W.LQ_ALPHA, W.LQ_BITS, out=oe, ctx=ectx)
+        torch.cuda.synchronize()
+        for k in ("p_codes", "q_codes", "p_colmax", "q_colmax", "p_hat"):
+            assert torch.equal(og[k], oe[k]), "replay %d: %s" % (rep, k)
+        assert torch.equal(Eg, Ee) and torch.equal(Qg, Qe), "replay %d" % rep
+    del graph
+    g.trim(ctx=gctx)
+    gctx.close()
+    ectx.close()

@@ -80,7 +80,22 @@ def _step_both(orc, G, E, Q, bits=BITS, bits_q=None):
     return ref, out, host(Ed), host(Qd)
 
 
-def _check_step(ref, out, E_gpu, Q_gpu, tol=2e-3, orthonormal=True):
+def _check_requant(orc, out, Q_gpu, alpha=ALPHA, bp=BITS, bq=BITS):
+    """Given the GPU's own unquantised factors, the oracle's quantiser reproduces the GPU's
+    codes, column maxima and decoded factors bit for bit (a wrong bin anywhere fails)."""
+    for pre, codes, cmax, hat, bits in (("p_pre", "p_codes", "p_colmax", host(out["p_hat"]), bp),
+                                        ("q_pre", "q_codes", "q_colmax", Q_gpu, bq)):
+        rc, rm, rh = orc.logquant(host(out[pre]), alpha, bits)
+        gc = host(out[codes])
+        assert np.array_equal(gc, rc), (codes, first_diff(gc, rc))
+        assert np.array_equal(host(out[cmax]), rm), cmax
+        assert np.array_equal(hat, rh), (pre, first_diff(hat, rh))
+
+
+def _check_step(ref, out, E_gpu, Q_gpu, tol=2e-3, orthonormal=True, orc=None, alpha=ALPHA,
+                bp=BITS, bq=BITS):
+    if orc is not None:
+        _check_requant(orc, out, Q_gpu, alpha, bp, bq)
     P_pre = host(out["p_pre"])
     Q_pre = host(out["q_pre"])
     assert _rel(P_pre, ref["P_pre"]) < 1e-5
@@ -118,7 +133,7 @@ def test_step_small(orc, n, m, r):
         G = (rng.standard_normal((n, m)) * 1e-3
              + np.outer(rng.standard_normal(n), rng.standard_normal(m)) * 1e-3).astype(np.float32)
         ref, out, Eg, Qg = _step_both(orc, G, E, Q)
-        _check_step(ref, out, Eg, Qg)
+        _check_step(ref, out, Eg, Qg, orc=orc)
         E, Q = ref["E"], ref["Q"]
 
 
@@ -146,7 +161,9 @@ def test_step_invariants_on_gpu():
 @pytest.mark.parametrize("r", W.LQ_RANKS)
 def test_step_full_shapes(orc, shape, r):
     """The LQ-SGD workload: noise (std 1e-3) + rank-8 signal, error feedback over 3 steps with
-    a fresh gradient per step; each step starts both sides from the oracle's state."""
+    a fresh gradient per step; each step starts both sides from the oracle's state.  Besides
+    the step tolerances, the oracle's quantiser on the GPU's own unquantised factors must give
+    the GPU's codes, maxima and decoded factors bit for bit."""
     n, m = shape
     say("lq step full", n, m, r)
     E = np.zeros((n, m), np.float32)
@@ -156,7 +173,7 @@ def test_step_full_shapes(orc, shape, r):
         if Q is None:
             Q = Q0.numpy()
         ref, out, Eg, Qg = _step_both(orc, Gt.numpy(), E, Q)
-        _check_step(ref, out, Eg, Qg)
+        _check_step(ref, out, Eg, Qg, orc=orc)
         E, Q = ref["E"], ref["Q"]
 
 
@@ -238,7 +255,7 @@ def test_step_separate_code_widths(orc, bp, bq):
         G = (rng.standard_normal((n, m)) * 1e-3
              + np.outer(rng.standard_normal(n), rng.standard_normal(m)) * 1e-3).astype(np.float32)
         ref, out, Eg, Qg = _step_both(orc, G, E, Q, bits=bp, bits_q=bq)
-        _check_step(ref, out, Eg, Qg)
+        _check_step(ref, out, Eg, Qg, orc=orc, bp=bp, bq=bq)
         pc, _, _ = orc.logquant(host(out["p_pre"]), ALPHA, bp)
         qc, _, _ = orc.logquant(host(out["q_pre"]), ALPHA, bq)
         assert np.array_equal(host(out["p_codes"]), pc)
@@ -288,7 +305,7 @@ def test_step_rank_deficient_gradient(orc, n, m, r, rank):
     assert not P_pre[:, dead].any()
     live = ~dead
     assert np.abs(P_pre[:, live].T @ P_pre[:, live] - np.eye(rank)).max() < 1e-5
-    _check_step(ref, out, Eg, Qg, orthonormal=False)
+    _check_step(ref, out, Eg, Qg, orthonormal=False, orc=orc)
 
 
 @pytest.mark.parametrize("ill", [False, True])
@@ -357,7 +374,7 @@ def test_step_fewer_rows_than_rank(orc, n, m, r):
     assert not P_pre[:, dead].any()
     k = int((~dead).sum())
     assert np.abs(P_pre[:, ~dead].T @ P_pre[:, ~dead] - np.eye(k)).max() < 1e-5
-    _check_step(ref, out, Eg, Qg, orthonormal=False)
+    _check_step(ref, out, Eg, Qg, orthonormal=False, orc=orc)
 
 
 @pytest.mark.parametrize("i", range(16))
@@ -381,7 +398,7 @@ def test_step_random_configurations(orc, i):
         ref = orc.powersgd_logquant(G, E, Q, alpha, bp, bits_q=bq)
         Ed, Qd = dev(E), dev(Q)
         out = g.powersgd_logquant(dev(G), Ed, Qd, alpha, bp, want_pre=True, bits_q=bq)
-        _check_step(ref, out, host(Ed), host(Qd))
+        _check_step(ref, out, host(Ed), host(Qd), orc=orc, alpha=alpha, bp=bp, bq=bq)
         E, Q = ref["E"], ref["Q"]
 
 
@@ -396,7 +413,7 @@ def test_step_extreme_shapes(orc, n, m, r):
     E = np.zeros((n, m), np.float32)
     Q = rng.standard_normal((m, r)).astype(np.float32)
     ref, out, Eg, Qg = _step_both(orc, G, E, Q)
-    _check_step(ref, out, Eg, Qg)
+    _check_step(ref, out, Eg, Qg, orc=orc)
 
 
 def test_step_rejects_too_many_rows():

@@ -36,12 +36,34 @@ def _step_both(orc, Gs, Es, Qs, bp=BITS, bq=BITS):
     ref = orc.lq_step_workers(Gs, Es, Qs, ALPHA, bp, bits_q=bq)
     Ed = [dev(E) for E in Es]
     Qd = [dev(Q) for Q in Qs]
-    out = g.lq_step_workers([dev(G) for G in Gs], Ed, Qd, ALPHA, bp, bits_q=bq)
+    out = g.lq_step_workers([dev(G) for G in Gs], Ed, Qd, ALPHA, bp, bits_q=bq, want_pre=True)
+    out["bits"] = (bp, bq)
     return ref, out, [host(E) for E in Ed], [host(Q) for Q in Qd]
+
+
+def _check_requant(out, Qg):
+    """Each worker's codes, column maxima and decoded warm start are what the oracle's
+    quantiser gives on that worker's own unquantised factors from the GPU, bit for bit."""
+    from oracle import oracle as orc
+    bp, bq = out["bits"]
+    alpha = out.get("alpha", ALPHA)
+    P_pre, Q_pre = host(out["p_pre"]), host(out["q_pre"])
+    pc, pm = host(out["p_codes"]), host(out["p_colmax"])
+    qc, qm = host(out["q_codes"]), host(out["q_colmax"])
+    for w in range(len(Qg)):
+        rc, rm, _ = orc.logquant(P_pre[w], alpha, bp)
+        assert np.array_equal(pc[w], rc), ("p_codes", w)
+        assert np.array_equal(pm[w], rm), ("p_colmax", w)
+        rc, rm, rh = orc.logquant(Q_pre[w], alpha, bq)
+        assert np.array_equal(qc[w], rc), ("q_codes", w)
+        assert np.array_equal(qm[w], rm), ("q_colmax", w)
+        assert np.array_equal(Qg[w], rh), ("warm start", w)
 
 
 def _check(ref, out, Eg, Qg, tol=2e-3):
     K = len(Eg)
+    if "p_pre" in out:
+        _check_requant(out, Qg)
     for key in ("p_codes", "q_codes"):
         gc = host(out[key]).astype(np.int32)
         rc = ref[key].astype(np.int32)
@@ -153,7 +175,7 @@ def test_argument_errors(case):
     if case == "K=0":
         ctx = g.context()
         rc = g._lib.gq_lq_step_workers(ctx.handle, None, None, None, 0, 32, 16, 2, ALPHA, BITS,
-                                       BITS, None, None, None, None, None, None)
+                                       BITS, None, None, None, None, None, None, None, None)
         assert rc == 1
         return
     n, m, r, K = 32, 16, 2, 3
@@ -205,6 +227,8 @@ def test_workers_random_configurations(orc, i):
         ref = orc.lq_step_workers(Gs, Es, Qs, alpha, bp, bits_q=bq)
         Ed = [dev(E) for E in Es]
         Qd = [dev(Q) for Q in Qs]
-        out = g.lq_step_workers([dev(G) for G in Gs], Ed, Qd, alpha, bp, bits_q=bq)
+        out = g.lq_step_workers([dev(G) for G in Gs], Ed, Qd, alpha, bp, bits_q=bq,
+                                want_pre=True)
+        out["bits"], out["alpha"] = (bp, bq), alpha
         _check(ref, out, [host(E) for E in Ed], [host(Q) for Q in Qd])
         Es, Qs = ref["E"], ref["Q"]
