@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -65,6 +66,12 @@ gq_status hip_fail(gq_ctx *c, hipError_t e, const char *what) {
   return fail(c, GQ_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
 }
 
+#define TRY(x)                     \
+  do {                             \
+    gq_status st_ = (x);           \
+    if (st_ != GQ_OK) return st_;  \
+  } while (0)
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): worker k's key is the low 32 bits of the
@@ -102,18 +109,12 @@ gq_status ensure_scratch(gq_ctx *c, size_t bytes, hipStream_t) {
   return GQ_OK;
 }
 
-// Validate the segment description and build the tile view (cached per layout).
-gq_status resolve_segments(gq_ctx *c, int64_t n, const int64_t *offsets, int32_t nseg,
-                           hipStream_t s, TileView *tv, int tile = gq::kTile) {
+// Validate the segment description (no table is built).
+gq_status check_segments(gq_ctx *c, int64_t n, const int64_t *offsets, int32_t nseg) {
   if (n < 0) return fail(c, GQ_EINVAL, "n = %lld is negative", (long long)n);
   if (nseg < 1) return fail(c, GQ_EINVAL, "nseg = %d must be >= 1", nseg);
-  tv->n = n;
-  tv->nseg = nseg;
   if (offsets == nullptr) {
     if (nseg != 1) return fail(c, GQ_EINVAL, "offsets = NULL needs nseg = 1");
-    tv->tiles = nullptr;
-    tv->seg_tile_start = nullptr;
-    tv->ntiles = (n + tile - 1) / tile;
     return GQ_OK;
   }
   if (offsets[0] != 0) return fail(c, GQ_EINVAL, "offsets[0] = %lld, must be 0", (long long)offsets[0]);
@@ -126,7 +127,16 @@ gq_status resolve_segments(gq_ctx *c, int64_t n, const int64_t *offsets, int32_t
       return fail(c, GQ_EALIGN, "interior offset %d = %lld is not a multiple of 8", g,
                   (long long)offsets[g]);
   }
-  if (nseg == 1) {
+  return GQ_OK;
+}
+
+// Validate the segment description and build the tile view (cached per layout).
+gq_status resolve_segments(gq_ctx *c, int64_t n, const int64_t *offsets, int32_t nseg,
+                           hipStream_t s, TileView *tv, int tile = gq::kTile) {
+  TRY(check_segments(c, n, offsets, nseg));
+  tv->n = n;
+  tv->nseg = nseg;
+  if (offsets == nullptr || nseg == 1) {
     tv->tiles = nullptr;
     tv->seg_tile_start = nullptr;
     tv->ntiles = (n + tile - 1) / tile;
@@ -223,11 +233,86 @@ double decode_denominator(int32_t grid, int32_t levels, int32_t K) {
   return grid == GQ_UNIFORM ? (double)levels * (double)K : (double)K * std::ldexp(1.0, levels - 1);
 }
 
-#define TRY(x)                     \
-  do {                             \
-    gq_status st_ = (x);           \
-    if (st_ != GQ_OK) return st_;  \
-  } while (0)
+}  // namespace
+
+// ---------------------------------------------------------------- fixed scratch (no allocation)
+// For callers that cannot allocate device memory (graph capture, tight serving loops): one
+// fixed buffer per GPU, in the library's code object, that gq_global_norm_noalloc uses for its
+// tile table, tile partials and per-worker norms.  In host code `scratch` names a host-side
+// stand-in; its device address comes from hipGetSymbolAddress, resolved once per device (at
+// gq_create, with that device current) and kept in g_fixed[device].
+static __device__ __align__(256) unsigned char scratch[GQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_fixed_mu;
+void *g_fixed[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (resolved on the first call there).
+hipError_t fixed_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_fixed_mu);
+  if (!g_fixed[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_fixed[dev] = p;
+  }
+  *out = g_fixed[dev];
+  return hipSuccess;
+}
+
+// The tile table of a segment layout given by value (at most kSegArgMax segments), built on
+// the device so that no host buffer has to be uploaded: each block scans the segments' tile
+// counts (one thread per segment) into every segment's first tile, block 0 stores those, and
+// tile t finds its segment by binary search over them (an empty segment owns no tile).  The
+// table is the one resolve_segments builds on the host.
+constexpr int kSegArgMax = 256;
+struct SegArg {
+  int64_t offsets[kSegArgMax + 1];
+  int64_t ntiles;
+  int32_t nseg;
+  int32_t tile;
+};
+
+__global__ __launch_bounds__(kSegArgMax) void k_build_tiles(const SegArg sa, Tile *tiles,
+                                                            int64_t *start) {
+  __shared__ int64_t st[kSegArgMax + 1];
+  const int g = threadIdx.x;
+  int64_t cnt = 0;
+  if (g < sa.nseg) cnt = (sa.offsets[g + 1] - sa.offsets[g] + sa.tile - 1) / sa.tile;
+  st[g + 1] = cnt;
+  if (g == 0) st[0] = 0;
+  __syncthreads();
+  for (int d = 1; d < kSegArgMax; d <<= 1) {  // inclusive scan of st[1..kSegArgMax]
+    const int64_t v = g >= d ? st[g + 1 - d] : 0;
+    __syncthreads();
+    st[g + 1] += v;
+    __syncthreads();
+  }
+  if (blockIdx.x == 0)
+    for (int i = g; i <= sa.nseg; i += kSegArgMax) start[i] = st[i];
+  for (int64_t t = (int64_t)blockIdx.x * kSegArgMax + g; t < sa.ntiles;
+       t += (int64_t)gridDim.x * kSegArgMax) {
+    int lo = 0, hi = sa.nseg;  // the segment lo with st[lo] <= t < st[lo + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (st[mid] <= t)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int64_t b = sa.offsets[lo] + (t - st[lo]) * sa.tile;
+    const int64_t rest = sa.offsets[lo + 1] - b;
+    tiles[t] = Tile{b, (int32_t)(rest < sa.tile ? rest : sa.tile), lo};
+  }
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -246,6 +331,13 @@ GQ_EXPORT gq_status gq_create(gq_ctx **out) {
     if (c->status_host) (void)hipHostFree(c->status_host);
     delete c;
     return GQ_ENOMEM;
+  }
+  void *fixed = nullptr;  // resolve the fixed scratch of this device now, while it is current
+  if (fixed_scratch(&fixed) != hipSuccess) {
+    (void)hipFree(c->status);
+    (void)hipHostFree(c->status_host);
+    delete c;
+    return GQ_ELAUNCH;
   }
   *out = c;
   return GQ_OK;
@@ -314,6 +406,81 @@ GQ_EXPORT gq_status gq_global_norm(gq_ctx *c, const void *const *grads, int32_t 
   a.tv = tv;
   a.K = K;
   hipError_t e = gq::launch_global_norm(a, dtype, s);
+  return e == hipSuccess ? GQ_OK : hip_fail(c, e, "global norm launch");
+}
+
+GQ_EXPORT gq_status gq_global_norm_noalloc(gq_ctx *c, const void *const *grads, int32_t K,
+                                           int32_t dtype, int64_t n, const int64_t *offsets,
+                                           int32_t nseg, float *scale_out, double *norms_out,
+                                           void *stream) {
+  if (!c) return GQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(check_K(c, K));
+  TRY(check_dtype(c, dtype, "dtype"));
+  if (!grads) return fail(c, GQ_EINVAL, "grads is NULL");
+  for (int k = 0; k < K; ++k) TRY(check_ptr(c, grads[k], "grads[k]", n == 0));
+  TRY(check_ptr(c, scale_out, "scale_out"));
+  if (norms_out) TRY(check_ptr(c, norms_out, "norms_out"));
+  TRY(check_segments(c, n, offsets, nseg));
+  const bool table = offsets != nullptr && nseg > 1;
+  if (table && nseg > kSegArgMax)
+    return fail(c, GQ_EINVAL, "nseg = %d: the allocation-free norm takes at most %d segments",
+                nseg, kSegArgMax);
+  const int64_t tile = gq::kNormTile;
+  int64_t ntiles = 0;
+  if (table)
+    for (int32_t g = 0; g < nseg; ++g) ntiles += (offsets[g + 1] - offsets[g] + tile - 1) / tile;
+  else
+    ntiles = (n + tile - 1) / tile;
+  // fixed scratch: [tile table | first tile of every segment | K x ntiles partials | K x nseg
+  // norms], each part 256-byte aligned
+  const size_t o_tiles = 0;
+  const size_t o_start = o_tiles + (table ? align256((size_t)ntiles * sizeof(Tile)) : 0);
+  const size_t o_part = o_start + (table ? align256((size_t)(nseg + 1) * sizeof(int64_t)) : 0);
+  const size_t o_norms = o_part + align256((size_t)K * (size_t)ntiles * sizeof(double));
+  const size_t need = o_norms + align256((size_t)K * (size_t)nseg * sizeof(double));
+  if (need > (size_t)GQ_NOALLOC_SCRATCH_BYTES)
+    return fail(c, GQ_EINVAL,
+                "the allocation-free norm needs %zu bytes of scratch for K = %d, n = %lld, "
+                "nseg = %d; its fixed buffer holds %zu",
+                need, K, (long long)n, nseg, (size_t)GQ_NOALLOC_SCRATCH_BYTES);
+  void *fixed = nullptr;
+  hipError_t e = fixed_scratch(&fixed);
+  if (e != hipSuccess) return hip_fail(c, e, "resolving the fixed scratch");
+  char *base = static_cast<char *>(fixed);
+  TileView tv;
+  tv.n = n;
+  tv.nseg = nseg;
+  tv.ntiles = ntiles;
+  tv.tiles = nullptr;
+  tv.seg_tile_start = nullptr;
+  if (table) {
+    SegArg sa;
+    std::memcpy(sa.offsets, offsets, (size_t)(nseg + 1) * sizeof(int64_t));
+    sa.ntiles = ntiles;
+    sa.nseg = nseg;
+    sa.tile = (int32_t)tile;
+    Tile *tiles = reinterpret_cast<Tile *>(base + o_tiles);
+    int64_t *start = reinterpret_cast<int64_t *>(base + o_start);
+    const int64_t blocks = (ntiles + kSegArgMax - 1) / kSegArgMax;
+    hipLaunchKernelGGL(k_build_tiles, dim3((unsigned)(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks))),
+                       dim3(kSegArgMax), 0, s, sa, tiles, start);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(c, e, "tile table launch");
+    tv.tiles = tiles;
+    tv.seg_tile_start = start;
+  }
+  gq::NormArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int k = 0; k < K; ++k) a.grads[k] = grads[k];
+  a.partial = reinterpret_cast<double *>(base + o_part);
+  a.norms = reinterpret_cast<double *>(base + o_norms);
+  a.scale_out = scale_out;
+  a.norms_out = norms_out;
+  a.status = c->status;
+  a.tv = tv;
+  a.K = K;
+  e = gq::launch_global_norm(a, dtype, s);
   return e == hipSuccess ? GQ_OK : hip_fail(c, e, "global norm launch");
 }
 

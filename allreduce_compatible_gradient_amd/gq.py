@@ -57,6 +57,7 @@ _SIGS = {
     "gq_lq_step_workers": (_i32, [_p, _p, _p, _p, _i32, _i64, _i64, _i32, _d, _i32, _i32, _p,
                                   _p, _p, _p, _p, _p, _p, _p]),
     "gq_trim": (_i32, [_p]),
+    "gq_global_norm_noalloc": (_i32, [_p, _p, _i32, _i32, _i64, _p, _i32, _p, _p, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -177,6 +178,23 @@ def global_norm(grads: Sequence[torch.Tensor], offsets=None, scale_out=None, nor
                                   _dev(scale_out, "scale_out", torch.float32),
                                   None if norms_out is None else
                                   _dev(norms_out, "norms_out", torch.float64), _stream()))
+    return scale_out, norms_out
+
+
+def global_norm_noalloc(grads: Sequence[torch.Tensor], offsets, scale_out, norms_out=None,
+                        ctx: Optional[Context] = None):
+    """gq_global_norm_noalloc: global_norm with its temporaries in the library's fixed buffer;
+    the caller passes scale_out (nseg fp32) and optionally norms_out (K*nseg fp64)."""
+    ctx = ctx or context()
+    n = grads[0].numel()
+    dt = _elt(grads[0])
+    ptrs = [_dev(g, "grads[%d]" % k, grads[0].dtype) for k, g in enumerate(grads)]
+    off, nseg, keep = _offsets(offsets, n)
+    ctx.check(_lib.gq_global_norm_noalloc(ctx.handle, _ptr_array(ptrs), len(grads), dt, n, off,
+                                          nseg, _dev(scale_out, "scale_out", torch.float32),
+                                          None if norms_out is None else
+                                          _dev(norms_out, "norms_out", torch.float64),
+                                          _stream()))
     return scale_out, norms_out
 
 

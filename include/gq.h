@@ -97,6 +97,25 @@ gq_status gq_global_norm(gq_ctx *ctx, const void *const *grads, int32_t K, int32
                          int64_t n, const int64_t *offsets, int32_t nseg, float *scale_out,
                          double *norms_out, void *stream);
 
+/* gq_global_norm for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same results, bit for
+ * bit, with every temporary (tile table, tile partials, per-worker norms) in one fixed buffer
+ * of GQ_NOALLOC_SCRATCH_BYTES per GPU that the library holds from the first gq_create on that
+ * device until the process ends.  No call allocates or frees anything; the caller passes the
+ * inputs and outputs as for gq_global_norm, with that device current.  Limits, each refused
+ * with GQ_EINVAL before anything is enqueued: at most 256 segments when `offsets` is given,
+ * and 8 * K * (ntiles + nseg) bytes (+ 16 * ntiles + 8 * (nseg + 1) for a segment table, each
+ * part rounded up to 256 bytes) within the buffer, ntiles = sum over segments of
+ * ceil(len / 65536) -- e.g. one segment of n elements fits for 8 workers while n <= 8.5e9 and
+ * for 64 workers while n <= 1.07e9.  Every call on a
+ * GPU uses the same buffer: calls that may overlap on one GPU (different streams, different
+ * threads) race and must be ordered by the caller.  Nothing in the buffer has to start at
+ * zero: every part is written before it is read. */
+#define GQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+gq_status gq_global_norm_noalloc(gq_ctx *ctx, const void *const *grads, int32_t K, int32_t dtype,
+                                 int64_t n, const int64_t *offsets, int32_t nseg,
+                                 float *scale_out, double *norms_out, void *stream);
+
 /* Stochastic quantisation onto the shared grid, packed to `bits` (4 or 8) per element
  * (Global-QSGD abstract: unbiased compressor on a grid all workers share; LQ-SGD review, "Core
  * claim": only the b-bit indices are transmitted).  With u = |x| * inv_g:
