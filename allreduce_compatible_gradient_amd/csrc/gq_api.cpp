@@ -392,7 +392,8 @@ GQ_EXPORT gq_status gq_global_norm(gq_ctx *c, const void *const *grads, int32_t 
   TRY(check_ptr(c, scale_out, "scale_out"));
   if (norms_out) TRY(check_ptr(c, norms_out, "norms_out"));
   TileView tv;
-  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, gq::kNormTile));
+  const int tile = gq::norm_tile(K, n);
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, tile));
   const size_t npart = (size_t)K * (size_t)tv.ntiles;
   TRY(ensure_scratch(c, (npart + (size_t)K * nseg) * sizeof(double), s));
   gq::NormArgs a;
@@ -405,6 +406,7 @@ GQ_EXPORT gq_status gq_global_norm(gq_ctx *c, const void *const *grads, int32_t 
   a.status = c->status;
   a.tv = tv;
   a.K = K;
+  a.tile = tile;
   hipError_t e = gq::launch_global_norm(a, dtype, s);
   return e == hipSuccess ? GQ_OK : hip_fail(c, e, "global norm launch");
 }
@@ -426,7 +428,7 @@ GQ_EXPORT gq_status gq_global_norm_noalloc(gq_ctx *c, const void *const *grads, 
   if (table && nseg > kSegArgMax)
     return fail(c, GQ_EINVAL, "nseg = %d: the allocation-free norm takes at most %d segments",
                 nseg, kSegArgMax);
-  const int64_t tile = gq::kNormTile;
+  const int64_t tile = gq::norm_tile(K, n);
   int64_t ntiles = 0;
   if (table)
     for (int32_t g = 0; g < nseg; ++g) ntiles += (offsets[g + 1] - offsets[g] + tile - 1) / tile;
@@ -480,6 +482,7 @@ GQ_EXPORT gq_status gq_global_norm_noalloc(gq_ctx *c, const void *const *grads, 
   a.status = c->status;
   a.tv = tv;
   a.K = K;
+  a.tile = (int32_t)tile;
   e = gq::launch_global_norm(a, dtype, s);
   return e == hipSuccess ? GQ_OK : hip_fail(c, e, "global norm launch");
 }
@@ -498,7 +501,7 @@ GQ_EXPORT gq_status gq_quantize_pack(gq_ctx *c, const void *grad, int32_t dtype,
   TRY(check_ptr(c, codes, "codes", n == 0));
   TRY(check_counter(c, n, index_base));
   TileView tv;
-  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, gq::quant_tile(dtype)));
   gq::QuantArgs a;
   a.grad = grad;
   a.scale = scale;
@@ -552,7 +555,7 @@ GQ_EXPORT gq_status gq_dequantize(gq_ctx *c, const void *sums, int32_t acc_bits,
   TRY(check_ptr(c, scale, "scale"));
   TRY(check_ptr(c, out, "out", n == 0));
   TileView tv;
-  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, gq::kTileMix));
   gq::DequantArgs a;
   a.sums = sums;
   a.scale = scale;
@@ -603,7 +606,7 @@ GQ_EXPORT gq_status gq_quantize_wire(gq_ctx *c, const void *grad, int32_t dtype,
   TRY(check_ptr(c, payload, "payload", n == 0));
   TRY(check_counter(c, n, index_base));
   TileView tv;
-  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, gq::quant_tile(dtype)));
   gq::WireQuantArgs a;
   a.grad = grad;
   a.scale = scale;
@@ -633,7 +636,7 @@ GQ_EXPORT gq_status gq_dequantize_wire(gq_ctx *c, const void *payload, int64_t n
   TRY(check_ptr(c, scale, "scale"));
   TRY(check_ptr(c, out, "out", n == 0));
   TileView tv;
-  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, gq::kTileMix));
   gq::WireDequantArgs a;
   a.payload = static_cast<const uint8_t *>(payload);
   a.scale = scale;
@@ -668,9 +671,11 @@ GQ_EXPORT gq_status gq_fused_mean(gq_ctx *c, const void *const *grads, int32_t K
   TRY(check_ptr(c, scale, "scale"));
   TRY(check_ptr(c, out, "out", n == 0));
   TileView tv;
-  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, gq::kTileMix));
+  TRY(ensure_scratch(c, (size_t)nseg * sizeof(gq::SegConst), s));
   gq::FusedArgs a;
   std::memset(&a, 0, sizeof a);
+  a.segc = static_cast<gq::SegConst *>(c->scratch);
   for (int k = 0; k < K; ++k) {
     a.grads[k] = grads[k];
     a.codes[k] = codes_or_null ? codes_or_null[k] : nullptr;
@@ -705,7 +710,8 @@ GQ_EXPORT gq_status gq_worker_scales(gq_ctx *c, const void *const *grads, int32_
   for (int k = 0; k < K; ++k) TRY(check_ptr(c, grads[k], "grads[k]", n == 0));
   TRY(check_ptr(c, scales_out, "scales_out"));
   TileView tv;
-  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, gq::kNormTile));
+  const int tile = gq::norm_tile(K, n);
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, tile));
   TRY(ensure_scratch(c, (size_t)K * (size_t)tv.ntiles * sizeof(double), s));
   gq::NormArgs a;
   std::memset(&a, 0, sizeof a);
@@ -714,6 +720,7 @@ GQ_EXPORT gq_status gq_worker_scales(gq_ctx *c, const void *const *grads, int32_
   a.status = c->status;
   a.tv = tv;
   a.K = K;
+  a.tile = tile;
   hipError_t e = gq::launch_worker_scales(a, dtype, norm, scales_out, s);
   return e == hipSuccess ? GQ_OK : hip_fail(c, e, "worker scales launch");
 }
@@ -737,7 +744,7 @@ GQ_EXPORT gq_status gq_worker_mean(gq_ctx *c, const void *const *grads, int32_t 
   TRY(check_ptr(c, scales, "scales"));
   TRY(check_ptr(c, out, "out", n == 0));
   TileView tv;
-  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, gq::kTileMix));
   TRY(ensure_scratch(c, (size_t)K * (size_t)nseg * sizeof(float2), s));
   gq::WorkerMeanArgs a;
   std::memset(&a, 0, sizeof a);
@@ -771,7 +778,7 @@ GQ_EXPORT gq_status gq_decode_workers(gq_ctx *c, const uint8_t *const *codes, in
   TRY(check_ptr(c, scales, "scales"));
   TRY(check_ptr(c, out, "out", n == 0));
   TileView tv;
-  TRY(resolve_segments(c, n, offsets, nseg, s, &tv));
+  TRY(resolve_segments(c, n, offsets, nseg, s, &tv, gq::kTileMix));
   TRY(ensure_scratch(c, (size_t)K * (size_t)nseg * sizeof(float2), s));
   gq::DecodeWorkersArgs a;
   std::memset(&a, 0, sizeof a);

@@ -1,10 +1,12 @@
 // gq_ceiling.hip -- measurement probe for bench.py (libgq_ceiling.so, not part of libgq.so).
 //
-// A plain stream with the same memory pattern as the hot kernels and no arithmetic beyond a
-// sum: K fp32 input streams read with the lane map of the streaming kernels (non-temporal
-// 16-byte loads, each wave instruction one contiguous 1 KB block) and, optionally, one fp32
-// output stream (their sum).  Its bandwidth is the empirical ceiling the quantisation kernels
-// are compared with, beside the 8 TB/s HBM peak.
+// Plain streams with no arithmetic beyond a sum: K fp32 input streams and, optionally, one
+// fp32 output stream (their sum), under several access patterns -- the lane map of the
+// streaming kernels with a fixed grid striding over the buffers (gqc_stream), and patterns
+// that are not the kernels' own (gqc_stream_pattern): one float4 group per thread with a grid
+// that covers the buffers once, and one block per tile in the XCD order the kernels use.  The
+// best of them is the empirical ceiling the quantisation kernels are compared with, beside
+// the 8 TB/s HBM peak.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,6 +51,75 @@ __global__ __launch_bounds__(256) void k_stream(Srcs s, int64_t nchunks, float *
   if (!WRITE && keep.x == 1.25e-37f && keep.y == -3.0e33f) sink[0] = keep.z;
 }
 
+// Element-wise: thread i handles float4 i + u * (n4 / U) for u < U, the grid covering the
+// buffers once (blocks in dispatch order), non-temporal loads and stores.
+template <int K, int U, bool WRITE>
+__global__ __launch_bounds__(256) void k_elem(Srcs s, int64_t n4, float *out, float *sink) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t span = n4 / U;
+  f32x4 keep = {0.f, 0.f, 0.f, 0.f};
+  if (i < span) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        a += __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(s.x[k]) + i + u * span);
+      if (WRITE)
+        __builtin_nontemporal_store(a, reinterpret_cast<f32x4 *>(out) + i + u * span);
+      else
+        keep += a;
+    }
+  }
+  if (!WRITE && keep.x == 1.25e-37f && keep.y == -3.0e33f) sink[0] = keep.z;
+}
+
+// One block per tile of T elements in XCD order (block b -> tile (b mod 8) * q + b / 8), each
+// wave one 1 KB chunk per stream per step, as the kernels' lane map.
+template <int K, int T, bool WRITE>
+__global__ __launch_bounds__(256) void k_tiles(Srcs s, int64_t ntiles, float *out, float *sink) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t b = blockIdx.x, q = ntiles >> 3;
+  const int64_t t = b < 8 * q ? (b & 7) * q + (b >> 3) : b;
+  f32x4 keep = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = w; c < T / 256; c += 4) {
+    const int64_t e = t * T + (int64_t)c * 256 + 4 * lane;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      a += __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(s.x[k] + e));
+    if (WRITE)
+      __builtin_nontemporal_store(a, reinterpret_cast<f32x4 *>(out + e));
+    else
+      keep += a;
+  }
+  if (!WRITE && keep.x == 1.25e-37f && keep.y == -3.0e33f) sink[0] = keep.z;
+}
+
+template <int K, bool WRITE>
+hipError_t launch_pattern(Srcs s, int pattern, int param, int64_t n, float *out, float *sink,
+                          hipStream_t st) {
+  const dim3 b(256);
+  if (pattern == 1) {
+    const int64_t n4 = n / 4;
+    const unsigned grid = (unsigned)((n4 / param + 255) / 256);
+    switch (param) {
+      case 1: hipLaunchKernelGGL((k_elem<K, 1, WRITE>), dim3(grid), b, 0, st, s, n4, out, sink); break;
+      case 2: hipLaunchKernelGGL((k_elem<K, 2, WRITE>), dim3(grid), b, 0, st, s, n4, out, sink); break;
+      case 4: hipLaunchKernelGGL((k_elem<K, 4, WRITE>), dim3(grid), b, 0, st, s, n4, out, sink); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (param) {
+      case 2048: hipLaunchKernelGGL((k_tiles<K, 2048, WRITE>), dim3((unsigned)(n / 2048)), b, 0, st, s, n / 2048, out, sink); break;
+      case 8192: hipLaunchKernelGGL((k_tiles<K, 8192, WRITE>), dim3((unsigned)(n / 8192)), b, 0, st, s, n / 8192, out, sink); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
 template <int K, bool WRITE>
 hipError_t launch_q(Srcs s, int Q, int64_t n, float *out, float *sink, int grid, hipStream_t st) {
   const dim3 g(grid), b(256);
@@ -76,6 +147,38 @@ hipError_t launch(Srcs s, int K, int Q, int64_t n, float *out, float *sink, int 
 }
 
 }  // namespace
+
+// Patterns that are not the kernels' grid-stride lane map: pattern 1, element-wise with
+// param = U in {1, 2, 4} float4 per thread; pattern 2, one block per tile of param in
+// {2048, 8192} elements in XCD order.  Streams the first (n / 16384) * 16384 elements; K in
+// {1, 2, 4, 8, 16}; arguments and results as gqc_stream below.
+GQC_EXPORT int gqc_stream_pattern(const float *const *srcs, int K, int64_t n, float *out,
+                                  float *sink, int pattern, int param, void *stream) {
+  if (K < 1 || K > 16 || n < 0 || !srcs || !sink || (pattern != 1 && pattern != 2)) return 1;
+  Srcs s = {};
+  for (int k = 0; k < K; ++k) {
+    if (!srcs[k] || (reinterpret_cast<uintptr_t>(srcs[k]) & 15)) return 1;
+    s.x[k] = srcs[k];
+  }
+  if (out && (reinterpret_cast<uintptr_t>(out) & 15)) return 1;
+  const int64_t neff = n / 16384 * 16384;
+  if (neff == 0) return 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipErrorInvalidValue;
+#define GQC_K(KK) \
+  e = out ? launch_pattern<KK, true>(s, pattern, param, neff, out, sink, st) \
+          : launch_pattern<KK, false>(s, pattern, param, neff, nullptr, sink, st)
+  switch (K) {
+    case 1: GQC_K(1); break;
+    case 2: GQC_K(2); break;
+    case 4: GQC_K(4); break;
+    case 8: GQC_K(8); break;
+    case 16: GQC_K(16); break;
+    default: return 1;
+  }
+#undef GQC_K
+  return e == hipSuccess ? 0 : (e == hipErrorInvalidValue ? 1 : 2);
+}
 
 // Streams the first (n / 2048) * 2048 elements of K fp32 buffers (K in {1, 2, 4, 8, 16}) with
 // `grid` 256-thread blocks and Q in {1, 2, 4} quads per lane per stream; with out != NULL

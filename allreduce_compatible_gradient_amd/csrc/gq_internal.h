@@ -9,11 +9,31 @@ namespace gq {
 
 constexpr int kMaxWorkers = 64;
 constexpr int kGroup = 8;            // elements per thread step: one 32 B fp32 / 16 B bf16 load
-constexpr int kTile = 8192;          // elements per tile; a tile never crosses a segment
+// Elements per tile (a tile never crosses a segment): 8192 for the one-worker quantisers (one
+// read and one write stream), 2048 for the kernels that mix several streams with a write
+// stream (fused pass, integer sum, decodes), whose grids of small tiles in the XCD order of
+// gq_stream.hip stream fastest (measured on the 1.3e9 x 8 fused pass: 9.2 ms with 8192-element
+// tiles on 4096 resident blocks, 8.0 ms like this).
+constexpr int kTile = 8192;
+constexpr int kTileMix = 2048;
+// The one-worker quantisers' tile is 32 KB of input: kTile fp32 or 2 kTile bf16 elements
+// (measured on GPT-2's bf16 buckets: 8192-element tiles ran 5-6% slower).
+constexpr int quant_tile(int dtype) { return dtype == 1 ? 2 * kTile : kTile; }
 constexpr int kNormTile = 65536;     // elements per tile of the norm pass (one fp64 partial each)
+constexpr int kNormTileMin = 4096;   // ... halved down to this while K x tiles < kNormGrid
+
 constexpr int kBlock = 256;          // threads per block of the streaming kernels
-constexpr int kStreamGrid = 4096;    // resident blocks of the element-wise streaming kernels
+constexpr int kGridAll = 1 << 30;    // grid cap of the element-wise kernels: one block per tile
 constexpr int kNormGrid = 2048;      // blocks per worker of the norm pass
+
+// Tile of the norm pass for K workers of n elements: 65536, halved while the K x tiles blocks
+// would not fill the GPU (kNormGrid), down to 4096.  The tile fixes the fp64 summation order,
+// so every norm entry point takes it from here.
+inline int norm_tile(int K, int64_t n) {
+  int tile = kNormTile;
+  while (tile > kNormTileMin && (int64_t)K * ((n + tile - 1) / tile) < kNormGrid) tile >>= 1;
+  return tile;
+}
 
 // One tile of a segmented buffer: elements [begin, begin + len) of segment `seg`.
 struct Tile {
@@ -42,6 +62,7 @@ struct NormArgs {
   unsigned *status;       // bit 0: a non-finite norm
   TileView tv;
   int32_t K;
+  int32_t tile;           // elements per tile (norm_tile)
 };
 
 struct QuantArgs {
@@ -95,11 +116,24 @@ struct WireDequantArgs {
   double denom;
 };
 
+// Per-segment constants of the fused pass, computed once per segment before the pass (tiles
+// are small, so computing them per tile cost the vector ALUs about one instruction per
+// worker-element): inv = s/S or 1/S (0 when the scale is not usable), the decode factor f,
+// the fast path's threshold fast_below (0: no fast path) and inv_up = inv * 2^32 (uniform) or
+// inv * 2^(E+31) (exponential).
+struct SegConst {
+  float inv;
+  float f;
+  float fast_below;
+  float inv_up;
+};
+
 struct FusedArgs {
   const void *grads[kMaxWorkers];
   uint8_t *codes[kMaxWorkers];   // all nullptr unless codes are materialised
   uint32_t key_mix[kMaxWorkers];  // key ^ (key >> 16) per worker
   const float *scale;
+  SegConst *segc;                // nseg entries (scratch), filled by launch_fused
   void *sums;                    // nullptr unless sums are materialised
   void *out;
   TileView tv;

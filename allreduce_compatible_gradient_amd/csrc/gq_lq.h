@@ -27,6 +27,8 @@ struct LqTables {
   float *dev = nullptr;        // thr[L] then lvl[L + 1]
   std::vector<float> host;     // source of the stream-ordered upload, kept alive
   int L = 0;
+  float alpha = 0.0f;          // the quantiser's alpha, as fp32
+  float tl = 0.0f;             // L / log2(1 + alpha): the encode's first estimate
 };
 
 // Scratch of the steps.  A buffer replaced by a larger one is retired, not freed: a captured

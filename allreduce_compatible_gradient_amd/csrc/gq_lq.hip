@@ -11,7 +11,11 @@
 // and the work is organised around the three passes over the n x m matrix:
 //   pass 1  E <- G + E and P = E Q              (read G, E; write E)   k_lq_ef_mq
 //   pass 2  Q' = E^T Pt                         (read E)               k_lq_mtp + k_lq_qsum
-//   pass 3  E <- E - Phat Q'hat^T               (read E; write E)      k_lq_ef_update
+//   pass 3  E <- E - Phat Q'hat^T               (read E; write E)      k_lq_ef_update_q (one
+//                                                                      worker: quantises P and
+//                                                                      Q' itself), or
+//                                                                      k_lq_quant_elems + the
+//                                                                      K workers' k_lq_mean_ef
 // With K workers (each its own G, E and warm start Q; the review's "Core claim" compresses each
 // worker's factors before the exchange) every per-worker kernel runs all K in one launch, the
 // worker taken from a grid dimension, and the last pass becomes k_lq_mean_ef: the mean of the
@@ -54,6 +58,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRowsA = 4;      // rows per block in the row passes
 constexpr int kBlockA = 256;
 constexpr int kWavesC = 8;     // waves per column-pass block
+constexpr int kRowsQ = 64;     // rows per block of the one-worker last pass (k_lq_ef_update_q)
 // Rows per column-pass chunk: 128, or 64 when 128-row chunks would give fewer than
 // kColBlocksMin blocks (the pass is then latency-bound and wants more of them).
 constexpr int kColBlocksMin = 1024;
@@ -640,6 +645,28 @@ __global__ __launch_bounds__(256) void k_lq_qsum(const float *__restrict__ part_
   if (threadIdx.x < RANK) atomicMax(&cmax_bits[threadIdx.x], smax[threadIdx.x]);
 }
 
+// Log-quantise one factor value x of a column with maximum mx: the code and the decoded value
+// (Eq. 5 encode: k = the number of boundaries thr[0..L-1] at or below y = |x| / mx; Eq. 6
+// decode by the level table lvl[0..L]).  Boundary k lies at y where L log(1 + alpha y) /
+// log(1 + alpha) = k + 1/2, so with tl = L / log2(1 + alpha) the count is about
+// floor(tl log2(1 + alpha y) + 1/2); the estimate is then moved, one boundary at a time, until
+// thr[k - 1] <= y < thr[k] holds, which fixes k exactly as a search of the table would (a NaN
+// y counts no boundary).  The estimate is rarely off by more than one step.
+__device__ __forceinline__ void logq_one(float x, float mx, const float *thr, const float *lvl,
+                                         int L, float alpha, float tl, int8_t &code, float &fh) {
+  int k = 0;
+  if (mx > 0.0f) {
+    const float y = fabsf(x) / mx;  // IEEE division, in [0, 1]
+    const float t = tl * __log2f(fmaf(alpha, y, 1.0f)) + 0.5f;
+    k = t >= (float)L ? L : (t >= 1.0f ? (int)t : 0);
+    while (k < L && thr[k] <= y) ++k;
+    while (k > 0 && !(thr[k - 1] <= y)) --k;
+  }
+  code = (int8_t)(x < 0.0f ? -k : k);
+  const float v = lvl[k] * mx;
+  fh = x < 0.0f ? -v : v;
+}
+
 struct ColJob {
   const float *F;        // rows x r
   int64_t rows;
@@ -650,10 +677,10 @@ struct ColJob {
   float *Fhat2;          // rows x r or nullptr (second copy)
 };
 
-// One block per column: max magnitude, then Eq. 5 encode by the boundary table and Eq. 6
-// decode by the level table.
+// One block per column: max magnitude, then the Eq. 5 encode and Eq. 6 decode of logq_one.
 __global__ __launch_bounds__(1024) void k_lq_quant_cols(ColJob j0, ColJob j1, int ncols0,
-                                                        const float *tab, int L) {
+                                                        const float *tab, int L, float alpha,
+                                                        float tl) {
   __shared__ float thr[128];
   __shared__ float lvl[128];
   __shared__ float wmax[16];
@@ -672,31 +699,18 @@ __global__ __launch_bounds__(1024) void k_lq_quant_cols(ColJob j0, ColJob j1, in
   for (int i = 0; i < (int)(blockDim.x >> 6); ++i) mx = fmaxf(mx, wmax[i]);
   if (tid == 0) J.colmax[c] = mx;
   for (int64_t i = tid; i < J.rows; i += blockDim.x) {
-    const float x = J.F[i * J.r + c];
-    int k = 0;
-    if (mx > 0.0f) {
-      const float y = fabsf(x) / mx;  // IEEE division, in [0, 1]
-      int lo = 0, hi = L;             // k = #{boundaries <= y}
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (thr[mid] <= y)
-          lo = mid + 1;
-        else
-          hi = mid;
-      }
-      k = lo;
-    }
-    J.codes[i * J.r + c] = (int8_t)(x < 0.0f ? -k : k);
-    const float v = lvl[k] * mx;
-    const float fh = x < 0.0f ? -v : v;
+    int8_t code;
+    float fh;
+    logq_one(J.F[i * J.r + c], mx, thr, lvl, L, alpha, tl, code, fh);
+    J.codes[i * J.r + c] = code;
     if (J.Fhat) J.Fhat[i * J.r + c] = fh;
     if (J.Fhat2) J.Fhat2[i * J.r + c] = fh;
   }
 }
 
 // Log-quantise both factors element by element, the column maxima already known (cmax_bits:
-// RANK words for Pt, then RANK for Q'), each with its own tables (code widths b_p and b_q).
-// Same encode/decode as k_lq_quant_cols.
+// RANK words for Pt, then RANK for Q'), each with its own tables (code widths b_p and b_q),
+// by logq_one.
 struct ElemJob {
   const float *Pt;       // n x r
   const float *Qn;       // m x r
@@ -712,8 +726,9 @@ struct ElemJob {
 // Worker blockIdx.y: every pointer of J0 is the base of a buffer stacked by worker (p_hat may
 // be null); the decoded Q goes into the worker's own Q.
 __global__ __launch_bounds__(256) void k_lq_quant_elems(const ElemJob J0, const LqWorkerPtrs W,
-                                                        const float *tab_p, int Lp,
-                                                        const float *tab_q, int Lq) {
+                                                        const float *tab_p, int Lp, float tlp,
+                                                        const float *tab_q, int Lq, float tlq,
+                                                        float alpha) {
   __shared__ float thr[2][128];
   __shared__ float lvl[2][128];
   const int tid = threadIdx.x;
@@ -752,22 +767,9 @@ __global__ __launch_bounds__(256) void k_lq_quant_elems(const ElemJob J0, const 
   }
   if (!live) return;
   const int t = isp ? 0 : 1;
-  int k = 0;
-  if (mx > 0.0f) {
-    const float y = fabsf(x) / mx;  // IEEE division, in [0, 1]
-    int lo = 0, hi = isp ? Lp : Lq; // k = #{boundaries <= y}
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (thr[t][mid] <= y)
-        lo = mid + 1;
-      else
-        hi = mid;
-    }
-    k = lo;
-  }
-  const int8_t code = (int8_t)(x < 0.0f ? -k : k);
-  const float v = lvl[t][k] * mx;
-  const float fh = x < 0.0f ? -v : v;
+  int8_t code;
+  float fh;
+  logq_one(x, mx, thr[t], lvl[t], isp ? Lp : Lq, alpha, isp ? tlp : tlq, code, fh);
   if (isp) {
     J.p_codes[i] = code;
     J.Ph[i] = fh;
@@ -778,39 +780,110 @@ __global__ __launch_bounds__(256) void k_lq_quant_elems(const ElemJob J0, const 
   }
 }
 
-// Pass 3: E <- E - Phat Qhat^T (Qhat row-major m x RANK).
-template <int RANK, int VEC>
-__global__ __launch_bounds__(kBlockA) void k_lq_ef_update(float *__restrict__ E,
-                                                          const float *__restrict__ Ph,
-                                                          const float *__restrict__ Qh,
-                                                          int64_t n, int64_t m) {
-  const int64_t row0 = (int64_t)blockIdx.x * kRowsA;
-  float p[kRowsA][RANK];
+// Pass 3 of one worker with the log quantiser folded in: block (x, y) owns columns
+// [x * 64 VEC, (x + 1) * 64 VEC) and rows [y * RC, (y + 1) * RC).  Once the column pass has
+// left Pt, Q' and their column maxima, the block quantises its columns' rows of Q' and its
+// rows of Pt into LDS (the first row chunk also stores the Q codes and the decoded Q as the
+// warm start, the first column tile the P codes and the decoded P), then updates its tile of
+// E <- E - Phat Qhat^T, each entry's products summed by fused multiply-adds over the columns of
+// the factors in order.  Each value of Q'
+// is quantised by every row chunk and each value of Pt by every column tile (a few thousand
+// values per block, against the block's 64 VEC x RC elements of E).
+template <int RANK, int VEC, int RC>
+__global__ __launch_bounds__(256) void k_lq_ef_update_q(const ElemJob J, const LqWorkerPtrs W,
+                                                        const float *tab_p, int Lp, float tlp,
+                                                        const float *tab_q, int Lq, float tlq,
+                                                        float alpha) {
+  constexpr int COLS = 64 * VEC;
+  __shared__ float thr[2][128];
+  __shared__ float lvl[2][128];
+  __shared__ float qh[COLS * RANK];
+  __shared__ float ph[RC * RANK];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t n = J.n, m = J.m;
+  const int64_t j0 = (int64_t)blockIdx.x * COLS, r0 = (int64_t)blockIdx.y * RC;
+  float *__restrict__ E = W.E[0];
+  float *__restrict__ Qh = W.Q[0];
+  // the wave's first RB rows of its columns are loaded before the factors are quantised, so
+  // that the quantisation runs while they are in flight
+  constexpr int RB = 4;  // rows loaded together per wave
+  const int64_t j = j0 + (int64_t)lane * VEC;
+  const int64_t r1 = r0 + RC < n ? r0 + RC : n;
+  int64_t rb = r0 + w * RB;
+  float mv[RB][VEC];
+  if (j < m)
 #pragma unroll
-  for (int rr = 0; rr < kRowsA; ++rr)
+    for (int u = 0; u < RB; ++u)
+      if (rb + u < r1) ldv<VEC>(E + (rb + u) * m + j, mv[u]);
+  if (tid < Lp) thr[0][tid] = tab_p[tid];
+  if (tid <= Lp) lvl[0][tid] = tab_p[Lp + tid];
+  if (tid < Lq) thr[1][tid] = tab_q[tid];
+  if (tid <= Lq) lvl[1][tid] = tab_q[Lq + tid];
+  __syncthreads();
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid < 2 * RANK) {
+    const float mxv = __uint_as_float(J.cmax_bits[tid]);
+    if (tid < RANK) J.p_colmax[tid] = mxv; else J.q_colmax[tid - RANK] = mxv;
+  }
+  for (int e = tid; e < COLS * RANK; e += 256) {
+    const int64_t i = j0 * RANK + e;  // element (j0 + e / RANK, e % RANK) of Q'
+    float fh = 0.0f;
+    if (i < m * RANK) {
+      int8_t code;
+      logq_one(J.Qn[i], __uint_as_float(J.cmax_bits[RANK + e % RANK]), thr[1], lvl[1], Lq,
+               alpha, tlq, code, fh);
+      if (blockIdx.y == 0) {
+        J.q_codes[i] = code;
+        Qh[i] = fh;
+      }
+    }
+    qh[e] = fh;
+  }
+  for (int e = tid; e < RC * RANK; e += 256) {
+    const int64_t i = r0 * RANK + e;  // element (r0 + e / RANK, e % RANK) of Pt
+    float fh = 0.0f;
+    if (i < n * RANK) {
+      int8_t code;
+      logq_one(J.Pt[i], __uint_as_float(J.cmax_bits[e % RANK]), thr[0], lvl[0], Lp, alpha, tlp,
+               code, fh);
+      if (blockIdx.x == 0) {
+        J.p_codes[i] = code;
+        if (J.p_hat) J.p_hat[i] = fh;
+      }
+    }
+    ph[e] = fh;
+  }
+  __syncthreads();
+  if (j >= m) return;
+  float q[RANK][VEC];
 #pragma unroll
-    for (int c = 0; c < RANK; ++c) p[rr][c] = row0 + rr < n ? Ph[(row0 + rr) * RANK + c] : 0.0f;
-  const int nr = n - row0 < kRowsA ? (int)(n - row0) : kRowsA;
-  for (int64_t j = (int64_t)threadIdx.x * VEC; j < m; j += (int64_t)kBlockA * VEC) {
-    float q[RANK][VEC];
-    float mv[kRowsA][VEC];
+  for (int v = 0; v < VEC; ++v)
 #pragma unroll
-    for (int rr = 0; rr < kRowsA; ++rr)
-      if (rr < nr) ldv<VEC>(E + (row0 + rr) * m + j, mv[rr]);
-    load_q_rows<RANK, VEC>(Qh, j, q);
+    for (int c = 0; c < RANK; ++c) q[c][v] = qh[(lane * VEC + v) * RANK + c];
+  for (; rb < r1; rb += 4 * RB) {
+    // the wave's next RB rows are loaded before this batch is updated and stored
+    const int64_t rn = rb + 4 * RB;
+    float nx[RB][VEC];
 #pragma unroll
-    for (int rr = 0; rr < kRowsA; ++rr) {
-      if (rr < nr) {
+    for (int u = 0; u < RB; ++u)
+      if (rn + u < r1) ldv<VEC>(E + (rn + u) * m + j, nx[u]);
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      if (rb + u < r1) {
+        const int lr = (int)(rb + u - r0);
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
           float s = 0.0f;
 #pragma unroll
-          for (int c = 0; c < RANK; ++c) s = fmaf(p[rr][c], q[c][v], s);
-          mv[rr][v] -= s;
+          for (int c = 0; c < RANK; ++c) s = fmaf(ph[lr * RANK + c], q[c][v], s);
+          mv[u][v] -= s;
         }
-        stv<VEC>(E + (row0 + rr) * m + j, mv[rr]);
+        stv<VEC>(E + (rb + u) * m + j, mv[u]);
       }
     }
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) mv[u][v] = nx[u][v];
   }
 }
 
@@ -819,7 +892,7 @@ __global__ __launch_bounds__(kBlockA) void k_lq_ef_update(float *__restrict__ E,
 // the factors, by fused multiply-add), stored once, and E_w <- M_w - Ghat for every worker
 // (E_w holds M_w).  The 4 rows' decoded P entries of every worker are staged in LDS (at most
 // 16 x 4 x 8 floats); each worker's decoded Q rows are read from its own Q (m x r, L2-resident).
-// Two workers' rows are loaded before either is stored.  At K = 1 this is k_lq_ef_update with
+// Two workers' rows are loaded before either is stored.  At K = 1 this is the one-worker update with
 // Ghat also stored.
 template <int RANK, int VEC>
 __global__ __launch_bounds__(kBlockA) void k_lq_mean_ef(const LqWorkerPtrs W, int K,
@@ -926,6 +999,8 @@ hipError_t tables(LqState &st, double alpha, int bits, hipStream_t s, const LqTa
       t.host[k] = f;
     }
     for (int k = 0; k <= L; ++k) t.host[L + k] = (float)(std::expm1(lg * k / L) / alpha);
+    t.alpha = (float)alpha;
+    t.tl = (float)(L / std::log2(1.0 + alpha));
     hipError_t e = hipMalloc(&t.dev, t.host.size() * sizeof(float));
     if (e != hipSuccess) return hipErrorOutOfMemory;
     e = hipMemcpyAsync(t.dev, t.host.data(), t.host.size() * sizeof(float), hipMemcpyHostToDevice, s);
@@ -990,14 +1065,18 @@ void launch_step(const StepIO &io, const StepBufs &b, const LqTables &tp, const 
                        b.nchunks);
   ElemJob je{b.Pt, b.Qn, n, m, RANK, b.cmax_bits, io.p_codes, io.q_codes, io.p_colmax,
              io.q_colmax, b.Ph, io.p_hat, nullptr};
-  hipLaunchKernelGGL(k_lq_quant_elems, dim3((unsigned)(((n + m) * RANK + 255) / 256), K),
-                     dim3(256), 0, s, je, io.W, tp.dev, tp.L, tq.dev, tq.L);
-  if (io.G_hat)
+  if (io.G_hat) {
+    hipLaunchKernelGGL(k_lq_quant_elems, dim3((unsigned)(((n + m) * RANK + 255) / 256), K),
+                       dim3(256), 0, s, je, io.W, tp.dev, tp.L, tp.tl, tq.dev, tq.L, tq.tl,
+                       tp.alpha);
     hipLaunchKernelGGL((k_lq_mean_ef<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA), 0,
                        s, io.W, io.K, b.Ph, io.G_hat, 1.0f / (float)io.K, n, m);
-  else
-    hipLaunchKernelGGL((k_lq_ef_update<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA),
-                       0, s, io.W.E[0], b.Ph, io.W.Q[0], n, m);
+  } else {
+    // one worker: the quantiser runs inside the last pass
+    const dim3 g3((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)((n + kRowsQ - 1) / kRowsQ));
+    hipLaunchKernelGGL((k_lq_ef_update_q<RANK, VEC, kRowsQ>), g3, dim3(256), 0, s, je, io.W,
+                       tp.dev, tp.L, tp.tl, tq.dev, tq.L, tq.tl, tp.alpha);
+  }
 }
 
 template <int RANK>
@@ -1017,7 +1096,8 @@ hipError_t lq_logquant(LqState &st, const float *F, int64_t rows, int r, double 
   hipError_t e = tables(st, alpha, bits, s, &tab);
   if (e != hipSuccess) return e;
   ColJob j{F, rows, r, codes, colmax, Fhat, nullptr};
-  hipLaunchKernelGGL(k_lq_quant_cols, dim3(r), dim3(1024), 0, s, j, j, r, tab->dev, tab->L);
+  hipLaunchKernelGGL(k_lq_quant_cols, dim3(r), dim3(1024), 0, s, j, j, r, tab->dev, tab->L,
+                     tab->alpha, tab->tl);
   return hipGetLastError();
 }
 

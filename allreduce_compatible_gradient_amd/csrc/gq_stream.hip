@@ -15,17 +15,21 @@
 // one contiguous block (1 KB of fp32, 256 B of int8 codes, ...): whole cache lines, never the
 // half-line writes a 32-byte-per-lane layout produces.  Gradient loads are non-temporal (they
 // are read once; keeping them out of the 256 MB Infinity Cache lets a pure read stream run at
-// ~7 TB/s on MI355X).  A 256-thread block walks tiles with a grid-stride loop, so a fixed grid
-// covers all 256 CUs whatever the size; tiles never cross segments, so the per-segment scale
-// is one scalar load per tile.  Codes are packed in registers.  No MFMA: there is no
+// ~7 TB/s on MI355X).  The element-wise kernels launch one 256-thread block per tile, in the
+// XCD order of xcd_tile (each XCD streams its own contiguous eighth of the buffers), with
+// 2048-element tiles where several read streams mix with a write stream and 32 KB of input
+// (8192 fp32 or 16384 bf16 elements) for one read and one write stream; tiles never cross
+// segments, so the per-segment scale is one scalar load per tile.  The norm pass (read only) keeps a fixed grid striding over 65536-element
+// tiles, one fp64 partial each.  Codes are packed in registers.  No MFMA: there is no
 // contraction here.  Reductions are fixed-order (no float atomics): results are bit-stable.
 //
 // Arithmetic contract (each step is one IEEE operation, so any conforming implementation of
 // the same definition gets the same bits; compiled with -ffp-contract=off and IEEE fp32
 // denormals): u = |x| * inv is one fp32 multiply; floor, fraction and the scaling of the
-// fraction by 2^32 are exact; the draw r = h * 2^-32 satisfies r < p exactly when
-// h < ceil(p * 2^32), which is the integer comparison used here.  Uniform sums are carried
-// in fp32, which is exact because |sum| <= 64 * 127 < 2^24.
+// fraction by 2^32 are exact; the draw is r = fp32(h) * 2^-32, the 32-bit hash h converted to
+// fp32 (round to nearest even, one v_cvt_f32_u32) and scaled exactly, so r < p is the fp32
+// comparison fp32(h) < p * 2^32.  Uniform sums are carried in fp32, which is exact because
+// |sum| <= 64 * 127 < 2^24.
 #include <float.h>
 #include <math.h>
 
@@ -73,6 +77,18 @@ __device__ __forceinline__ void tile_of(const TileView &tv, int64_t t, int tile_
 __device__ __forceinline__ int64_t seg_first_tile(const TileView &tv, int g) {
   if (tv.seg_tile_start == nullptr) return g == 0 ? 0 : tv.ntiles;
   return tv.seg_tile_start[g];
+}
+
+// Block -> tile order of the element-wise kernels, which launch one block per tile.  The
+// hardware hands workgroups to the 8 XCDs in turn (block b to XCD b mod 8), so giving block b
+// tile (b mod 8) * q + b / 8 (q = ntiles / 8; the last ntiles mod 8 tiles in order) makes every
+// XCD stream its own contiguous eighth of each buffer, and blocks in dispatch order keep each
+// of those regions' active window compact; with consecutive tiles spread over the XCDs, or a
+// fixed grid striding over the whole buffer, the streams of reads mixed with a stream of
+// writes ran 10-15% slower.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t ntiles) {
+  const int64_t q = ntiles >> 3;
+  return b < 8 * q ? (b & 7) * q + (b >> 3) : b;
 }
 
 // Offset within the tile of part j of this lane in chunk ci.
@@ -409,8 +425,7 @@ __device__ __forceinline__ float quant_uniform_mag(float x, float inv, float sf,
   const float u = fminf(fabsf(x) * inv, sf);  // NaN -> s
   const float fl = floorf(u);
   const float p = u - fl;                     // exact
-  const uint32_t c = (uint32_t)ceilf(p * 4294967296.0f);
-  return h < c ? ceilf(u) : fl;               // p > 0 whenever h < c, so ceil(u) = fl + 1
+  return (float)h < p * 4294967296.0f ? ceilf(u) : fl;  // p > 0 then, so ceil(u) = fl + 1
 }
 
 // Exponential grid: index j in [0, E] of the level (level j > 0 is 2^(j-E)).  Above the
@@ -424,10 +439,10 @@ __device__ __forceinline__ uint32_t quant_exp_index(float x, float inv, int E, f
   const uint32_t b = __float_as_uint(u);
   const int32_t jn = (int32_t)(b >> 23) - (127 - E);  // <= 0 below the lowest level
   const bool low = jn <= 0;
-  const uint32_t c_hi = (b & 0x7FFFFFu) << 9;
-  const uint32_t c_lo = (uint32_t)ceilf(u * lo_scale);
-  const uint32_t c = low ? c_lo : c_hi;
-  return (low ? 0u : (uint32_t)jn) + (h < c ? 1u : 0u);
+  const float c_hi = (float)((b & 0x7FFFFFu) << 9);  // exact: 23 significant bits
+  const float c_lo = u * lo_scale;
+  const float c = low ? c_lo : c_hi;
+  return (low ? 0u : (uint32_t)jn) + ((float)h < c ? 1u : 0u);
 }
 
 // Code field of a uniform level (signed, two's complement in `bits`).
@@ -497,7 +512,7 @@ __global__ __launch_bounds__(kBlock) void k_norm_partial(NormArgs a) {
   for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, kNormTile, begin, len, seg);
+    tile_of(a.tv, t, a.tile, begin, len, seg);
     const int nch = (len + kChunk - 1) / kChunk;
     double acc = 0.0;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
@@ -561,6 +576,11 @@ __global__ void k_norm_scale(NormArgs a) {
 }
 
 // ================================================================ quantise + pack (one worker)
+// With the fused pass's fast path: a part whose elements, in every active lane, lie below the
+// lowest nonzero level (the lane's largest magnitude, NaN-propagating, against the tile's
+// threshold) has levels 0 and +-1 only, and it rounds up when fp32(h) < fl(|x| * inv) * 2^32
+// (uniform) or fl(|x| * inv) * 2^(E+31) (exponential): bit for bit the general path's codes
+// without its clamp, floor, fraction and exponent split.
 template <int DT, int GRID>
 __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
   constexpr int P = DT == 0 ? 4 : 8;
@@ -568,11 +588,15 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float sf = (float)a.levels;
   const float lo_scale = ldexpf(1.0f, a.levels + 31);
-  for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
+  const float up_scale = GRID == 0 ? 4294967296.0f : lo_scale;
+  const float bound = GRID == 0 ? 1.0f : ldexpf(1.0f, 1 - a.levels);
+  for (int64_t b = blockIdx.x; b < a.tv.ntiles; b += gridDim.x) {
+    const int64_t t = xcd_tile(b, a.tv.ntiles);
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, kTile, begin, len, seg);
+    tile_of(a.tv, t, quant_tile(DT), begin, len, seg);
     const SegQ q = seg_quant<GRID>(a.scale[seg], a.levels);
+    const float fast_below = q.valid ? below_bound(q.inv, bound) : 0.0f;
     const int nch = (len + kChunk - 1) / kChunk;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
 #pragma unroll
@@ -586,6 +610,22 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
           float x[P];
           load_part<DT, P>(a.grad, e0, cnt, x);
           const uint32_t ctr = a.index_base + (uint32_t)e0;
+          float big = 0.0f;  // a part's missing elements are loaded as zeros
+#pragma unroll
+          for (int e = 0; e < P; ++e) big = max_abs(big, x[e]);
+          if (__all(big < fast_below)) {
+#pragma unroll
+            for (int e = 0; e < P; ++e) {
+              const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+              const uint32_t up = (float)h < fabsf(x[e]) * q.inv * up_scale ? 1u : 0u;
+              if constexpr (GRID == 0)
+                c[e] = (sign_bit(x[e]) ? (0u - up) : up) & ((1u << a.bits) - 1u);
+              else
+                c[e] = exp_code(up, x[e], a.bits);
+            }
+            store_codes<P>(a.codes, e0, cnt, a.bits, c);
+            continue;
+          }
 #pragma unroll
           for (int e = 0; e < P; ++e) {
             const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
@@ -610,11 +650,12 @@ template <int GRID, int P>
 __global__ __launch_bounds__(kBlock) void k_accumulate(AccArgs a) {
   constexpr int NP = kChunk / (64 * P);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const TileView tv{nullptr, nullptr, (a.n + kTile - 1) / kTile, a.n, 1};
-  for (int64_t t = blockIdx.x; t < tv.ntiles; t += gridDim.x) {
+  const TileView tv{nullptr, nullptr, (a.n + kTileMix - 1) / kTileMix, a.n, 1};
+  for (int64_t b = blockIdx.x; b < tv.ntiles; b += gridDim.x) {
+    const int64_t t = xcd_tile(b, tv.ntiles);
     int64_t begin;
     int len, seg;
-    tile_of(tv, t, kTile, begin, len, seg);
+    tile_of(tv, t, kTileMix, begin, len, seg);
     const int nch = (len + kChunk - 1) / kChunk;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
 #pragma unroll
@@ -643,10 +684,11 @@ template <int P>
 __global__ __launch_bounds__(kBlock) void k_dequantize(DequantArgs a) {
   constexpr int NP = kChunk / (64 * P);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
+  for (int64_t b = blockIdx.x; b < a.tv.ntiles; b += gridDim.x) {
+    const int64_t t = xcd_tile(b, a.tv.ntiles);
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, kTile, begin, len, seg);
+    tile_of(a.tv, t, kTileMix, begin, len, seg);
     const float f = seg_decode(a.scale[seg], a.denom);
     const int nch = (len + kChunk - 1) / kChunk;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
@@ -768,10 +810,11 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float sf = (float)a.levels;
   const float lo_scale = ldexpf(1.0f, a.levels + 31);
-  for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
+  for (int64_t b = blockIdx.x; b < a.tv.ntiles; b += gridDim.x) {
+    const int64_t t = xcd_tile(b, a.tv.ntiles);
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, kTile, begin, len, seg);
+    tile_of(a.tv, t, quant_tile(DT), begin, len, seg);
     const SegQ q = seg_quant<GRID>(a.scale[seg], a.levels);
     // the fused pass's fast path: a part whose elements, in every active lane, lie below the
     // lowest nonzero level has levels 0 and +-1 only (bit for bit the general path's)
@@ -804,8 +847,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
             for (int e = 0; e < P; ++e) {
               const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
               const float up = DT == 1 ? fabsf(x[e]) * inv_up : fabsf(x[e]) * q.inv * up_scale;
-              const uint32_t c = (uint32_t)ceilf(up);
-              const int32_t lin = h < c ? (x[e] < 0.0f ? -1 : 1) : 0;
+              const int32_t lin = (float)h < up ? (x[e] < 0.0f ? -1 : 1) : 0;
               v[e] = (uint32_t)(lin + a.offset);
             }
             store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
@@ -837,10 +879,11 @@ template <int P, int WB>
 __global__ __launch_bounds__(kBlock) void k_dequantize_wire(WireDequantArgs a) {
   constexpr int NP = kChunk / (64 * P);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
+  for (int64_t b = blockIdx.x; b < a.tv.ntiles; b += gridDim.x) {
+    const int64_t t = xcd_tile(b, a.tv.ntiles);
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, kTile, begin, len, seg);
+    tile_of(a.tv, t, kTileMix, begin, len, seg);
     const float f = seg_decode(a.scale[seg], a.denom);
     const int nch = (len + kChunk - 1) / kChunk;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
@@ -870,8 +913,8 @@ __global__ __launch_bounds__(kBlock) void k_dequantize_wire(WireDequantArgs a) {
 // Fast path (FAST, without code stores): when one worker's elements in every lane of the wave
 // have |x| below fast_below -- so that fl(|x| * inv) is below the lowest nonzero level (1 on
 // the uniform grid, 2^(1-E) on the exponential one), as for almost every element of a large
-// tensor -- the level is 0 or 1 and the round-up threshold is ceil(fl(|x| * inv) * 2^32)
-// (uniform) or ceil(fl(|x| * inv) * 2^(E+31)) (exponential), so the clamp, floor, fraction,
+// tensor -- the level is 0 or 1 and the draw rounds up when fp32(h) < fl(|x| * inv) * 2^32
+// (uniform) or fl(|x| * inv) * 2^(E+31) (exponential), so the clamp, floor, fraction,
 // exponent split and level selection of the general path drop out.  The results are the
 // general path's bit for bit (adding copysign(0, x) or +0 to a sum that starts at +0 gives the
 // same sum).  Used on the exponential grid (ResNet-50's 161 tensors x 8 workers: 0.190 ->
@@ -925,11 +968,10 @@ __device__ __forceinline__ void fused_compute(const FusedArgs &a, int k0, int kn
           const uint32_t h = fmix32_tail(am[j][e] ^ km);
           const float up = FOLD ? fabsf(xv) * inv_up
                                 : fabsf(xv) * q.inv * (GRID == 0 ? 4294967296.0f : lo_scale);
-          const uint32_t c = (uint32_t)ceilf(up);
           if constexpr (GRID == 0)
-            accf[j][e] += h < c ? copysignf(1.0f, xv) : 0.0f;
+            accf[j][e] += (float)h < up ? copysignf(1.0f, xv) : 0.0f;
           else
-            acci[j][e] += h < c ? (xv < 0.0f ? -1 : 1) : 0;
+            acci[j][e] += (float)h < up ? (xv < 0.0f ? -1 : 1) : 0;
         }
       continue;
     }
@@ -991,26 +1033,16 @@ void k_fused(FusedArgs a) {
   const int K = KT > 0 ? KT : a.K;
   const float sf = (float)a.levels;
   const float lo_scale = ldexpf(1.0f, a.levels + 31);
-  for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
+  for (int64_t b = blockIdx.x; b < a.tv.ntiles; b += gridDim.x) {
+    const int64_t t = xcd_tile(b, a.tv.ntiles);
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, kTile, begin, len, seg);
-    const float S = a.scale[seg];
-    const SegQ q = seg_quant<GRID>(S, a.levels);
-    const float f = seg_decode(S, a.denom);
-    // In the double-buffered pass the fast path scales |x| by inv_up = inv * 2^32 (or
-    // inv * lo_scale) in one product.  Below the threshold fl(|x| * inv) < 1, and scaling it by
-    // that power of two is exact, so the one product equals it whenever fl(|x| * inv) is a
-    // normal number; when it is subnormal both ceilings are 1 (products below 2^-126 * 2^(E+31)
-    // <= 1, hence E <= 95), and they differ only if fl(|x| * inv) underflows to zero for a
-    // nonzero x, which inv >= 2^-16 rules out for bf16 (whose smallest magnitude is 2^-133).
-    // A tile whose scale fails these conditions takes the general path throughout.
-    const float inv_up = q.inv * (GRID == 0 ? 4294967296.0f : lo_scale);
-    const bool fold_ok = q.inv >= 0x1p-16f && inv_up < 0x1p127f && (GRID == 0 || a.levels <= 95);
-    const float fast_below =
-        q.valid && (GRID == 1 || PIPE) && (!PIPE || fold_ok)
-            ? below_bound(q.inv, GRID == 1 ? ldexpf(1.0f, 1 - a.levels) : 1.0f)
-            : 0.0f;
+    tile_of(a.tv, t, kTileMix, begin, len, seg);
+    const SegConst sc = a.segc[seg];
+    const SegQ q{sc.inv, sc.inv > 0.0f};
+    const float f = sc.f;
+    const float inv_up = sc.inv_up;
+    const float fast_below = sc.fast_below;
     const int nch = (len + kChunk - 1) / kChunk;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
       int64_t e0[NP];
@@ -1118,7 +1150,7 @@ __global__ __launch_bounds__(kBlock) void k_absmax_partial(NormArgs a) {
   for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, kNormTile, begin, len, seg);
+    tile_of(a.tv, t, a.tile, begin, len, seg);
     const int nch = (len + kChunk - 1) / kChunk;
     unsigned m = 0u;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
@@ -1255,10 +1287,11 @@ void k_worker_mean(WorkerMeanArgs a) {
   const int K = KT > 0 ? KT : a.K;
   const float sf = (float)a.levels;
   const float lo_scale = ldexpf(1.0f, a.levels + 31);
-  for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
+  for (int64_t b = blockIdx.x; b < a.tv.ntiles; b += gridDim.x) {
+    const int64_t t = xcd_tile(b, a.tv.ntiles);
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, kTile, begin, len, seg);
+    tile_of(a.tv, t, kTileMix, begin, len, seg);
     const int nch = (len + kChunk - 1) / kChunk;
     // lane k holds worker k's (s/S or 1/S, decode factor) for this tile's segment (K <= 64)
     const float2 fl = a.fac[(int64_t)(lane < K ? lane : 0) * a.tv.nseg + seg];
@@ -1313,10 +1346,11 @@ __global__ __launch_bounds__(kBlock) void k_decode_workers(DecodeWorkersArgs a) 
   constexpr int P = 8;
   constexpr int NP = kChunk / (64 * P);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int64_t t = blockIdx.x; t < a.tv.ntiles; t += gridDim.x) {
+  for (int64_t b = blockIdx.x; b < a.tv.ntiles; b += gridDim.x) {
+    const int64_t t = xcd_tile(b, a.tv.ntiles);
     int64_t begin;
     int len, seg;
-    tile_of(a.tv, t, kTile, begin, len, seg);
+    tile_of(a.tv, t, kTileMix, begin, len, seg);
     const float fl = a.fac[(int64_t)(lane < a.K ? lane : 0) * a.tv.nseg + seg].y;
     const int nch = (len + kChunk - 1) / kChunk;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
@@ -1372,7 +1406,7 @@ hipError_t launch_global_norm(const NormArgs &a, int dtype, hipStream_t s) {
 
 hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, hipStream_t s) {
   if (a.tv.ntiles == 0) return hipSuccess;
-  dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+  dim3 g(grid_for(a.tv.ntiles, kGridAll));
   if (dtype == 0 && grid == 0) hipLaunchKernelGGL((k_quantize_pack<0, 0>), g, dim3(kBlock), 0, s, a);
   if (dtype == 0 && grid == 1) hipLaunchKernelGGL((k_quantize_pack<0, 1>), g, dim3(kBlock), 0, s, a);
   if (dtype == 1 && grid == 0) hipLaunchKernelGGL((k_quantize_pack<1, 0>), g, dim3(kBlock), 0, s, a);
@@ -1381,9 +1415,9 @@ hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, hipStre
 }
 
 hipError_t launch_accumulate(const AccArgs &a, int grid, hipStream_t s) {
-  const int64_t ntiles = (a.n + kTile - 1) / kTile;
+  const int64_t ntiles = (a.n + kTileMix - 1) / kTileMix;
   if (ntiles == 0) return hipSuccess;
-  dim3 g(grid_for(ntiles, kStreamGrid));
+  dim3 g(grid_for(ntiles, kGridAll));
   if (a.acc_bits == 16) {
     if (grid == 0) hipLaunchKernelGGL((k_accumulate<0, 8>), g, dim3(kBlock), 0, s, a);
     else hipLaunchKernelGGL((k_accumulate<1, 8>), g, dim3(kBlock), 0, s, a);
@@ -1396,7 +1430,7 @@ hipError_t launch_accumulate(const AccArgs &a, int grid, hipStream_t s) {
 
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s) {
   if (a.tv.ntiles == 0) return hipSuccess;
-  dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+  dim3 g(grid_for(a.tv.ntiles, kGridAll));
   // 16-byte accesses on both sides: int16 -> bf16 with 8 elements per part, else 4
   if (a.acc_bits == 16 && a.out_dtype == 1)
     hipLaunchKernelGGL(k_dequantize<8>, g, dim3(kBlock), 0, s, a);
@@ -1415,7 +1449,7 @@ static void launch_qw(const WireQuantArgs &a, int wb, dim3 g, hipStream_t s) {
 hipError_t launch_quantize_wire(const WireQuantArgs &a, int dtype, int grid, int wb,
                                 hipStream_t s) {
   if (a.tv.ntiles == 0) return hipSuccess;
-  const dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+  const dim3 g(grid_for(a.tv.ntiles, kGridAll));
   if (dtype == 0 && grid == 0) launch_qw<0, 0>(a, wb, g, s);
   if (dtype == 0 && grid == 1) launch_qw<0, 1>(a, wb, g, s);
   if (dtype == 1 && grid == 0) launch_qw<1, 0>(a, wb, g, s);
@@ -1425,7 +1459,7 @@ hipError_t launch_quantize_wire(const WireQuantArgs &a, int dtype, int grid, int
 
 hipError_t launch_dequantize_wire(const WireDequantArgs &a, int wb, hipStream_t s) {
   if (a.tv.ntiles == 0) return hipSuccess;
-  const dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+  const dim3 g(grid_for(a.tv.ntiles, kGridAll));
   // 16-byte output stores: 8 elements per part for bf16 output, 4 for fp32
   if (a.out_dtype == 1) {
     if (wb == 1) hipLaunchKernelGGL((k_dequantize_wire<8, 1>), g, dim3(kBlock), 0, s, a);
@@ -1437,6 +1471,33 @@ hipError_t launch_dequantize_wire(const WireDequantArgs &a, int wb, hipStream_t 
     if (wb == 4) hipLaunchKernelGGL((k_dequantize_wire<4, 4>), g, dim3(kBlock), 0, s, a);
   }
   return hipGetLastError();
+}
+
+// The per-segment constants of k_fused.  In the double-buffered pass (pipe) the fast path
+// scales |x| by inv_up = inv * 2^32 (or inv * 2^(E+31)) in one product.  Below the threshold
+// fl(|x| * inv) < 1, and scaling it by that power of two is exact, so the one product equals
+// it whenever fl(|x| * inv) is a normal number; when it is subnormal both thresholds lie in
+// (0, 1] (products below 2^-126 * 2^(E+31) <= 1, hence E <= 95), where fp32(h) < threshold
+// holds for h = 0 alone, so the two round up alike; they differ only if
+// fl(|x| * inv) underflows to zero for a nonzero x, which inv >= 2^-16 rules out for bf16
+// (whose smallest magnitude is 2^-133).  A segment whose scale fails these conditions takes
+// the general path throughout (fast_below = 0).  The fast path runs on the exponential grid,
+// and on the uniform grid in the double-buffered pass.
+template <int GRID>
+__global__ void k_seg_consts(const float *scale, int nseg, int levels, double denom, int pipe,
+                             SegConst *out) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= nseg) return;
+  const float S = scale[g];
+  const SegQ q = seg_quant<GRID>(S, levels);
+  const float lo_scale = ldexpf(1.0f, levels + 31);
+  const float inv_up = q.inv * (GRID == 0 ? 4294967296.0f : lo_scale);
+  const bool fold_ok = q.inv >= 0x1p-16f && inv_up < 0x1p127f && (GRID == 0 || levels <= 95);
+  const float fast_below =
+      q.valid && (GRID == 1 || pipe) && (!pipe || fold_ok)
+          ? below_bound(q.inv, GRID == 1 ? ldexpf(1.0f, 1 - levels) : 1.0f)
+          : 0.0f;
+  out[g] = SegConst{q.valid ? q.inv : 0.0f, seg_decode(S, denom), fast_below, inv_up};
 }
 
 template <int DT, int GRID, bool STORE>
@@ -1461,7 +1522,16 @@ static void launch_fused_s(const FusedArgs &a, int dtype, int grid, dim3 g, hipS
 
 hipError_t launch_fused(const FusedArgs &a, int dtype, int grid, hipStream_t s) {
   if (a.tv.ntiles == 0) return hipSuccess;
-  dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+  // the double-buffered pass: bf16, 16 workers, no code stores
+  const int pipe = dtype == 1 && a.K == 16 && !a.store_codes;
+  const dim3 gs((unsigned)((a.tv.nseg + 255) / 256));
+  if (grid == 0)
+    hipLaunchKernelGGL(k_seg_consts<0>, gs, dim3(256), 0, s, a.scale, a.tv.nseg, a.levels,
+                       a.denom, pipe, a.segc);
+  else
+    hipLaunchKernelGGL(k_seg_consts<1>, gs, dim3(256), 0, s, a.scale, a.tv.nseg, a.levels,
+                       a.denom, pipe, a.segc);
+  dim3 g(grid_for(a.tv.ntiles, kGridAll));
   if (a.store_codes)
     launch_fused_s<true>(a, dtype, grid, g, s);
   else
@@ -1507,7 +1577,7 @@ hipError_t launch_worker_mean(const WorkerMeanArgs &a, const float *scales, int 
     hipLaunchKernelGGL(k_worker_factors<1>, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,
                        scales, count, a.levels, a.denom, fac);
   if (a.tv.ntiles > 0) {
-    dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+    dim3 g(grid_for(a.tv.ntiles, kGridAll));
     if (dtype == 0 && grid == 0) launch_worker_mean_k<0, 0>(a, g, s);
     if (dtype == 0 && grid == 1) launch_worker_mean_k<0, 1>(a, g, s);
     if (dtype == 1 && grid == 0) launch_worker_mean_k<1, 0>(a, g, s);
@@ -1527,7 +1597,7 @@ hipError_t launch_decode_workers(const DecodeWorkersArgs &a, const float *scales
     hipLaunchKernelGGL(k_worker_factors<1>, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,
                        scales, count, levels, denom, fac);
   if (a.tv.ntiles > 0) {
-    dim3 g(grid_for(a.tv.ntiles, kStreamGrid));
+    dim3 g(grid_for(a.tv.ntiles, kGridAll));
     if (grid == 0)
       hipLaunchKernelGGL(k_decode_workers<0>, g, dim3(kBlock), 0, s, a);
     else

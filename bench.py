@@ -356,36 +356,57 @@ def rows_baselines(torch, gq, W, grads, w, row, it):
 
 
 def measure_ceilings(torch, grads, out):
-    """Bandwidth of a plain stream with the fused pass's memory pattern and with the norm
-    pass's (libgq_ceiling.so): K fp32 reads + 1 fp32 write, and K fp32 reads; and of a plain
-    one-read, one-write copy with the same lane map."""
+    """Bandwidth of plain streams (libgq_ceiling.so): K fp32 reads + 1 fp32 write (the fused
+    pass's streams), K fp32 reads (the norm pass's), and a one-read, one-write copy, each the
+    best of the kernels' lane map on 15 fixed grids and of patterns that are not the kernels'
+    own (element-wise float4 groups on a grid covering the buffers once, U = 1, 2, 4 windows;
+    one block per 2048- or 8192-element tile in XCD order)."""
     import ctypes as C
     from allreduce_compatible_gradient_amd import build as B
     lib = C.CDLL(B.CEILING_LIB)
     lib.gqc_stream.restype = C.c_int
     lib.gqc_stream.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_void_p,
                                C.c_int, C.c_int, C.c_void_p]
+    lib.gqc_stream_pattern.restype = C.c_int
+    lib.gqc_stream_pattern.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_void_p,
+                                       C.c_int, C.c_int, C.c_void_p]
     K, n = len(grads), grads[0].numel()
     srcs = (C.c_void_p * K)(*[g.data_ptr() for g in grads])
     sink = torch.zeros(4, dtype=torch.float32, device="cuda")
     stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
     src1 = (C.c_void_p * 1)(grads[0].data_ptr())
     res = {}
-    for name, kk, o, nbytes in (
-            ("read_K%d_write1" % K, K, out.data_ptr(), (K + 1) * (n // 2048) * 8192),
-            ("read_K%d" % K, K, None, K * (n // 2048) * 8192),
-            ("copy_read1_write1", 1, out.data_ptr(), 2 * (n // 2048) * 8192)):
-        best = 0.0
+    detail = {}
+    for name, kk, o, streams in (
+            ("read_K%d_write1" % K, K, out.data_ptr(), K + 1),
+            ("read_K%d" % K, K, None, K),
+            ("copy_read1_write1", 1, out.data_ptr(), 2)):
+        best, how = 0.0, ""
+        src = srcs if kk == K else src1
         for grid in (1024, 2048, 4096, 8192, 16384):
             for chunk in (1, 2, 4):
                 def run():
-                    assert lib.gqc_stream(srcs if kk == K else src1, kk, n, o, sink.data_ptr(),
-                                          grid, chunk, stream) == 0
+                    assert lib.gqc_stream(src, kk, n, o, sink.data_ptr(), grid, chunk,
+                                          stream) == 0
                 ms = time_calls(torch, run, 3)
-                best = max(best, nbytes / (ms * 1e-3) / 1e9)
+                gbs = streams * (n // 2048) * 8192 / (ms * 1e-3) / 1e9
+                if gbs > best:
+                    best, how = gbs, "lane map, grid %d, %d KB per wave and stream" % (grid, chunk)
+        for pattern, params in ((1, (1, 2, 4)), (2, (2048, 8192))):
+            for prm in params:
+                def run():
+                    assert lib.gqc_stream_pattern(src, kk, n, o, sink.data_ptr(), pattern, prm,
+                                                  stream) == 0
+                ms = time_calls(torch, run, 3)
+                gbs = streams * (n // 16384) * 65536 / (ms * 1e-3) / 1e9
+                if gbs > best:
+                    best, how = gbs, ("element-wise, %d window(s)" % prm if pattern == 1
+                                      else "one block per %d-element tile, XCD order" % prm)
         res[name] = round(best, 1)
-        log("ceiling %-22s %8.1f GB/s (%.1f%% of HBM), best of 15 launch shapes"
-            % (name, res[name], 100 * res[name] / HBM_PEAK_GBS))
+        detail[name] = how
+        log("ceiling %-22s %8.1f GB/s (%.1f%% of HBM): %s"
+            % (name, res[name], 100 * res[name] / HBM_PEAK_GBS, how))
+    res["best_pattern"] = detail
     return res
 
 

@@ -106,7 +106,8 @@ gq_status gq_global_norm(gq_ctx *ctx, const void *const *grads, int32_t K, int32
  * with GQ_EINVAL before anything is enqueued: at most 256 segments when `offsets` is given,
  * and 8 * K * (ntiles + nseg) bytes (+ 16 * ntiles + 8 * (nseg + 1) for a segment table, each
  * part rounded up to 256 bytes) within the buffer, ntiles = sum over segments of
- * ceil(len / 65536) -- e.g. one segment of n elements fits for 8 workers while n <= 8.5e9 and
+ * ceil(len / T), T the norm's tile (65536 elements, smaller for inputs too small to fill the
+ * GPU with such tiles) -- e.g. one segment of n elements fits for 8 workers while n <= 8.5e9 and
  * for 64 workers while n <= 1.07e9.  Every call on a
  * GPU uses the same buffer: calls that may overlap on one GPU (different streams, different
  * threads) race and must be ordered by the caller.  Nothing in the buffer has to start at
@@ -124,8 +125,9 @@ gq_status gq_global_norm_noalloc(gq_ctx *ctx, const void *const *grads, int32_t 
  *   exponential: inv_g = fp32(1 / S_g); u <- min(u, 1); j = largest level index with
  *                level_j <= u (level_0 = 0, level_j = 2^(j-E)); p = (u - level_j) /
  *                (level_{j+1} - level_j); j <- j + [r < p]; code = sign bit << (bits-1) | j
- * where r = fmix32((index_base + i) XOR key_k) * 2^-32 and key_k is the low 32 bits of
- * SplitMix64 output k+1 from state `seed`; sign(x) is x's sign bit on both grids, so a NaN
+ * where r = fp32(fmix32((index_base + i) XOR key_k)) * 2^-32 (the 32-bit hash rounded to the
+ * nearest fp32, ties to even, then scaled exactly) and key_k is the low 32 bits of SplitMix64
+ * output k+1 from state `seed`; sign(x) is x's sign bit on both grids, so a NaN
  * element (possible only under a caller-given finite scale) takes the top level with the sign
  * its bit gives it.  A segment whose scale is not a positive finite number (or whose inv_g
  * overflows) gets all-zero codes.  Element 2t of a 4-bit buffer sits in

@@ -44,7 +44,8 @@ uint64_t orc_splitmix64_next(uint64_t *state);
 uint32_t orc_fmix32(uint32_t h);
 /* Key of worker k: low 32 bits of SplitMix64 output number k+1 from state `seed`. */
 uint32_t orc_worker_key(uint64_t seed, uint32_t worker);
-/* Uniform draw in [0,1): fmix32(counter XOR key) * 2^-32 (exact in double). */
+/* Uniform draw in [0,1]: fp32(fmix32(counter XOR key)) * 2^-32, the hash rounded to the
+ * nearest fp32 (ties to even), then scaled (exact in double). */
 double orc_uniform(uint32_t key, uint32_t counter);
 /* out[t] = fmix32((counter0 + t) XOR key) for t < cnt (raw 32-bit hashes). */
 void orc_hash_fill(uint32_t key, uint32_t counter0, int64_t cnt, uint32_t *out);

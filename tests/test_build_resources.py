@@ -22,7 +22,8 @@ def test_report_covers_the_kernels(resources):
     names = " ".join(resources)
     for k in ("k_fused", "k_norm_partial", "k_quantize_pack", "k_accumulate", "k_dequantize",
               "k_quantize_wire", "k_worker_mean", "k_decode_workers", "k_lq_ef_mq",
-              "k_lq_solve", "k_lq_mtp", "k_lq_ef_update"):
+              "k_lq_solve", "k_lq_mtp", "k_lq_qsum", "k_lq_ef_update_q", "k_lq_quant_elems",
+              "k_lq_mean_ef", "k_lq_quant_cols", "k_seg_consts"):
         assert k in names, k
 
 

@@ -30,8 +30,12 @@ MUTATIONS = [
     ("fmix32 constant", "h *= 0xC2B2AE35U;", "h *= 0xC2B2AE37U;"),
     ("worker key is output k, not k+1", "for (j = 0; j <= worker; ++j)",
      "for (j = 0; j < worker; ++j)"),
-    ("counter added to key, not xor-ed", "return (double)orc_fmix32(counter ^ key) * 0x1p-32;",
-     "return (double)orc_fmix32(counter + key) * 0x1p-32;"),
+    ("counter added to key, not xor-ed", "const float h = (float)orc_fmix32(counter ^ key);",
+     "const float h = (float)orc_fmix32(counter + key);"),
+    ("draw: hash not rounded to fp32", "const float h = (float)orc_fmix32(counter ^ key);",
+     "const double h = (double)orc_fmix32(counter ^ key);"),
+    ("draw: hash truncated to fp32", "const float h = (float)orc_fmix32(counter ^ key);",
+     "const float h = (float)(orc_fmix32(counter ^ key) & ~((1u << (orc_fmix32(counter ^ key) >= (1u << 24) ? 8 : 0)) - 1u));"),
     ("norm: signed square", "acc += v * v;", "acc += v * fabs(v);"),
     ("norm: sum over workers, not max", "best = nrm;", "best += nrm;"),
     ("uniform: scale 1/S, not s/S", "inv = (float)s / S;", "inv = 1.0f / S;"),

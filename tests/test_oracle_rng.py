@@ -1,8 +1,11 @@
 """Pins of the oracle's counter-based generator (CPU only).
 
-The stochastic rounding draws r = fmix32(counter XOR key_k) * 2^-32 with key_k the low 32 bits
-of SplitMix64 output k+1 from the step seed.  Both generators are pinned to published
-known-answer values (tests/golden/rng_kat.json); the draw is then checked statistically.
+The stochastic rounding draws r = fp32(fmix32(counter XOR key_k)) * 2^-32 -- the 32-bit hash
+rounded to the nearest fp32 (ties to even), scaled exactly -- with key_k the low 32 bits of
+SplitMix64 output k+1 from the step seed.  Both generators are pinned to published
+known-answer values (tests/golden/rng_kat.json); the rounding of the hash is pinned on chosen
+hash values (reached through the inverse of the finaliser, written here); the draw is then
+checked statistically.
 """
 import json
 import os
@@ -58,10 +61,57 @@ def test_fmix32_via_murmur3_known_answers(orc, case):
     assert got == int(case["hash"], 16)
 
 
-def test_uniform_is_exact_scaling(orc):
+def _inv_fmix32(h: int) -> int:
+    """The input whose fmix32 is h: each step of the finaliser undone in reverse order."""
+    h ^= h >> 16                              # x ^ (x >> 16) is its own inverse
+    h = (h * pow(0xC2B2AE35, -1, 1 << 32)) & M32
+    x = h                                     # undo x ^ (x >> 13): fixed point, 3 rounds
+    for _ in range(3):
+        x = h ^ (x >> 13)
+    h = (x * pow(0x85EBCA6B, -1, 1 << 32)) & M32
+    return h ^ (h >> 16)
+
+
+def _counter_for_hash(orc, key: int, h: int) -> int:
+    c = _inv_fmix32(h) ^ key
+    assert orc.fmix32(c ^ key) == h
+    return c
+
+
+def test_uniform_is_scaled_nearest_fp32_of_hash(orc):
     key = orc.worker_key(7, 3)
     for c in (0, 1, 12345, M32):
-        assert orc.uniform(key, c) == orc.fmix32(c ^ key) / 2.0 ** 32
+        assert orc.uniform(key, c) == float(np.float32(orc.fmix32(c ^ key))) / 2.0 ** 32
+
+
+@pytest.mark.parametrize("h,nearest", [
+    (0, 0), (1, 1), ((1 << 24) - 1, (1 << 24) - 1),
+    ((1 << 24) + 1, 1 << 24),                 # halfway: ties to the even neighbour
+    ((1 << 24) + 3, (1 << 24) + 4),           # halfway: ties to the even neighbour
+    ((1 << 31) + 127, 1 << 31),               # spacing 256: 127 rounds down
+    ((1 << 31) + 129, (1 << 31) + 256),       # 129 rounds up
+    ((1 << 31) + 384, (1 << 31) + 512),       # halfway between +256 (odd) and +512 (even)
+    (M32 - 127, 1 << 32), (M32, 1 << 32),     # the top hashes round to 2^32: r = 1
+])
+def test_uniform_rounds_the_hash_to_nearest_even_fp32(orc, h, nearest):
+    key = orc.worker_key(11, 2)
+    assert orc.uniform(key, _counter_for_hash(orc, key, h)) == nearest / 2.0 ** 32
+
+
+def test_round_up_compares_the_rounded_hash(orc):
+    # s = 1, S = 1, x = 1/2 + 2^-24: u = x, level 0, p = u, p * 2^32 = 2^31 + 256.  The hash
+    # 2^31 + 200 is below that threshold but rounds to it (spacing 256), so it does not round
+    # up; 2^31 + 100 rounds to 2^31 and does.
+    key = orc.worker_key(5, 1)
+    x = float(np.float32(0.5 + 2.0 ** -24))
+    assert orc.quant_one(0, 1, x, 1.0, key, _counter_for_hash(orc, key, (1 << 31) + 200)) == 0
+    assert orc.quant_one(0, 1, x, 1.0, key, _counter_for_hash(orc, key, (1 << 31) + 100)) == 1
+    assert orc.quant_one(0, 1, -x, 1.0, key, _counter_for_hash(orc, key, (1 << 31) + 100)) == -1
+    # exponential grid, E = 2 (levels 1/2, 1): u = 3/4 + 2^-24 is above 1/2 with
+    # p = 1/2 + 2^-23, p * 2^32 = 2^31 + 512; 2^31 + 400 rounds to it, 2^31 + 300 to 2^31 + 256
+    x = float(np.float32(0.75 + 2.0 ** -24))
+    assert orc.quant_one(1, 2, x, 1.0, key, _counter_for_hash(orc, key, (1 << 31) + 400)) == 1
+    assert orc.quant_one(1, 2, x, 1.0, key, _counter_for_hash(orc, key, (1 << 31) + 300)) == 2
 
 
 def test_zero_draw_at_counter_equal_key(orc):
