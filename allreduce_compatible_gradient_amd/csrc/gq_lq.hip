@@ -12,10 +12,12 @@
 //   pass 1  E <- G + E and P = E Q              (read G, E; write E)   k_lq_ef_mq
 //   pass 2  Q' = E^T Pt                         (read E)               k_lq_mtp + k_lq_qsum
 //   pass 3  E <- E - Phat Q'hat^T               (read E; write E)      k_lq_ef_update_q (one
-//                                                                      worker: quantises P and
-//                                                                      Q' itself), or
-//                                                                      k_lq_quant_elems + the
-//                                                                      K workers' k_lq_mean_ef
+//                                                                      worker, r <= 4: quantises
+//                                                                      P and Q' itself), or
+//                                                                      k_lq_quant_elems, then
+//                                                                      k_lq_ef_update (one
+//                                                                      worker) or the K
+//                                                                      workers' k_lq_mean_ef
 // With K workers (each its own G, E and warm start Q; the review's "Core claim" compresses each
 // worker's factors before the exchange) every per-worker kernel runs all K in one launch, the
 // worker taken from a grid dimension, and the last pass becomes k_lq_mean_ef: the mean of the
@@ -59,6 +61,11 @@ constexpr int kRowsA = 4;      // rows per block in the row passes
 constexpr int kBlockA = 256;
 constexpr int kWavesC = 8;     // waves per column-pass block
 constexpr int kRowsQ = 64;     // rows per block of the one-worker last pass (k_lq_ef_update_q)
+// Highest rank whose one-worker last pass quantises the factors itself (k_lq_ef_update_q):
+// each of its blocks quantises its columns' r values of Q' again, which at r = 7 cost more than
+// the separate quantiser it saves (measured at 4096 x 4096: 29.7 us against 23.2 + 4.7 us;
+// at r = 1, 24.0 against 22.5 + 4.7).
+constexpr int kFoldRankMax = 4;
 // Rows per column-pass chunk: 128, or 64 when 128-row chunks would give fewer than
 // kColBlocksMin blocks (the pass is then latency-bound and wants more of them).
 constexpr int kColBlocksMin = 1024;
@@ -887,6 +894,45 @@ __global__ __launch_bounds__(256) void k_lq_ef_update_q(const ElemJob J, const L
   }
 }
 
+// Pass 3 of one worker at ranks above kFoldRankMax, the factors already quantised by
+// k_lq_quant_elems: E <- E - Phat Qhat^T (Qhat row-major m x RANK), 4 rows per block, each
+// entry's products summed by fused multiply-adds over the columns in order (the same
+// arithmetic as k_lq_ef_update_q).
+template <int RANK, int VEC>
+__global__ __launch_bounds__(kBlockA) void k_lq_ef_update(float *__restrict__ E,
+                                                          const float *__restrict__ Ph,
+                                                          const float *__restrict__ Qh,
+                                                          int64_t n, int64_t m) {
+  const int64_t row0 = (int64_t)blockIdx.x * kRowsA;
+  float p[kRowsA][RANK];
+#pragma unroll
+  for (int rr = 0; rr < kRowsA; ++rr)
+#pragma unroll
+    for (int c = 0; c < RANK; ++c) p[rr][c] = row0 + rr < n ? Ph[(row0 + rr) * RANK + c] : 0.0f;
+  const int nr = n - row0 < kRowsA ? (int)(n - row0) : kRowsA;
+  for (int64_t j = (int64_t)threadIdx.x * VEC; j < m; j += (int64_t)kBlockA * VEC) {
+    float q[RANK][VEC];
+    float mv[kRowsA][VEC];
+#pragma unroll
+    for (int rr = 0; rr < kRowsA; ++rr)
+      if (rr < nr) ldv<VEC>(E + (row0 + rr) * m + j, mv[rr]);
+    load_q_rows<RANK, VEC>(Qh, j, q);
+#pragma unroll
+    for (int rr = 0; rr < kRowsA; ++rr) {
+      if (rr < nr) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          float s = 0.0f;
+#pragma unroll
+          for (int c = 0; c < RANK; ++c) s = fmaf(p[rr][c], q[c][v], s);
+          mv[rr][v] -= s;
+        }
+        stv<VEC>(E + (row0 + rr) * m + j, mv[rr]);
+      }
+    }
+  }
+}
+
 // Last pass of a step of K workers: the approximate global gradient
 // Ghat = (1/K) sum_w Phat_w Qhat_w^T for 4 rows at a time (sums over workers, then columns of
 // the factors, by fused multiply-add), stored once, and E_w <- M_w - Ghat for every worker
@@ -1071,6 +1117,13 @@ void launch_step(const StepIO &io, const StepBufs &b, const LqTables &tp, const 
                        tp.alpha);
     hipLaunchKernelGGL((k_lq_mean_ef<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA), 0,
                        s, io.W, io.K, b.Ph, io.G_hat, 1.0f / (float)io.K, n, m);
+  } else if (RANK > kFoldRankMax) {
+    // one worker at a higher rank: the quantiser, then the plain last pass
+    hipLaunchKernelGGL(k_lq_quant_elems, dim3((unsigned)(((n + m) * RANK + 255) / 256), K),
+                       dim3(256), 0, s, je, io.W, tp.dev, tp.L, tp.tl, tq.dev, tq.L, tq.tl,
+                       tp.alpha);
+    hipLaunchKernelGGL((k_lq_ef_update<RANK, VEC>), dim3((unsigned)b.nblocks), dim3(kBlockA),
+                       0, s, io.W.E[0], b.Ph, io.W.Q[0], n, m);
   } else {
     // one worker: the quantiser runs inside the last pass
     const dim3 g3((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)((n + kRowsQ - 1) / kRowsQ));
