@@ -6,7 +6,8 @@
 // that are not the kernels' own (gqc_stream_pattern): one float4 group per thread with a grid
 // that covers the buffers once, and one block per tile in the XCD order the kernels use.  The
 // best of them is the empirical ceiling the quantisation kernels are compared with, beside
-// the 8 TB/s HBM peak.
+// the 8 TB/s HBM peak; and the byte mix of a one-worker 4-bit quantiser (gqc_pack4), the
+// ceiling of that row at its own size.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -97,6 +98,19 @@ __global__ __launch_bounds__(256) void k_tiles(Srcs s, int64_t ntiles, float *ou
   if (!WRITE && keep.x == 1.25e-37f && keep.y == -3.0e33f) sink[0] = keep.z;
 }
 
+// The byte mix of a one-worker 4-bit quantiser: thread i reads fp32 elements [8i, 8i + 8) (two
+// non-temporal float4 loads) and writes one 32-bit word at word i (non-temporal), so the grid,
+// covering the buffer once in address order, reads 4n bytes and writes n/2.
+__global__ __launch_bounds__(256) void k_pack4(const float *x, int64_t n8, uint32_t *out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n8) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x) + 2 * i);
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x) + 2 * i + 1);
+    const f32x4 c = a + b;
+    __builtin_nontemporal_store(__float_as_uint(c.x + c.y + c.z + c.w), out + i);
+  }
+}
+
 template <int K, bool WRITE>
 hipError_t launch_pattern(Srcs s, int pattern, int param, int64_t n, float *out, float *sink,
                           hipStream_t st) {
@@ -178,6 +192,20 @@ GQC_EXPORT int gqc_stream_pattern(const float *const *srcs, int K, int64_t n, fl
   }
 #undef GQC_K
   return e == hipSuccess ? 0 : (e == hipErrorInvalidValue ? 1 : 2);
+}
+
+// The 4-bit quantiser's byte mix (k_pack4) over the first (n / 8) * 8 elements of one fp32
+// buffer: reads 4 * (n / 8) * 8 bytes, writes (n / 8) * 4 bytes to `out` (16-byte aligned device
+// memory).  Returns 0 on success, 1 on a bad argument, 2 on a launch error.
+GQC_EXPORT int gqc_pack4(const float *src, int64_t n, uint32_t *out, void *stream) {
+  if (!src || !out || n < 0 || (reinterpret_cast<uintptr_t>(src) & 15) ||
+      (reinterpret_cast<uintptr_t>(out) & 15))
+    return 1;
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return 0;
+  hipLaunchKernelGGL(k_pack4, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), src, n8, out);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 // Streams the first (n / 2048) * 2048 elements of K fp32 buffers (K in {1, 2, 4, 8, 16}) with

@@ -19,9 +19,11 @@
 // XCD order of xcd_tile (each XCD streams its own contiguous eighth of the buffers), with
 // 2048-element tiles where several read streams mix with a write stream and 32 KB of input
 // (8192 fp32 or 16384 bf16 elements) for one read and one write stream; tiles never cross
-// segments, so the per-segment scale is one scalar load per tile.  The norm pass (read only) keeps a fixed grid striding over 65536-element
-// tiles, one fp64 partial each.  Codes are packed in registers.  No MFMA: there is no
-// contraction here.  Reductions are fixed-order (no float atomics): results are bit-stable.
+// segments, so the per-segment scale is one scalar load per tile.  The one-worker quantisers
+// run a full tile through a copy of their loop whose part and chunk counts are constants.
+// The norm pass (read only) keeps a fixed grid striding over 65536-element tiles, one fp64
+// partial each.  Codes are packed in registers.  No MFMA: there is no contraction here.
+// Reductions are fixed-order (no float atomics): results are bit-stable.
 //
 // Arithmetic contract (each step is one IEEE operation, so any conforming implementation of
 // the same definition gets the same bits; compiled with -ffp-contract=off and IEEE fp32
@@ -32,6 +34,8 @@
 // |sum| <= 64 * 127 < 2^24.
 #include <float.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "gq_internal.h"
 
@@ -597,50 +601,58 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
     tile_of(a.tv, t, quant_tile(DT), begin, len, seg);
     const SegQ q = seg_quant<GRID>(a.scale[seg], a.levels);
     const float fast_below = q.valid ? below_bound(q.inv, bound) : 0.0f;
-    const int nch = (len + kChunk - 1) / kChunk;
-    for (int ci = wv; ci < nch; ci += kBlock / 64) {
+    // a full tile takes a copy of the loop whose chunk and part counts are constants
+    auto run = [&](auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      const int nch = FULL ? quant_tile(DT) / kChunk : (len + kChunk - 1) / kChunk;
+      for (int ci = wv; ci < nch; ci += kBlock / 64) {
 #pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        const int o = part_offset<P>(ci, j, lane);
-        const int cnt = min(P, len - o);
-        if (cnt <= 0) continue;
-        const int64_t e0 = begin + o;
-        uint32_t c[P];
-        if (q.valid) {
-          float x[P];
-          load_part<DT, P>(a.grad, e0, cnt, x);
-          const uint32_t ctr = a.index_base + (uint32_t)e0;
-          float big = 0.0f;  // a part's missing elements are loaded as zeros
+        for (int j = 0; j < NP; ++j) {
+          const int o = part_offset<P>(ci, j, lane);
+          const int cnt = FULL ? P : min(P, len - o);
+          if (!FULL && cnt <= 0) continue;
+          const int64_t e0 = begin + o;
+          uint32_t c[P];
+          if (q.valid) {
+            float x[P];
+            load_part<DT, P>(a.grad, e0, cnt, x);
+            const uint32_t ctr = a.index_base + (uint32_t)e0;
+            float big = 0.0f;  // a part's missing elements are loaded as zeros
 #pragma unroll
-          for (int e = 0; e < P; ++e) big = max_abs(big, x[e]);
-          if (__all(big < fast_below)) {
+            for (int e = 0; e < P; ++e) big = max_abs(big, x[e]);
+            if (__all(big < fast_below)) {
+#pragma unroll
+              for (int e = 0; e < P; ++e) {
+                const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+                const uint32_t up = (float)h < fabsf(x[e]) * q.inv * up_scale ? 1u : 0u;
+                if constexpr (GRID == 0)
+                  c[e] = (sign_bit(x[e]) ? (0u - up) : up) & ((1u << a.bits) - 1u);
+                else
+                  c[e] = exp_code(up, x[e], a.bits);
+              }
+              store_codes<P>(a.codes, e0, cnt, a.bits, c);
+              continue;
+            }
 #pragma unroll
             for (int e = 0; e < P; ++e) {
               const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
-              const uint32_t up = (float)h < fabsf(x[e]) * q.inv * up_scale ? 1u : 0u;
               if constexpr (GRID == 0)
-                c[e] = (sign_bit(x[e]) ? (0u - up) : up) & ((1u << a.bits) - 1u);
+                c[e] = uniform_code(quant_uniform_mag(x[e], q.inv, sf, h), x[e], a.bits);
               else
-                c[e] = exp_code(up, x[e], a.bits);
+                c[e] = exp_code(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e], a.bits);
             }
-            store_codes<P>(a.codes, e0, cnt, a.bits, c);
-            continue;
-          }
+          } else {
 #pragma unroll
-          for (int e = 0; e < P; ++e) {
-            const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
-            if constexpr (GRID == 0)
-              c[e] = uniform_code(quant_uniform_mag(x[e], q.inv, sf, h), x[e], a.bits);
-            else
-              c[e] = exp_code(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e], a.bits);
+            for (int e = 0; e < P; ++e) c[e] = 0;
           }
-        } else {
-#pragma unroll
-          for (int e = 0; e < P; ++e) c[e] = 0;
+          store_codes<P>(a.codes, e0, cnt, a.bits, c);
         }
-        store_codes<P>(a.codes, e0, cnt, a.bits, c);
       }
-    }
+    };
+    if (len == quant_tile(DT))
+      run(std::true_type{});
+    else
+      run(std::false_type{});
   }
 }
 
@@ -826,50 +838,58 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
     const bool fold_ok =
         DT == 0 || (q.inv >= 0x1p-16f && inv_up < 0x1p127f && (GRID == 0 || a.levels <= 95));
     const float fast_below = q.valid && fold_ok ? below_bound(q.inv, bound) : 0.0f;
-    const int nch = (len + kChunk - 1) / kChunk;
-    for (int ci = wv; ci < nch; ci += kBlock / 64) {
+    // a full tile takes a copy of the loop whose chunk and part counts are constants
+    auto run = [&](auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      const int nch = FULL ? quant_tile(DT) / kChunk : (len + kChunk - 1) / kChunk;
+      for (int ci = wv; ci < nch; ci += kBlock / 64) {
 #pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        const int o = part_offset<P>(ci, j, lane);
-        const int cnt = min(P, len - o);
-        if (cnt <= 0) continue;
-        const int64_t e0 = begin + o;
-        uint32_t v[P];
-        if (q.valid) {
-          float x[P];
-          load_part<DT, P>(a.grad, e0, cnt, x);
-          const uint32_t ctr = a.index_base + (uint32_t)e0;
-          float big = 0.0f;  // a part's missing elements are loaded as zeros
+        for (int j = 0; j < NP; ++j) {
+          const int o = part_offset<P>(ci, j, lane);
+          const int cnt = FULL ? P : min(P, len - o);
+          if (!FULL && cnt <= 0) continue;
+          const int64_t e0 = begin + o;
+          uint32_t v[P];
+          if (q.valid) {
+            float x[P];
+            load_part<DT, P>(a.grad, e0, cnt, x);
+            const uint32_t ctr = a.index_base + (uint32_t)e0;
+            float big = 0.0f;  // a part's missing elements are loaded as zeros
 #pragma unroll
-          for (int e = 0; e < P; ++e) big = max_abs(big, x[e]);
-          if (__all(big < fast_below)) {
+            for (int e = 0; e < P; ++e) big = max_abs(big, x[e]);
+            if (__all(big < fast_below)) {
+#pragma unroll
+              for (int e = 0; e < P; ++e) {
+                const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+                const float up = DT == 1 ? fabsf(x[e]) * inv_up : fabsf(x[e]) * q.inv * up_scale;
+                const int32_t lin = (float)h < up ? (x[e] < 0.0f ? -1 : 1) : 0;
+                v[e] = (uint32_t)(lin + a.offset);
+              }
+              store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
+              continue;
+            }
 #pragma unroll
             for (int e = 0; e < P; ++e) {
               const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
-              const float up = DT == 1 ? fabsf(x[e]) * inv_up : fabsf(x[e]) * q.inv * up_scale;
-              const int32_t lin = (float)h < up ? (x[e] < 0.0f ? -1 : 1) : 0;
+              int32_t lin;
+              if constexpr (GRID == 0)
+                lin = (int32_t)copysignf(quant_uniform_mag(x[e], q.inv, sf, h), x[e]);
+              else
+                lin = exp_lin_of(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e]);
               v[e] = (uint32_t)(lin + a.offset);
             }
-            store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
-            continue;
-          }
+          } else {
 #pragma unroll
-          for (int e = 0; e < P; ++e) {
-            const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
-            int32_t lin;
-            if constexpr (GRID == 0)
-              lin = (int32_t)copysignf(quant_uniform_mag(x[e], q.inv, sf, h), x[e]);
-            else
-              lin = exp_lin_of(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e]);
-            v[e] = (uint32_t)(lin + a.offset);
+            for (int e = 0; e < P; ++e) v[e] = (uint32_t)a.offset;
           }
-        } else {
-#pragma unroll
-          for (int e = 0; e < P; ++e) v[e] = (uint32_t)a.offset;
+          store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
         }
-        store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
       }
-    }
+    };
+    if (len == quant_tile(DT))
+      run(std::true_type{});
+    else
+      run(std::false_type{});
   }
 }
 

@@ -127,10 +127,11 @@ def rows_breakdown(torch, gq, W, grads, S, w, args, groups=ROW_GROUPS):
     n, K = w.n, w.K
     it = 3
 
-    def row(name, ms, nbytes, note):
+    def row(name, ms, nbytes, note, **extra):
         gbs = nbytes / (ms * 1e-3) / 1e9
         rows[name] = {"ms": round(ms, 4), "algo_bytes": int(nbytes), "GBps": round(gbs, 1),
                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "what": note}
+        rows[name].update(extra)
         log("row %-28s %9.3f ms %8.1f GB/s (%.1f%% of HBM)" % (name, ms, gbs,
                                                                 100 * gbs / HBM_PEAK_GBS))
 
@@ -236,8 +237,26 @@ def rows_resnet50(torch, gq, W, row):
     row("norm_resnet50_161seg_K8", ms, w2.K * w2.n * 4, "K fp32 buffers in")
     ms = time_calls(torch, lambda: gq.quantize_pack(g2[0], S2, w2.grid, w2.levels, w2.bits, 1, 0,
                                                     offsets=w2.offsets, codes=c2), 11)
+    # the same byte mix as a plain stream of this size (fp32 in, 4 bits per element out): the
+    # ceiling of a 115 MB one-worker pass, whose start and drain are a large part of its time
+    import ctypes as C
+    from allreduce_compatible_gradient_amd import build as B
+    clib = C.CDLL(B.CEILING_LIB)
+    clib.gqc_pack4.restype = C.c_int
+    clib.gqc_pack4.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def pack4():
+        assert clib.gqc_pack4(g2[0].data_ptr(), w2.n, c2.data_ptr(), stream) == 0
+    ms_c = time_calls(torch, pack4, 11)
+    n8 = w2.n // 8 * 8
+    gbs_c = (n8 * 4 + n8 // 2) / (ms_c * 1e-3) / 1e9
+    row("ceiling_pack4_stream_resnet50_size", ms_c, n8 * 4 + n8 // 2,
+        "plain stream with the 4-bit quantiser's byte mix at this size (fp32 in, 4 bits out)")
+    gbs_q = (w2.n * 4 + (w2.n + 1) // 2) / (ms * 1e-3) / 1e9
     row("quantize_pack_resnet50_exp7_int4", ms, w2.n * 4 + (w2.n + 1) // 2,
-        "one worker, exponential grid, 4-bit codes")
+        "one worker, exponential grid, 4-bit codes",
+        frac_of_size_ceiling=round(gbs_q / gbs_c, 4))
     ms = time_calls(torch, lambda: gq.fused_mean(g2, S2, w2.grid, w2.levels, w2.bits, 1, 16, 0,
                                                  offsets=w2.offsets, out=o2), 11)
     row("fused_resnet50_exp7_K8", ms, w2.K * w2.n * 4 + w2.n * 4, "fused pass, 161 segments")
