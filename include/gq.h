@@ -119,7 +119,7 @@ gq_status gq_global_norm_noalloc(gq_ctx *ctx, const void *const *grads, int32_t 
 
 /* Stochastic quantisation onto the shared grid, packed to `bits` (4 or 8) per element
  * (Global-QSGD abstract: unbiased compressor on a grid all workers share; LQ-SGD review, "Core
- * claim": only the b-bit indices are transmitted).  With u = |x| * inv_g:
+ * claim": each value travels as its bin number in b bits).  With u = |x| * inv_g:
  *   uniform:     inv_g = fp32(s / S_g); u <- min(u, s); l = floor(u); p = u - l;
  *                code = sign(x) * (l + [r < p])                     (two's complement)
  *   exponential: inv_g = fp32(1 / S_g); u <- min(u, 1); j = largest level index with

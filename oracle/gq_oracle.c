@@ -238,8 +238,8 @@ void orc_quantize_list(const float *x, const float *S, const uint32_t *counter, 
 
 /* ======================= codes ======================= */
 
-/* [LQ] "Core claim": only the b-bit indices are transmitted.  Uniform levels are stored in
- * two's complement; exponential levels as a sign bit above the index j. */
+/* [LQ] "Core claim": the message carries each value as its bin number in b bits.  Uniform
+ * levels are stored in two's complement; exponential levels as a sign bit above the index j. */
 static uint32_t encode_level(int32_t grid, int32_t bits, int32_t q)
 {
     uint32_t mask = (1u << bits) - 1u;
