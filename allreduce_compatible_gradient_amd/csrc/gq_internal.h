@@ -9,11 +9,11 @@ namespace gq {
 
 constexpr int kMaxWorkers = 64;
 constexpr int kGroup = 8;            // elements per thread step: one 32 B fp32 / 16 B bf16 load
-// Elements per tile (a tile never crosses a segment): 8192 for the one-worker quantisers (one
-// read and one write stream), 2048 for the kernels that mix several streams with a write
-// stream (fused pass, integer sum, decodes), whose grids of small tiles in the XCD order of
-// gq_stream.hip stream fastest (measured on the 1.3e9 x 8 fused pass: 9.2 ms with 8192-element
-// tiles on 4096 resident blocks, 8.0 ms like this).
+// Elements per tile (a tile never crosses a segment): 8192 fp32 for the one-worker quantisers
+// (one read and one write stream; see quant_tile), 2048 for the kernels that mix several
+// streams with a write stream (fused pass, integer sum, decodes), whose grids of small tiles
+// in the XCD order of gq_stream.hip stream fastest (measured on the 1.3e9 x 8 fused pass:
+// 9.2 ms with 8192-element tiles on 4096 resident blocks, 8.0 ms like this).
 constexpr int kTile = 8192;
 constexpr int kTileMix = 2048;
 // The one-worker quantisers' tile is 32 KB of input: kTile fp32 or 2 kTile bf16 elements
@@ -43,7 +43,7 @@ struct Tile {
 };
 
 // How tiles map onto segments.  With tiles == nullptr there is one segment [0, n) cut into
-// kTile-element tiles; otherwise tiles[t] describes tile t and seg_tile_start[g] is the first
+// tiles of the kernel's own size (kTileMix, quant_tile or the norm's tile); otherwise tiles[t] describes tile t and seg_tile_start[g] is the first
 // tile of segment g (nseg + 1 entries).
 struct TileView {
   const Tile *tiles;
