@@ -4,14 +4,16 @@ The stochastic rounding draws r = fp32(fmix32(counter XOR key_k)) * 2^-32 -- the
 rounded to the nearest fp32 (ties to even), scaled exactly -- with key_k the low 32 bits of
 SplitMix64 output k+1 from the step seed.  Both generators are pinned to published
 known-answer values (tests/golden/rng_kat.json); the rounding of the hash is pinned on chosen
-hash values (reached through the inverse of the finaliser, written here); the draw is then
-checked statistically.
+hash values (reached through the inverse of the finaliser, tests/draw_helpers.py); the draw is
+then checked statistically.
 """
 import json
 import os
 
 import numpy as np
 import pytest
+
+from tests.draw_helpers import counter_for_hash
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "rng_kat.json")
 M32 = 0xFFFFFFFF
@@ -61,19 +63,8 @@ def test_fmix32_via_murmur3_known_answers(orc, case):
     assert got == int(case["hash"], 16)
 
 
-def _inv_fmix32(h: int) -> int:
-    """The input whose fmix32 is h: each step of the finaliser undone in reverse order."""
-    h ^= h >> 16                              # x ^ (x >> 16) is its own inverse
-    h = (h * pow(0xC2B2AE35, -1, 1 << 32)) & M32
-    x = h                                     # undo x ^ (x >> 13): fixed point, 3 rounds
-    for _ in range(3):
-        x = h ^ (x >> 13)
-    h = (x * pow(0x85EBCA6B, -1, 1 << 32)) & M32
-    return h ^ (h >> 16)
-
-
 def _counter_for_hash(orc, key: int, h: int) -> int:
-    c = _inv_fmix32(h) ^ key
+    c = counter_for_hash(key, h)
     assert orc.fmix32(c ^ key) == h
     return c
 
