@@ -25,6 +25,13 @@ constexpr int kNormTileMin = 4096;   // ... halved down to this while K x tiles 
 constexpr int kBlock = 256;          // threads per block of the streaming kernels
 constexpr int kGridAll = 1 << 30;    // grid cap of the element-wise kernels: one block per tile
 constexpr int kNormGrid = 2048;      // blocks per worker of the norm pass
+// Up to this many partials (K x tiles) one kernel finishes the norm (a block per segment sums
+// every worker's partials and takes the maximum); above it the per-worker sums get a block
+// each and the maximum a kernel of its own.
+constexpr int64_t kNormFinishMax = 65536;
+// Fused passes of at most this many tiles (other than the double-buffered bf16 one) compute
+// their segment constants per tile.
+constexpr int64_t kSegConstTilesMin = 4096;
 
 // Tile of the norm pass for K workers of n elements: 65536, halved while the K x tiles blocks
 // would not fill the GPU (kNormGrid), down to 4096.  The tile fixes the fp64 summation order,
@@ -43,8 +50,8 @@ struct Tile {
 };
 
 // How tiles map onto segments.  With tiles == nullptr there is one segment [0, n) cut into
-// tiles of the kernel's own size (kTileMix, quant_tile or the norm's tile); otherwise tiles[t] describes tile t and seg_tile_start[g] is the first
-// tile of segment g (nseg + 1 entries).
+// tiles of the kernel's own size (kTileMix, quant_tile or the norm's tile); otherwise tiles[t]
+// describes tile t and seg_tile_start[g] is the first tile of segment g (nseg + 1 entries).
 struct TileView {
   const Tile *tiles;
   const int64_t *seg_tile_start;
@@ -118,9 +125,10 @@ struct WireDequantArgs {
 
 // Per-segment constants of the fused pass, computed once per segment before the pass (tiles
 // are small, so computing them per tile cost the vector ALUs about one instruction per
-// worker-element): inv = s/S or 1/S (0 when the scale is not usable), the decode factor f,
-// the fast path's threshold fast_below (0: no fast path) and inv_up = inv * 2^32 (uniform) or
-// inv * 2^(E+31) (exponential).
+// worker-element) -- except in a pass of at most kSegConstTilesMin tiles (not the
+// double-buffered bf16 one), whose time the extra launch would stretch by more than that: inv = s/S or 1/S (0 when the scale is not
+// usable), the decode factor f, the fast path's threshold fast_below (0: no fast path) and
+// inv_up = inv * 2^32 (uniform) or inv * 2^(E+31) (exponential).
 struct SegConst {
   float inv;
   float f;

@@ -579,6 +579,57 @@ __global__ void k_norm_scale(NormArgs a) {
   a.scale_out[g] = S;
 }
 
+// The two kernels above in one, for inputs with few norm tiles (K x tiles <= kNormFinishMax):
+// one block per segment; wave w sums the partials of workers w, w + 4, ... (lane l adds
+// partials l, l + 64, ... in order, then the wave's fixed-order butterfly), and one thread takes
+// the maximum over the workers in worker order as k_norm_scale does.  The summation order
+// differs from k_norm_segments' (the path is chosen by size alone, so a given input always
+// takes the same one).
+__global__ __launch_bounds__(kBlock) void k_norm_finish(NormArgs a) {
+  __shared__ double nrm_s[kMaxWorkers];
+  const int g = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t t0 = seg_first_tile(a.tv, g), t1 = seg_first_tile(a.tv, g + 1);
+  for (int k = w; k < a.K; k += kBlock / 64) {
+    const double *part = a.partial + (int64_t)k * a.tv.ntiles;
+    constexpr int UB = 8;  // loads in flight per lane
+    double acc = 0.0;
+    for (int64_t t = t0 + lane; t < t1; t += UB * 64) {
+      double v[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int64_t tt = t + (int64_t)u * 64;
+        v[u] = tt < t1 ? part[tt] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u)
+        if (t + (int64_t)u * 64 < t1) acc += v[u];
+    }
+    const double nrm = sqrt(wave_sum(acc));
+    if (lane == 0) {
+      nrm_s[k] = nrm;
+      if (a.norms_out) a.norms_out[(int64_t)k * a.tv.nseg + g] = nrm;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double best = 0.0;
+    bool bad = false;
+    for (int k = 0; k < a.K; ++k) {
+      const double nrm = nrm_s[k];
+      if (!isfinite(nrm))
+        bad = true;
+      else if (nrm > best)
+        best = nrm;
+    }
+    float S = (float)best;
+    if (bad || !isfinite(S)) {
+      S = 0.0f;
+      atomicOr(a.status, 1u);
+    }
+    a.scale_out[g] = S;
+  }
+}
+
 // ================================================================ quantise + pack (one worker)
 // With the fused pass's fast path: a part whose elements, in every active lane, lie below the
 // lowest nonzero level (the lane's largest magnitude, NaN-propagating, against the tile's
@@ -941,6 +992,29 @@ __global__ __launch_bounds__(kBlock) void k_dequantize_wire(WireDequantArgs a) {
 // 0.184 ms) and in the double-buffered bf16 pass below; in the single-buffered bf16 pass the
 // uniform grid's shortcut saved instructions but no time (the waits for each batch's loads were
 // then exposed), so it is not used there.
+// The per-segment constants of k_fused.  In the double-buffered pass (pipe) the fast path
+// scales |x| by inv_up = inv * 2^32 (or inv * 2^(E+31)) in one product.  Below the threshold
+// fl(|x| * inv) < 1, and scaling it by that power of two is exact, so the one product equals
+// it whenever fl(|x| * inv) is a normal number; when it is subnormal both thresholds lie in
+// (0, 1] (products below 2^-126 * 2^(E+31) <= 1, hence E <= 95), where fp32(h) < threshold
+// holds for h = 0 alone, so the two round up alike; they differ only if
+// fl(|x| * inv) underflows to zero for a nonzero x, which inv >= 2^-16 rules out for bf16
+// (whose smallest magnitude is 2^-133).  A segment whose scale fails these conditions takes
+// the general path throughout (fast_below = 0).  The fast path runs on the exponential grid,
+// and on the uniform grid in the double-buffered pass.
+template <int GRID>
+__device__ __forceinline__ SegConst seg_const(float S, int levels, double denom, int pipe) {
+  const SegQ q = seg_quant<GRID>(S, levels);
+  const float lo_scale = ldexpf(1.0f, levels + 31);
+  const float inv_up = q.inv * (GRID == 0 ? 4294967296.0f : lo_scale);
+  const bool fold_ok = q.inv >= 0x1p-16f && inv_up < 0x1p127f && (GRID == 0 || levels <= 95);
+  const float fast_below =
+      q.valid && (GRID == 1 || pipe) && (!pipe || fold_ok)
+          ? below_bound(q.inv, GRID == 1 ? ldexpf(1.0f, 1 - levels) : 1.0f)
+          : 0.0f;
+  return SegConst{q.valid ? q.inv : 0.0f, seg_decode(S, denom), fast_below, inv_up};
+}
+
 template <int DT, int P, int NP, int KB>
 __device__ __forceinline__ void fused_load(const FusedArgs &a, int k0, int kn,
                                            const int64_t (&e0)[NP], const int (&cnt)[NP],
@@ -1058,7 +1132,13 @@ void k_fused(FusedArgs a) {
     int64_t begin;
     int len, seg;
     tile_of(a.tv, t, kTileMix, begin, len, seg);
-    const SegConst sc = a.segc[seg];
+    // from the table k_seg_consts filled, or (a small pass other than the double-buffered one,
+    // which the table's launch would cost more than this) computed here
+    SegConst sc;
+    if constexpr (PIPE)
+      sc = a.segc[seg];
+    else
+      sc = a.segc ? a.segc[seg] : seg_const<GRID>(a.scale[seg], a.levels, a.denom, 0);
     const SegQ q{sc.inv, sc.inv > 0.0f};
     const float f = sc.f;
     const float inv_up = sc.inv_up;
@@ -1417,7 +1497,9 @@ hipError_t launch_global_norm(const NormArgs &a, int dtype, hipStream_t s) {
     else
       hipLaunchKernelGGL(k_norm_partial<1>, grid, dim3(kBlock), 0, s, a);
   }
-  if (a.tv.nseg > 0) {
+  if (a.tv.nseg > 0 && (int64_t)a.K * a.tv.ntiles <= kNormFinishMax) {
+    hipLaunchKernelGGL(k_norm_finish, dim3(a.tv.nseg), dim3(kBlock), 0, s, a);
+  } else if (a.tv.nseg > 0) {
     hipLaunchKernelGGL(k_norm_segments, dim3(a.tv.nseg, a.K), dim3(kBlock), 0, s, a);
     hipLaunchKernelGGL(k_norm_scale, dim3((a.tv.nseg + 255) / 256), dim3(256), 0, s, a);
   }
@@ -1493,31 +1575,12 @@ hipError_t launch_dequantize_wire(const WireDequantArgs &a, int wb, hipStream_t 
   return hipGetLastError();
 }
 
-// The per-segment constants of k_fused.  In the double-buffered pass (pipe) the fast path
-// scales |x| by inv_up = inv * 2^32 (or inv * 2^(E+31)) in one product.  Below the threshold
-// fl(|x| * inv) < 1, and scaling it by that power of two is exact, so the one product equals
-// it whenever fl(|x| * inv) is a normal number; when it is subnormal both thresholds lie in
-// (0, 1] (products below 2^-126 * 2^(E+31) <= 1, hence E <= 95), where fp32(h) < threshold
-// holds for h = 0 alone, so the two round up alike; they differ only if
-// fl(|x| * inv) underflows to zero for a nonzero x, which inv >= 2^-16 rules out for bf16
-// (whose smallest magnitude is 2^-133).  A segment whose scale fails these conditions takes
-// the general path throughout (fast_below = 0).  The fast path runs on the exponential grid,
-// and on the uniform grid in the double-buffered pass.
 template <int GRID>
 __global__ void k_seg_consts(const float *scale, int nseg, int levels, double denom, int pipe,
                              SegConst *out) {
   const int g = blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= nseg) return;
-  const float S = scale[g];
-  const SegQ q = seg_quant<GRID>(S, levels);
-  const float lo_scale = ldexpf(1.0f, levels + 31);
-  const float inv_up = q.inv * (GRID == 0 ? 4294967296.0f : lo_scale);
-  const bool fold_ok = q.inv >= 0x1p-16f && inv_up < 0x1p127f && (GRID == 0 || levels <= 95);
-  const float fast_below =
-      q.valid && (GRID == 1 || pipe) && (!pipe || fold_ok)
-          ? below_bound(q.inv, GRID == 1 ? ldexpf(1.0f, 1 - levels) : 1.0f)
-          : 0.0f;
-  out[g] = SegConst{q.valid ? q.inv : 0.0f, seg_decode(S, denom), fast_below, inv_up};
+  out[g] = seg_const<GRID>(scale[g], levels, denom, pipe);
 }
 
 template <int DT, int GRID, bool STORE>
@@ -1544,6 +1607,16 @@ hipError_t launch_fused(const FusedArgs &a, int dtype, int grid, hipStream_t s) 
   if (a.tv.ntiles == 0) return hipSuccess;
   // the double-buffered pass: bf16, 16 workers, no code stores
   const int pipe = dtype == 1 && a.K == 16 && !a.store_codes;
+  if (!pipe && a.tv.ntiles <= kSegConstTilesMin) {
+    FusedArgs b = a;
+    b.segc = nullptr;  // constants computed per tile
+    dim3 g(grid_for(a.tv.ntiles, kGridAll));
+    if (a.store_codes)
+      launch_fused_s<true>(b, dtype, grid, g, s);
+    else
+      launch_fused_s<false>(b, dtype, grid, g, s);
+    return hipGetLastError();
+  }
   const dim3 gs((unsigned)((a.tv.nseg + 255) / 256));
   if (grid == 0)
     hipLaunchKernelGGL(k_seg_consts<0>, gs, dim3(256), 0, s, a.scale, a.tv.nseg, a.levels,
