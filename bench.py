@@ -31,6 +31,7 @@ WORKLOAD = "flat-1.3G-f32-K8-uniform127"
 METRIC = "gradient GB/s quantized+aggregated over K workers; % of HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_mean_flat-1.3G-f32-K8.traffic.json")
 STREAM_SRC = os.path.join(ROOT, "allreduce_compatible_gradient_amd", "csrc", "gq_stream.hip")
+INTERNAL_H = os.path.join(ROOT, "allreduce_compatible_gradient_amd", "csrc", "gq_internal.h")
 
 
 def log(*a):
@@ -38,10 +39,11 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """sha256 (16 hex digits) of the streaming kernels' source with comments and whitespace
-    removed: it changes when the code changes, not when a comment does."""
+    """sha256 (16 hex digits) of the streaming kernels' source and the header of their shared
+    constants (tile sizes, grids), comments and whitespace removed: it changes when the code
+    changes, not when a comment does."""
     import re
-    src = open(STREAM_SRC).read()
+    src = open(STREAM_SRC).read() + open(INTERNAL_H).read()
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = " ".join(src.split())
