@@ -60,7 +60,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRowsA = 4;      // rows per block in the row passes
 constexpr int kBlockA = 256;
 constexpr int kWavesC = 8;     // waves per column-pass block
-constexpr int kRowsQ = 64;     // rows per block of the one-worker last pass (k_lq_ef_update_q)
+// Rows per block of the one-worker last pass (k_lq_ef_update_q): 64, or 32 at rank 1, where
+// requantising a block's Q' values costs least and more, shorter blocks fill the GPU better
+// (4096 x 4096 step: 0.087 -> 0.083 ms; 16 rows, or 32 at rank 4, ran slower).
+template <int RANK>
+constexpr int rows_q() { return RANK == 1 ? 32 : 64; }
 // Highest rank whose one-worker last pass quantises the factors itself (k_lq_ef_update_q):
 // each of its blocks quantises its columns' r values of Q' again, which at r = 7 cost more than
 // the separate quantiser it saves (measured at 4096 x 4096: 29.7 us against 23.2 + 4.7 us;
@@ -1126,8 +1130,9 @@ void launch_step(const StepIO &io, const StepBufs &b, const LqTables &tp, const 
                        0, s, io.W.E[0], b.Ph, io.W.Q[0], n, m);
   } else {
     // one worker: the quantiser runs inside the last pass
-    const dim3 g3((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)((n + kRowsQ - 1) / kRowsQ));
-    hipLaunchKernelGGL((k_lq_ef_update_q<RANK, VEC, kRowsQ>), g3, dim3(256), 0, s, je, io.W,
+    constexpr int RQ = rows_q<RANK>();
+    const dim3 g3((unsigned)((m + 64 * VEC - 1) / (64 * VEC)), (unsigned)((n + RQ - 1) / RQ));
+    hipLaunchKernelGGL((k_lq_ef_update_q<RANK, VEC, RQ>), g3, dim3(256), 0, s, je, io.W,
                        tp.dev, tp.L, tp.tl, tq.dev, tq.L, tq.tl, tp.alpha);
   }
 }
