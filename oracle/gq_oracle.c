@@ -52,9 +52,10 @@ uint32_t orc_worker_key(uint64_t seed, uint32_t worker)
     return (uint32_t)z;
 }
 
-/* The 32-bit hash rounded to the nearest fp32 (ties to even: C's conversion under the default
- * rounding mode), then scaled by 2^-32 (exact).  Values within 128 of 2^32 round to 1.0, which
- * no p < 1 exceeds. */
+/* The draw as an fp32 program makes it: the 32-bit hash rounded to the nearest fp32 (ties to
+ * even: C's conversion under the default rounding mode), then scaled by 2^-32 (exact), so that
+ * it has the precision of the fp32 probability p it is compared with.  Values within 128 of
+ * 2^32 round to 1.0, which no p < 1 exceeds. */
 double orc_uniform(uint32_t key, uint32_t counter)
 {
     const float h = (float)orc_fmix32(counter ^ key);
