@@ -640,6 +640,12 @@ template <int DT, int GRID>
 __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
   constexpr int P = DT == 0 ? 4 : 8;
   constexpr int NP = kChunk / (64 * P);
+  constexpr int WAVES = kBlock / 64;
+  constexpr int CPW = quant_tile(DT) / kChunk / WAVES;  // chunks per wave in a full tile
+  // chunks whose loads a wave issues before it uses the first: all of its share of an fp32
+  // tile (8 loads of 1 KB in flight per wave); one at a time for bf16, which measured faster
+  constexpr int GR = DT == 0 ? CPW : 1;
+  static_assert(CPW % GR == 0, "group size");
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float sf = (float)a.levels;
   const float lo_scale = ldexpf(1.0f, a.levels + 31);
@@ -652,58 +658,86 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
     tile_of(a.tv, t, quant_tile(DT), begin, len, seg);
     const SegQ q = seg_quant<GRID>(a.scale[seg], a.levels);
     const float fast_below = q.valid ? below_bound(q.inv, bound) : 0.0f;
-    // a full tile takes a copy of the loop whose chunk and part counts are constants
-    auto run = [&](auto full) {
-      constexpr bool FULL = decltype(full)::value;
-      const int nch = FULL ? quant_tile(DT) / kChunk : (len + kChunk - 1) / kChunk;
-      for (int ci = wv; ci < nch; ci += kBlock / 64) {
+    // codes of one part of cnt elements at e0, from its loaded values (zeros where missing)
+    auto quant_part = [&](int64_t e0, int cnt, const float (&x)[P]) {
+      uint32_t c[P];
+      const uint32_t ctr = a.index_base + (uint32_t)e0;
+      float big = 0.0f;
+#pragma unroll
+      for (int e = 0; e < P; ++e) big = max_abs(big, x[e]);
+      if (__all(big < fast_below)) {
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+          const uint32_t up = (float)h < fabsf(x[e]) * q.inv * up_scale ? 1u : 0u;
+          if constexpr (GRID == 0)
+            c[e] = (sign_bit(x[e]) ? (0u - up) : up) & ((1u << a.bits) - 1u);
+          else
+            c[e] = exp_code(up, x[e], a.bits);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+          if constexpr (GRID == 0)
+            c[e] = uniform_code(quant_uniform_mag(x[e], q.inv, sf, h), x[e], a.bits);
+          else
+            c[e] = exp_code(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e], a.bits);
+        }
+      }
+      store_codes<P>(a.codes, e0, cnt, a.bits, c);
+    };
+    auto zero_part = [&](int64_t e0, int cnt) {
+      uint32_t c[P];
+#pragma unroll
+      for (int e = 0; e < P; ++e) c[e] = 0;
+      store_codes<P>(a.codes, e0, cnt, a.bits, c);
+    };
+    if (len == quant_tile(DT)) {
+      // a full tile: each wave issues the loads of GR chunks before it uses the first
+      for (int i0 = 0; i0 < CPW; i0 += GR) {
+        if (!q.valid) {
+#pragma unroll
+          for (int i = 0; i < GR; ++i)
+#pragma unroll
+            for (int j = 0; j < NP; ++j)
+              zero_part(begin + part_offset<P>(wv + (i0 + i) * WAVES, j, lane), P);
+          continue;
+        }
+        PartBuf<DT, P> buf[GR][NP];
+#pragma unroll
+        for (int i = 0; i < GR; ++i)
+#pragma unroll
+          for (int j = 0; j < NP; ++j)
+            buf[i][j].load(a.grad, begin + part_offset<P>(wv + (i0 + i) * WAVES, j, lane), P);
+#pragma unroll
+        for (int i = 0; i < GR; ++i)
+#pragma unroll
+          for (int j = 0; j < NP; ++j) {
+            float x[P];
+#pragma unroll
+            for (int e = 0; e < P; ++e) x[e] = buf[i][j].get(e);
+            quant_part(begin + part_offset<P>(wv + (i0 + i) * WAVES, j, lane), P, x);
+          }
+      }
+    } else {
+      const int nch = (len + kChunk - 1) / kChunk;
+      for (int ci = wv; ci < nch; ci += WAVES) {
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
           const int o = part_offset<P>(ci, j, lane);
-          const int cnt = FULL ? P : min(P, len - o);
-          if (!FULL && cnt <= 0) continue;
-          const int64_t e0 = begin + o;
-          uint32_t c[P];
+          const int cnt = min(P, len - o);
+          if (cnt <= 0) continue;
           if (q.valid) {
             float x[P];
-            load_part<DT, P>(a.grad, e0, cnt, x);
-            const uint32_t ctr = a.index_base + (uint32_t)e0;
-            float big = 0.0f;  // a part's missing elements are loaded as zeros
-#pragma unroll
-            for (int e = 0; e < P; ++e) big = max_abs(big, x[e]);
-            if (__all(big < fast_below)) {
-#pragma unroll
-              for (int e = 0; e < P; ++e) {
-                const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
-                const uint32_t up = (float)h < fabsf(x[e]) * q.inv * up_scale ? 1u : 0u;
-                if constexpr (GRID == 0)
-                  c[e] = (sign_bit(x[e]) ? (0u - up) : up) & ((1u << a.bits) - 1u);
-                else
-                  c[e] = exp_code(up, x[e], a.bits);
-              }
-              store_codes<P>(a.codes, e0, cnt, a.bits, c);
-              continue;
-            }
-#pragma unroll
-            for (int e = 0; e < P; ++e) {
-              const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
-              if constexpr (GRID == 0)
-                c[e] = uniform_code(quant_uniform_mag(x[e], q.inv, sf, h), x[e], a.bits);
-              else
-                c[e] = exp_code(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e], a.bits);
-            }
+            load_part<DT, P>(a.grad, begin + o, cnt, x);
+            quant_part(begin + o, cnt, x);
           } else {
-#pragma unroll
-            for (int e = 0; e < P; ++e) c[e] = 0;
+            zero_part(begin + o, cnt);
           }
-          store_codes<P>(a.codes, e0, cnt, a.bits, c);
         }
       }
-    };
-    if (len == quant_tile(DT))
-      run(std::true_type{});
-    else
-      run(std::false_type{});
+    }
   }
 }
 
