@@ -100,6 +100,40 @@ def test_zero_and_nonfinite_segments(orc):
     assert g.read_status() == g.ENONFINITE
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("grid,levels,bits", [(U, 7, 4), (X, 7, 4), (U, 127, 8)])
+def test_zero_and_nonfinite_segments_over_full_tiles(orc, dt, grid, levels, bits):
+    """Segments whose scale is unusable (all zero; an infinite element) spanning several full
+    quantisation tiles (8192 fp32 or 16384 bf16 elements): their codes are written as zero,
+    also over a code buffer that held other bytes, and the segments around them stay
+    bit-exact with the oracle."""
+    g = gq()
+    say("unusable segments over full tiles", dt, grid, levels, bits)
+    tile = 8192 if dt == "f32" else 16384
+    lens = [tile + 8, 3 * tile, 2 * tile + 16, tile + 5]
+    off = [0] + list(np.cumsum(lens))
+    n = off[-1]
+    rng = np.random.default_rng(61 + grid + levels + (dt == "bf16"))
+    xs = [rng.standard_normal(n).astype(np.float32) for _ in range(3)]
+    for x in xs:
+        x[off[1]:off[2]] = 0.0
+    xs[1][off[2] + tile + 3] = np.inf
+    if dt == "bf16":
+        xs = [(x.view(np.uint32) >> 16).astype(np.uint16) for x in xs]
+    g.read_status()
+    ref = _run_both(orc, xs, grid, levels, bits, 16, offsets=off)
+    assert ref["scale"][1] == 0 and ref["scale"][2] == 0 and ref["scale"][0] > 0
+    assert g.read_status() == g.ENONFINITE
+    S = dev(ref["scale"])
+    for k in range(len(xs)):
+        codes = torch.full((g.code_bytes(n, bits),), 0xA5, dtype=torch.uint8, device="cuda")
+        g.quantize_pack(dev(xs[k]), S, grid, levels, bits, 3, k, 0, off, codes=codes)
+        got = host(codes)
+        assert np.array_equal(got, ref["codes"][k]), first_diff(got, ref["codes"][k])
+        lo, hi = off[1] * bits // 8, off[3] * bits // 8
+        assert not np.any(got[lo:hi])
+
+
 def test_one_hot_at_scale_hits_top_level(orc):
     say("one-hot")
     n = 1000
