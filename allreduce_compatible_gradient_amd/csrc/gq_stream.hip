@@ -904,6 +904,11 @@ template <int DT, int GRID, int WB>
 __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
   constexpr int P = DT == 0 ? 4 : 8;
   constexpr int NP = kChunk / (64 * P);
+  constexpr int WAVES = kBlock / 64;
+  constexpr int CPW = quant_tile(DT) / kChunk / WAVES;  // chunks per wave in a full tile
+  // chunks whose loads a wave issues before it uses the first (as in k_quantize_pack)
+  constexpr int GR = DT == 0 ? CPW : 1;
+  static_assert(CPW % GR == 0, "group size");
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float sf = (float)a.levels;
   const float lo_scale = ldexpf(1.0f, a.levels + 31);
@@ -923,58 +928,86 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
     const bool fold_ok =
         DT == 0 || (q.inv >= 0x1p-16f && inv_up < 0x1p127f && (GRID == 0 || a.levels <= 95));
     const float fast_below = q.valid && fold_ok ? below_bound(q.inv, bound) : 0.0f;
-    // a full tile takes a copy of the loop whose chunk and part counts are constants
-    auto run = [&](auto full) {
-      constexpr bool FULL = decltype(full)::value;
-      const int nch = FULL ? quant_tile(DT) / kChunk : (len + kChunk - 1) / kChunk;
-      for (int ci = wv; ci < nch; ci += kBlock / 64) {
+    // lanes of one part of cnt elements at e0, from its loaded values (zeros where missing)
+    auto wire_part = [&](int64_t e0, int cnt, const float (&x)[P]) {
+      uint32_t v[P];
+      const uint32_t ctr = a.index_base + (uint32_t)e0;
+      float big = 0.0f;
+#pragma unroll
+      for (int e = 0; e < P; ++e) big = max_abs(big, x[e]);
+      if (__all(big < fast_below)) {
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+          const float up = DT == 1 ? fabsf(x[e]) * inv_up : fabsf(x[e]) * q.inv * up_scale;
+          const int32_t lin = (float)h < up ? (x[e] < 0.0f ? -1 : 1) : 0;
+          v[e] = (uint32_t)(lin + a.offset);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+          int32_t lin;
+          if constexpr (GRID == 0)
+            lin = (int32_t)copysignf(quant_uniform_mag(x[e], q.inv, sf, h), x[e]);
+          else
+            lin = exp_lin_of(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e]);
+          v[e] = (uint32_t)(lin + a.offset);
+        }
+      }
+      store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
+    };
+    auto offset_part = [&](int64_t e0, int cnt) {
+      uint32_t v[P];
+#pragma unroll
+      for (int e = 0; e < P; ++e) v[e] = (uint32_t)a.offset;
+      store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
+    };
+    if (len == quant_tile(DT)) {
+      // a full tile: each wave issues the loads of GR chunks before it uses the first
+      for (int i0 = 0; i0 < CPW; i0 += GR) {
+        if (!q.valid) {
+#pragma unroll
+          for (int i = 0; i < GR; ++i)
+#pragma unroll
+            for (int j = 0; j < NP; ++j)
+              offset_part(begin + part_offset<P>(wv + (i0 + i) * WAVES, j, lane), P);
+          continue;
+        }
+        PartBuf<DT, P> buf[GR][NP];
+#pragma unroll
+        for (int i = 0; i < GR; ++i)
+#pragma unroll
+          for (int j = 0; j < NP; ++j)
+            buf[i][j].load(a.grad, begin + part_offset<P>(wv + (i0 + i) * WAVES, j, lane), P);
+#pragma unroll
+        for (int i = 0; i < GR; ++i)
+#pragma unroll
+          for (int j = 0; j < NP; ++j) {
+            float x[P];
+#pragma unroll
+            for (int e = 0; e < P; ++e) x[e] = buf[i][j].get(e);
+            wire_part(begin + part_offset<P>(wv + (i0 + i) * WAVES, j, lane), P, x);
+          }
+      }
+    } else {
+      const int nch = (len + kChunk - 1) / kChunk;
+      for (int ci = wv; ci < nch; ci += WAVES) {
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
           const int o = part_offset<P>(ci, j, lane);
-          const int cnt = FULL ? P : min(P, len - o);
-          if (!FULL && cnt <= 0) continue;
-          const int64_t e0 = begin + o;
-          uint32_t v[P];
+          const int cnt = min(P, len - o);
+          if (cnt <= 0) continue;
           if (q.valid) {
             float x[P];
-            load_part<DT, P>(a.grad, e0, cnt, x);
-            const uint32_t ctr = a.index_base + (uint32_t)e0;
-            float big = 0.0f;  // a part's missing elements are loaded as zeros
-#pragma unroll
-            for (int e = 0; e < P; ++e) big = max_abs(big, x[e]);
-            if (__all(big < fast_below)) {
-#pragma unroll
-              for (int e = 0; e < P; ++e) {
-                const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
-                const float up = DT == 1 ? fabsf(x[e]) * inv_up : fabsf(x[e]) * q.inv * up_scale;
-                const int32_t lin = (float)h < up ? (x[e] < 0.0f ? -1 : 1) : 0;
-                v[e] = (uint32_t)(lin + a.offset);
-              }
-              store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
-              continue;
-            }
-#pragma unroll
-            for (int e = 0; e < P; ++e) {
-              const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
-              int32_t lin;
-              if constexpr (GRID == 0)
-                lin = (int32_t)copysignf(quant_uniform_mag(x[e], q.inv, sf, h), x[e]);
-              else
-                lin = exp_lin_of(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e]);
-              v[e] = (uint32_t)(lin + a.offset);
-            }
+            load_part<DT, P>(a.grad, begin + o, cnt, x);
+            wire_part(begin + o, cnt, x);
           } else {
-#pragma unroll
-            for (int e = 0; e < P; ++e) v[e] = (uint32_t)a.offset;
+            offset_part(begin + o, cnt);
           }
-          store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
         }
       }
-    };
-    if (len == quant_tile(DT))
-      run(std::true_type{});
-    else
-      run(std::false_type{});
+    }
   }
 }
 
