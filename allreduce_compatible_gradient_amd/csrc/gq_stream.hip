@@ -742,10 +742,12 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
 }
 
 // ================================================================ integer sum of codes
-// sums_i = sum_k lin(code_{k,i}).  P = 8 for int16 sums (16 B stores), 4 for int32.
-template <int GRID, int P>
+// sums_i = sum_k lin(code_{k,i}).  P = 8 for int16 sums (16 B stores), 4 for int32.  The code
+// loads of KB workers are issued together (the sum is exact in any order).
+template <int GRID, int P, int BITS>
 __global__ __launch_bounds__(kBlock) void k_accumulate(AccArgs a) {
   constexpr int NP = kChunk / (64 * P);
+  constexpr int KB = 4;  // workers whose code loads are issued together
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const TileView tv{nullptr, nullptr, (a.n + kTileMix - 1) / kTileMix, a.n, 1};
   for (int64_t b = blockIdx.x; b < tv.ntiles; b += gridDim.x) {
@@ -764,11 +766,17 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(AccArgs a) {
         int32_t acc[P];
 #pragma unroll
         for (int e = 0; e < P; ++e) acc[e] = 0;
-        for (int k = 0; k < a.K; ++k) {
-          uint32_t c[P];
-          load_codes<P>(a.codes[k], e0, cnt, a.bits, c);
+        for (int k0 = 0; k0 < a.K; k0 += KB) {
+          // a batch past the last worker loads the last worker's codes again and adds nothing
+          uint32_t c[KB][P];
 #pragma unroll
-          for (int e = 0; e < P; ++e) acc[e] += lin_of_code<GRID>(c[e], a.bits);
+          for (int u = 0; u < KB; ++u)
+            load_codes<P>(a.codes[min(k0 + u, a.K - 1)], e0, cnt, BITS, c[u]);
+#pragma unroll
+          for (int u = 0; u < KB; ++u)
+            if (k0 + u < a.K)
+#pragma unroll
+              for (int e = 0; e < P; ++e) acc[e] += lin_of_code<GRID>(c[u][e], BITS);
         }
         store_sums<P>(a.sums, a.acc_bits, e0, cnt, acc);
       }
@@ -777,9 +785,10 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(AccArgs a) {
 }
 
 // ================================================================ decode of the mean
-template <int P>
+template <int P, int ACC>
 __global__ __launch_bounds__(kBlock) void k_dequantize(DequantArgs a) {
   constexpr int NP = kChunk / (64 * P);
+  constexpr int CPW = kTileMix / kChunk / (kBlock / 64);  // chunks per wave in a full tile
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   for (int64_t b = blockIdx.x; b < a.tv.ntiles; b += gridDim.x) {
     const int64_t t = xcd_tile(b, a.tv.ntiles);
@@ -787,6 +796,27 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(DequantArgs a) {
     int len, seg;
     tile_of(a.tv, t, kTileMix, begin, len, seg);
     const float f = seg_decode(a.scale[seg], a.denom);
+    if (len == kTileMix) {
+      // a full tile: the wave's loads are all issued before the first conversion
+      int32_t sv[CPW][NP][P];
+#pragma unroll
+      for (int i = 0; i < CPW; ++i)
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+          load_sums<P>(a.sums, ACC, begin + part_offset<P>(wv + i * (kBlock / 64), j, lane), P,
+                       sv[i][j]);
+#pragma unroll
+      for (int i = 0; i < CPW; ++i)
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+          float v[P];
+#pragma unroll
+          for (int e = 0; e < P; ++e) v[e] = (float)sv[i][j][e] * f;
+          store_mean<P>(a.out, a.out_dtype, begin + part_offset<P>(wv + i * (kBlock / 64), j, lane),
+                        P, v);
+        }
+      continue;
+    }
     const int nch = (len + kChunk - 1) / kChunk;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
 #pragma unroll
@@ -795,11 +825,11 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(DequantArgs a) {
         const int cnt = min(P, len - o);
         if (cnt <= 0) continue;
         const int64_t e0 = begin + o;
-        int32_t s[P];
-        load_sums<P>(a.sums, a.acc_bits, e0, cnt, s);
+        int32_t sv[P];
+        load_sums<P>(a.sums, ACC, e0, cnt, sv);
         float v[P];
 #pragma unroll
-        for (int e = 0; e < P; ++e) v[e] = (float)s[e] * f;
+        for (int e = 0; e < P; ++e) v[e] = (float)sv[e] * f;
         store_mean<P>(a.out, a.out_dtype, e0, cnt, v);
       }
     }
@@ -1023,6 +1053,28 @@ __global__ __launch_bounds__(kBlock) void k_dequantize_wire(WireDequantArgs a) {
     int len, seg;
     tile_of(a.tv, t, kTileMix, begin, len, seg);
     const float f = seg_decode(a.scale[seg], a.denom);
+    if (len == kTileMix) {
+      constexpr int CPW = kTileMix / kChunk / (kBlock / 64);
+      uint32_t lv[CPW][NP][P];
+#pragma unroll
+      for (int i = 0; i < CPW; ++i)
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+          load_lanes<P, WB>(a.payload, begin + part_offset<P>(wv + i * (kBlock / 64), j, lane), P,
+                            lv[i][j]);
+#pragma unroll
+      for (int i = 0; i < CPW; ++i)
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+          float m[P];
+#pragma unroll
+          for (int e = 0; e < P; ++e)
+            m[e] = (float)(int32_t)((int64_t)lv[i][j][e] - a.world_offset) * f;
+          store_mean<P>(a.out, a.out_dtype, begin + part_offset<P>(wv + i * (kBlock / 64), j, lane),
+                        P, m);
+        }
+      continue;
+    }
     const int nch = (len + kChunk - 1) / kChunk;
     for (int ci = wv; ci < nch; ci += kBlock / 64) {
 #pragma unroll
@@ -1508,10 +1560,11 @@ void k_worker_mean(WorkerMeanArgs a) {
 // The receiver's side after an allgather of per-worker-scaled codes: each worker's packed
 // codes decoded with its own factor (lane k of `fl`), accumulated by fused multiply-add in
 // worker order.  P = 8 elements per part: 8 (8-bit) or 4 (4-bit) code bytes per worker.
-template <int GRID>
+template <int GRID, int BITS>
 __global__ __launch_bounds__(kBlock) void k_decode_workers(DecodeWorkersArgs a) {
   constexpr int P = 8;
   constexpr int NP = kChunk / (64 * P);
+  constexpr int KB = 4;  // workers whose code loads are issued together
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   for (int64_t b = blockIdx.x; b < a.tv.ntiles; b += gridDim.x) {
     const int64_t t = xcd_tile(b, a.tv.ntiles);
@@ -1530,13 +1583,22 @@ __global__ __launch_bounds__(kBlock) void k_decode_workers(DecodeWorkersArgs a) 
         float acc[P];
 #pragma unroll
         for (int e = 0; e < P; ++e) acc[e] = 0.0f;
-        for (int k = 0; k < a.K; ++k) {
-          const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), k));
-          uint32_t c[P];
-          load_codes<P>(a.codes[k], e0, cnt, a.bits, c);
+        for (int k0 = 0; k0 < a.K; k0 += KB) {
+          // the code loads of KB workers go out together (a batch past the last worker loads
+          // the last worker's codes again and adds nothing); products are added in worker order
+          uint32_t c[KB][P];
 #pragma unroll
-          for (int e = 0; e < P; ++e)
-            acc[e] = fmaf((float)lin_of_code<GRID>(c[e], a.bits), f, acc[e]);
+          for (int u = 0; u < KB; ++u)
+            load_codes<P>(a.codes[min(k0 + u, a.K - 1)], e0, cnt, BITS, c[u]);
+#pragma unroll
+          for (int u = 0; u < KB; ++u) {
+            if (k0 + u >= a.K) break;
+            const float f =
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), k0 + u));
+#pragma unroll
+            for (int e = 0; e < P; ++e)
+              acc[e] = fmaf((float)lin_of_code<GRID>(c[u][e], BITS), f, acc[e]);
+          }
         }
         store_mean<P>(a.out, a.out_dtype, e0, cnt, acc);
       }
@@ -1587,12 +1649,17 @@ hipError_t launch_accumulate(const AccArgs &a, int grid, hipStream_t s) {
   const int64_t ntiles = (a.n + kTileMix - 1) / kTileMix;
   if (ntiles == 0) return hipSuccess;
   dim3 g(grid_for(ntiles, kGridAll));
+  const bool b8 = a.bits == 8;
   if (a.acc_bits == 16) {
-    if (grid == 0) hipLaunchKernelGGL((k_accumulate<0, 8>), g, dim3(kBlock), 0, s, a);
-    else hipLaunchKernelGGL((k_accumulate<1, 8>), g, dim3(kBlock), 0, s, a);
+    if (grid == 0 && b8) hipLaunchKernelGGL((k_accumulate<0, 8, 8>), g, dim3(kBlock), 0, s, a);
+    if (grid == 0 && !b8) hipLaunchKernelGGL((k_accumulate<0, 8, 4>), g, dim3(kBlock), 0, s, a);
+    if (grid == 1 && b8) hipLaunchKernelGGL((k_accumulate<1, 8, 8>), g, dim3(kBlock), 0, s, a);
+    if (grid == 1 && !b8) hipLaunchKernelGGL((k_accumulate<1, 8, 4>), g, dim3(kBlock), 0, s, a);
   } else {
-    if (grid == 0) hipLaunchKernelGGL((k_accumulate<0, 4>), g, dim3(kBlock), 0, s, a);
-    else hipLaunchKernelGGL((k_accumulate<1, 4>), g, dim3(kBlock), 0, s, a);
+    if (grid == 0 && b8) hipLaunchKernelGGL((k_accumulate<0, 4, 8>), g, dim3(kBlock), 0, s, a);
+    if (grid == 0 && !b8) hipLaunchKernelGGL((k_accumulate<0, 4, 4>), g, dim3(kBlock), 0, s, a);
+    if (grid == 1 && b8) hipLaunchKernelGGL((k_accumulate<1, 4, 8>), g, dim3(kBlock), 0, s, a);
+    if (grid == 1 && !b8) hipLaunchKernelGGL((k_accumulate<1, 4, 4>), g, dim3(kBlock), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -1602,9 +1669,11 @@ hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s) {
   dim3 g(grid_for(a.tv.ntiles, kGridAll));
   // 16-byte accesses on both sides: int16 -> bf16 with 8 elements per part, else 4
   if (a.acc_bits == 16 && a.out_dtype == 1)
-    hipLaunchKernelGGL(k_dequantize<8>, g, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_dequantize<8, 16>), g, dim3(kBlock), 0, s, a);
+  else if (a.acc_bits == 16)
+    hipLaunchKernelGGL((k_dequantize<4, 16>), g, dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL(k_dequantize<4>, g, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_dequantize<4, 32>), g, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1758,10 +1827,11 @@ hipError_t launch_decode_workers(const DecodeWorkersArgs &a, const float *scales
                        scales, count, levels, denom, fac);
   if (a.tv.ntiles > 0) {
     dim3 g(grid_for(a.tv.ntiles, kGridAll));
-    if (grid == 0)
-      hipLaunchKernelGGL(k_decode_workers<0>, g, dim3(kBlock), 0, s, a);
-    else
-      hipLaunchKernelGGL(k_decode_workers<1>, g, dim3(kBlock), 0, s, a);
+    const bool b8 = a.bits == 8;
+    if (grid == 0 && b8) hipLaunchKernelGGL((k_decode_workers<0, 8>), g, dim3(kBlock), 0, s, a);
+    if (grid == 0 && !b8) hipLaunchKernelGGL((k_decode_workers<0, 4>), g, dim3(kBlock), 0, s, a);
+    if (grid == 1 && b8) hipLaunchKernelGGL((k_decode_workers<1, 8>), g, dim3(kBlock), 0, s, a);
+    if (grid == 1 && !b8) hipLaunchKernelGGL((k_decode_workers<1, 4>), g, dim3(kBlock), 0, s, a);
   }
   return hipGetLastError();
 }
