@@ -261,14 +261,20 @@ def rows_resnet50(torch, gq, W, row):
         frac_of_size_ceiling=round(gbs_q / gbs_c, 4))
     ms = time_calls(torch, lambda: gq.fused_mean(g2, S2, w2.grid, w2.levels, w2.bits, 1, 16, 0,
                                                  offsets=w2.offsets, out=o2), 11)
-    row("fused_resnet50_exp7_K8", ms, w2.K * w2.n * 4 + w2.n * 4, "fused pass, 161 segments")
+    nb = w2.K * w2.n * 4 + w2.n * 4
+    gbs_f = size_ceiling(torch, g2, o2)
+    row("ceiling_read8_write1_resnet50_size", nb / (gbs_f * 1e9) * 1e3, nb,
+        "best plain stream of the fused pass's byte mix at this size (8 fp32 reads, 1 write)")
+    row("fused_resnet50_exp7_K8", ms, nb, "fused pass, 161 segments",
+        frac_of_size_ceiling=round(nb / (ms * 1e-3) / 1e9 / gbs_f, 4))
     # the literal 9-level reading {0, 2^-7 .. 2^0} (E = 8) with 8-bit codes: same kernel
     S8 = torch.empty_like(S2)
     gq.global_norm(g2, w2.offsets, scale_out=S8)
     ms = time_calls(torch, lambda: gq.fused_mean(g2, S8, w2.grid, 8, 8, 1, 16, 0,
                                                  offsets=w2.offsets, out=o2), 11)
-    row("fused_resnet50_exp8_int8_K8", ms, w2.K * w2.n * 4 + w2.n * 4,
-        "fused pass, the 9-level exponential grid in 8-bit codes")
+    row("fused_resnet50_exp8_int8_K8", ms, nb,
+        "fused pass, the 9-level exponential grid in 8-bit codes",
+        frac_of_size_ceiling=round(nb / (ms * 1e-3) / 1e9 / gbs_f, 4))
     del g2, o2, c2
     torch.cuda.empty_cache()
 
@@ -283,7 +289,12 @@ def rows_gpt2(torch, gq, W, row):
     row("norm_gpt2_bf16_K16", ms, w3.K * w3.n * 2, "K bf16 buffers in")
     ms = time_calls(torch, lambda: gq.fused_mean(g3, S3, w3.grid, w3.levels, w3.bits, 1, 16, 1,
                                                  offsets=w3.offsets, out=o3), 7)
-    row("fused_gpt2_bf16_s7_K16", ms, w3.K * w3.n * 2 + w3.n * 2, "fused pass, bf16 in and out")
+    nb = w3.K * w3.n * 2 + w3.n * 2
+    gbs_f = size_ceiling(torch, g3, o3)
+    row("ceiling_read16_write1_gpt2_size", nb / (gbs_f * 1e9) * 1e3, nb,
+        "best plain stream of the fused pass's byte mix at this size (16 bf16 reads, 1 write)")
+    row("fused_gpt2_bf16_s7_K16", ms, nb, "fused pass, bf16 in and out",
+        frac_of_size_ceiling=round(nb / (ms * 1e-3) / 1e9 / gbs_f, 4))
     wb = gq.wire_lane_bytes(w3.grid, w3.levels, w3.K)
     p3 = torch.empty(gq.wire_bytes(w3.n, w3.grid, w3.levels, w3.K), dtype=torch.uint8,
                      device="cuda")
@@ -376,12 +387,7 @@ def rows_baselines(torch, gq, W, grads, w, row, it):
     torch.cuda.empty_cache()
 
 
-def measure_ceilings(torch, grads, out):
-    """Bandwidth of plain streams (libgq_ceiling.so): K fp32 reads + 1 fp32 write (the fused
-    pass's streams), K fp32 reads (the norm pass's), and a one-read, one-write copy, each the
-    best of the kernels' lane map on 15 fixed grids and of patterns that are not the kernels'
-    own (element-wise float4 groups on a grid covering the buffers once, U = 1, 2, 4 windows;
-    one block per 2048- or 8192-element tile in XCD order)."""
+def _ceiling_lib(torch):
     import ctypes as C
     from allreduce_compatible_gradient_amd import build as B
     lib = C.CDLL(B.CEILING_LIB)
@@ -391,10 +397,60 @@ def measure_ceilings(torch, grads, out):
     lib.gqc_stream_pattern.restype = C.c_int
     lib.gqc_stream_pattern.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_void_p, C.c_void_p,
                                        C.c_int, C.c_int, C.c_void_p]
+    return lib
+
+
+def _best_stream(torch, lib, src, kk, n, o, streams):
+    """Best GB/s of kk fp32 reads of n words (+ one write to o, if given) over the kernels'
+    lane map on 15 fixed grids and the patterns that are not the kernels' own."""
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    import ctypes as C
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best, how = 0.0, ""
+    for grid in (1024, 2048, 4096, 8192, 16384):
+        for chunk in (1, 2, 4):
+            def run():
+                assert lib.gqc_stream(src, kk, n, o, sink.data_ptr(), grid, chunk, stream) == 0
+            ms = time_calls(torch, run, 3)
+            gbs = streams * (n // 2048) * 8192 / (ms * 1e-3) / 1e9
+            if gbs > best:
+                best, how = gbs, "lane map, grid %d, %d KB per wave and stream" % (grid, chunk)
+    for pattern, params in ((1, (1, 2, 4)), (2, (2048, 8192))):
+        for prm in params:
+            def run():
+                assert lib.gqc_stream_pattern(src, kk, n, o, sink.data_ptr(), pattern, prm,
+                                              stream) == 0
+            ms = time_calls(torch, run, 3)
+            gbs = streams * (n // 16384) * 65536 / (ms * 1e-3) / 1e9
+            if gbs > best:
+                best, how = gbs, ("element-wise, %d window(s)" % prm if pattern == 1
+                                  else "one block per %d-element tile, XCD order" % prm)
+    return best, how
+
+
+def size_ceiling(torch, bufs, out):
+    """Best plain stream that reads every buffer of `bufs` once and writes `out` once, at their
+    size (the buffers taken as fp32 words, so bf16 buffers give the bf16 byte mix): the ceiling
+    of a fused pass over those buffers at this size.  Returns GB/s."""
+    import ctypes as C
+    lib = _ceiling_lib(torch)
+    K = len(bufs)
+    words = bufs[0].numel() * bufs[0].element_size() // 4
+    srcs = (C.c_void_p * K)(*[b.data_ptr() for b in bufs])
+    best, _ = _best_stream(torch, lib, srcs, K, words, out.data_ptr(), K + 1)
+    return best
+
+
+def measure_ceilings(torch, grads, out):
+    """Bandwidth of plain streams (libgq_ceiling.so): K fp32 reads + 1 fp32 write (the fused
+    pass's streams), K fp32 reads (the norm pass's), and a one-read, one-write copy, each the
+    best of the kernels' lane map on 15 fixed grids and of patterns that are not the kernels'
+    own (element-wise float4 groups on a grid covering the buffers once, U = 1, 2, 4 windows;
+    one block per 2048- or 8192-element tile in XCD order)."""
+    import ctypes as C
+    lib = _ceiling_lib(torch)
     K, n = len(grads), grads[0].numel()
     srcs = (C.c_void_p * K)(*[g.data_ptr() for g in grads])
-    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
-    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
     src1 = (C.c_void_p * 1)(grads[0].data_ptr())
     res = {}
     detail = {}
@@ -402,27 +458,7 @@ def measure_ceilings(torch, grads, out):
             ("read_K%d_write1" % K, K, out.data_ptr(), K + 1),
             ("read_K%d" % K, K, None, K),
             ("copy_read1_write1", 1, out.data_ptr(), 2)):
-        best, how = 0.0, ""
-        src = srcs if kk == K else src1
-        for grid in (1024, 2048, 4096, 8192, 16384):
-            for chunk in (1, 2, 4):
-                def run():
-                    assert lib.gqc_stream(src, kk, n, o, sink.data_ptr(), grid, chunk,
-                                          stream) == 0
-                ms = time_calls(torch, run, 3)
-                gbs = streams * (n // 2048) * 8192 / (ms * 1e-3) / 1e9
-                if gbs > best:
-                    best, how = gbs, "lane map, grid %d, %d KB per wave and stream" % (grid, chunk)
-        for pattern, params in ((1, (1, 2, 4)), (2, (2048, 8192))):
-            for prm in params:
-                def run():
-                    assert lib.gqc_stream_pattern(src, kk, n, o, sink.data_ptr(), pattern, prm,
-                                                  stream) == 0
-                ms = time_calls(torch, run, 3)
-                gbs = streams * (n // 16384) * 65536 / (ms * 1e-3) / 1e9
-                if gbs > best:
-                    best, how = gbs, ("element-wise, %d window(s)" % prm if pattern == 1
-                                      else "one block per %d-element tile, XCD order" % prm)
+        best, how = _best_stream(torch, lib, srcs if kk == K else src1, kk, n, o, streams)
         res[name] = round(best, 1)
         detail[name] = how
         log("ceiling %-22s %8.1f GB/s (%.1f%% of HBM): %s"
