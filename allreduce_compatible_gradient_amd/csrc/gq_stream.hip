@@ -636,7 +636,7 @@ __global__ __launch_bounds__(kBlock) void k_norm_finish(NormArgs a) {
 // threshold) has levels 0 and +-1 only, and it rounds up when fp32(h) < fl(|x| * inv) * 2^32
 // (uniform) or fl(|x| * inv) * 2^(E+31) (exponential): bit for bit the general path's codes
 // without its clamp, floor, fraction and exponent split.
-template <int DT, int GRID>
+template <int DT, int GRID, bool AL>
 __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
   constexpr int P = DT == 0 ? 4 : 8;
   constexpr int NP = kChunk / (64 * P);
@@ -662,13 +662,16 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
     auto quant_part = [&](int64_t e0, int cnt, const float (&x)[P]) {
       uint32_t c[P];
       const uint32_t ctr = a.index_base + (uint32_t)e0;
+      // AL (index_base a multiple of 8, e0 one of P): ctr + e, e < P, only fills ctr's zero
+      // low bits, so it is ctr ^ e with the same upper half and mix16(ctr + e) = mix16(ctr) ^ e
+      const uint32_t m0 = mix16(ctr) ^ a.key_mix;
       float big = 0.0f;
 #pragma unroll
       for (int e = 0; e < P; ++e) big = max_abs(big, x[e]);
       if (__all(big < fast_below)) {
 #pragma unroll
         for (int e = 0; e < P; ++e) {
-          const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+          const uint32_t h = fmix32_tail(AL ? m0 ^ (uint32_t)e : mix16(ctr + e) ^ a.key_mix);
           const uint32_t up = (float)h < fabsf(x[e]) * q.inv * up_scale ? 1u : 0u;
           if constexpr (GRID == 0)
             c[e] = (sign_bit(x[e]) ? (0u - up) : up) & ((1u << a.bits) - 1u);
@@ -678,7 +681,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
       } else {
 #pragma unroll
         for (int e = 0; e < P; ++e) {
-          const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+          const uint32_t h = fmix32_tail(AL ? m0 ^ (uint32_t)e : mix16(ctr + e) ^ a.key_mix);
           if constexpr (GRID == 0)
             c[e] = uniform_code(quant_uniform_mag(x[e], q.inv, sf, h), x[e], a.bits);
           else
@@ -930,7 +933,7 @@ __device__ __forceinline__ void load_lanes(const uint8_t *payload, int64_t e0, i
 }
 
 // One worker's quantisation (identical to k_quantize_pack) written as wire lanes.
-template <int DT, int GRID, int WB>
+template <int DT, int GRID, int WB, bool AL>
 __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
   constexpr int P = DT == 0 ? 4 : 8;
   constexpr int NP = kChunk / (64 * P);
@@ -962,13 +965,16 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
     auto wire_part = [&](int64_t e0, int cnt, const float (&x)[P]) {
       uint32_t v[P];
       const uint32_t ctr = a.index_base + (uint32_t)e0;
+      // AL (index_base a multiple of 8, e0 one of P): ctr + e, e < P, only fills ctr's zero
+      // low bits, so it is ctr ^ e with the same upper half and mix16(ctr + e) = mix16(ctr) ^ e
+      const uint32_t m0 = mix16(ctr) ^ a.key_mix;
       float big = 0.0f;
 #pragma unroll
       for (int e = 0; e < P; ++e) big = max_abs(big, x[e]);
       if (__all(big < fast_below)) {
 #pragma unroll
         for (int e = 0; e < P; ++e) {
-          const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+          const uint32_t h = fmix32_tail(AL ? m0 ^ (uint32_t)e : mix16(ctr + e) ^ a.key_mix);
           const float up = DT == 1 ? fabsf(x[e]) * inv_up : fabsf(x[e]) * q.inv * up_scale;
           const int32_t lin = (float)h < up ? (x[e] < 0.0f ? -1 : 1) : 0;
           v[e] = (uint32_t)(lin + a.offset);
@@ -976,7 +982,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
       } else {
 #pragma unroll
         for (int e = 0; e < P; ++e) {
-          const uint32_t h = fmix32_tail(mix16(ctr + e) ^ a.key_mix);
+          const uint32_t h = fmix32_tail(AL ? m0 ^ (uint32_t)e : mix16(ctr + e) ^ a.key_mix);
           int32_t lin;
           if constexpr (GRID == 0)
             lin = (int32_t)copysignf(quant_uniform_mag(x[e], q.inv, sf, h), x[e]);
@@ -1635,13 +1641,26 @@ hipError_t launch_global_norm(const NormArgs &a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool AL>
+static void launch_qp(const QuantArgs &a, int dtype, int grid, dim3 g, hipStream_t s) {
+  if (dtype == 0 && grid == 0)
+    hipLaunchKernelGGL((k_quantize_pack<0, 0, AL>), g, dim3(kBlock), 0, s, a);
+  if (dtype == 0 && grid == 1)
+    hipLaunchKernelGGL((k_quantize_pack<0, 1, AL>), g, dim3(kBlock), 0, s, a);
+  if (dtype == 1 && grid == 0)
+    hipLaunchKernelGGL((k_quantize_pack<1, 0, AL>), g, dim3(kBlock), 0, s, a);
+  if (dtype == 1 && grid == 1)
+    hipLaunchKernelGGL((k_quantize_pack<1, 1, AL>), g, dim3(kBlock), 0, s, a);
+}
+
 hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, hipStream_t s) {
   if (a.tv.ntiles == 0) return hipSuccess;
   dim3 g(grid_for(a.tv.ntiles, kGridAll));
-  if (dtype == 0 && grid == 0) hipLaunchKernelGGL((k_quantize_pack<0, 0>), g, dim3(kBlock), 0, s, a);
-  if (dtype == 0 && grid == 1) hipLaunchKernelGGL((k_quantize_pack<0, 1>), g, dim3(kBlock), 0, s, a);
-  if (dtype == 1 && grid == 0) hipLaunchKernelGGL((k_quantize_pack<1, 0>), g, dim3(kBlock), 0, s, a);
-  if (dtype == 1 && grid == 1) hipLaunchKernelGGL((k_quantize_pack<1, 1>), g, dim3(kBlock), 0, s, a);
+  // counters that start on a multiple of 8 are mixed once per part
+  if ((a.index_base & 7u) == 0)
+    launch_qp<true>(a, dtype, grid, g, s);
+  else
+    launch_qp<false>(a, dtype, grid, g, s);
   return hipGetLastError();
 }
 
@@ -1677,11 +1696,20 @@ hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DT, int GRID, bool AL>
+static void launch_qw(const WireQuantArgs &a, int wb, dim3 g, hipStream_t s) {
+  if (wb == 1) hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 1, AL>), g, dim3(kBlock), 0, s, a);
+  if (wb == 2) hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 2, AL>), g, dim3(kBlock), 0, s, a);
+  if (wb == 4) hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 4, AL>), g, dim3(kBlock), 0, s, a);
+}
+
 template <int DT, int GRID>
 static void launch_qw(const WireQuantArgs &a, int wb, dim3 g, hipStream_t s) {
-  if (wb == 1) hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 1>), g, dim3(kBlock), 0, s, a);
-  if (wb == 2) hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 2>), g, dim3(kBlock), 0, s, a);
-  if (wb == 4) hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 4>), g, dim3(kBlock), 0, s, a);
+  // counters that start on a multiple of 8 are mixed once per part
+  if ((a.index_base & 7u) == 0)
+    launch_qw<DT, GRID, true>(a, wb, g, s);
+  else
+    launch_qw<DT, GRID, false>(a, wb, g, s);
 }
 
 hipError_t launch_quantize_wire(const WireQuantArgs &a, int dtype, int grid, int wb,

@@ -1,6 +1,8 @@
 """GPU edge cases and host-side argument checks of the Global-QSGD entry points: empty and
 ragged inputs, tiny segments, zero and non-finite segments, one-hot inputs at the scale, the
 zero draw, the generic-K path, maximum K, and every error code the host checks return."""
+import itertools
+
 import numpy as np
 import pytest
 import torch
@@ -132,6 +134,40 @@ def test_zero_and_nonfinite_segments_over_full_tiles(orc, dt, grid, levels, bits
         assert np.array_equal(got, ref["codes"][k]), first_diff(got, ref["codes"][k])
         lo, hi = off[1] * bits // 8, off[3] * bits // 8
         assert not np.any(got[lo:hi])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("base", [0, 8, 5, 4096003, "top8"])
+def test_index_base_alignment(orc, dt, base):
+    """The one-worker quantisers mix a part's counters once when index_base is a multiple of 8
+    and element by element otherwise: codes and wire payloads equal the oracle's on both
+    paths, over several full tiles and a ragged tail, on both grids."""
+    g = gq()
+    tile = 8192 if dt == "f32" else 16384
+    n = 2 * tile + 1003
+    if base == "top8":
+        base = (2 ** 32 - n) // 8 * 8
+    say("index base", dt, base)
+    rng = np.random.default_rng(int(base) % 1000 + (dt == "bf16"))
+    x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 0, n)).astype(np.float32)
+    if dt == "bf16":
+        x = (x.view(np.uint32) >> 16).astype(np.uint16)
+    xd = dev(x)
+    xf = x if dt == "f32" else (x.astype(np.uint32) << 16).view(np.float32)
+    # the largest magnitude (levels across the range: the general path) and the L2 norm (small
+    # levels: the fast path)
+    scales = (np.max(np.abs(xf)), np.sqrt(np.sum(xf.astype(np.float64) ** 2)))
+    for (grid, levels, bits, world), S in itertools.product(((U, 7, 4, 16), (X, 7, 4, 8),
+                                                             (U, 127, 8, 8)), scales):
+        Sv = np.array([S], np.float32)
+        q = orc.quantize(x, Sv, grid, levels, 11, 2, index_base=base)
+        codes = g.quantize_pack(xd, dev(Sv), grid, levels, bits, 11, 2, index_base=base)
+        ref = orc.pack(q, grid, bits)
+        assert np.array_equal(host(codes), ref), first_diff(host(codes), ref)
+        pay = g.quantize_wire(xd, dev(Sv), grid, levels, 11, 2, world, index_base=base)
+        ref = orc.wire_encode(q, grid, levels, world)
+        assert np.array_equal(host(pay), ref), first_diff(host(pay), ref)
+        assert np.any(q != 0)
 
 
 def test_one_hot_at_scale_hits_top_level(orc):
