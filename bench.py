@@ -306,9 +306,47 @@ def rows_gpt2(torch, gq, W, row):
     torch.cuda.empty_cache()
 
 
+def lq_three_stream_floor(torch, G, E):
+    """The LQ-SGD step's three passes as plain streams, timed together as one call so that the
+    middle one reads M from the Infinity Cache as the column pass does: G and E read and M
+    written; M read; M read and E written.  Best of the ceiling probe's patterns.  Returns ms."""
+    import ctypes as C
+    lib = _ceiling_lib(torch)
+    words = G.numel()
+    M = torch.empty_like(G)
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ge = (C.c_void_p * 2)(G.data_ptr(), E.data_ptr())
+    mm = (C.c_void_p * 1)(M.data_ptr())
+    shapes = [("pattern", 1, u) for u in (1, 2, 4)] + [("pattern", 2, t) for t in (2048, 8192)] \
+        + [("grid", gr, q) for gr, q in ((1024, 4), (2048, 4), (4096, 2))]
+    best = float("inf")
+    for kind, a, b in shapes:
+        def one(src, k, out):
+            if kind == "pattern":
+                assert lib.gqc_stream_pattern(src, k, words, out, sink.data_ptr(), a, b,
+                                              stream) == 0
+            else:
+                assert lib.gqc_stream(src, k, words, out, sink.data_ptr(), a, b, stream) == 0
+
+        def run():
+            one(ge, 2, M.data_ptr())
+            one(mm, 1, None)
+            one(mm, 1, E.data_ptr())
+        best = min(best, time_calls(torch, run, 5))
+    del M
+    return best
+
+
 def rows_lq(torch, gq, W, shape, row):
     """One LQ-SGD step at ranks 1, 4 and 7."""
     n5, m5 = shape
+    G, _ = W.lq_problem(n5, m5, 1, 0, "cuda")
+    E = torch.zeros_like(G)
+    floor_ms = lq_three_stream_floor(torch, G, E)
+    row("ceiling_three_streams_lq_%dx%d" % (n5, m5), floor_ms, 6 * n5 * m5 * 4,
+        "the step's three passes as plain streams (G, E -> M; M; M -> E), back to back")
+    del G, E
     for r5 in W.LQ_RANKS:
         G, Q0 = W.lq_problem(n5, m5, r5, 0, "cuda")
         E = torch.zeros_like(G)
@@ -318,7 +356,8 @@ def rows_lq(torch, gq, W, shape, row):
         ms = time_calls(torch, lambda: gq.powersgd_logquant(G, E, Q, W.LQ_ALPHA, W.LQ_BITS,
                                                             out=o5), 11)
         row("lq_step_%dx%d_r%d" % (n5, m5, r5), ms, 6 * n5 * m5 * 4,
-            "G read, E read+write, E read, E read+write")
+            "G read, E read+write, E read, E read+write",
+            frac_of_size_ceiling=round(floor_ms / ms, 4))
         del G, E, Q
 
 
