@@ -662,8 +662,8 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
     auto quant_part = [&](int64_t e0, int cnt, const float (&x)[P]) {
       uint32_t c[P];
       const uint32_t ctr = a.index_base + (uint32_t)e0;
-      // AL (index_base a multiple of 8, e0 one of P): ctr + e, e < P, only fills ctr's zero
-      // low bits, so it is ctr ^ e with the same upper half and mix16(ctr + e) = mix16(ctr) ^ e
+      // AL (index_base a multiple of 8, e0 a multiple of P): ctr + e, e < P, only fills ctr's
+      // zero low bits, so it is ctr ^ e with the same upper half: mix16(ctr + e) = mix16(ctr) ^ e
       const uint32_t m0 = mix16(ctr) ^ a.key_mix;
       float big = 0.0f;
 #pragma unroll
@@ -965,8 +965,8 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
     auto wire_part = [&](int64_t e0, int cnt, const float (&x)[P]) {
       uint32_t v[P];
       const uint32_t ctr = a.index_base + (uint32_t)e0;
-      // AL (index_base a multiple of 8, e0 one of P): ctr + e, e < P, only fills ctr's zero
-      // low bits, so it is ctr ^ e with the same upper half and mix16(ctr + e) = mix16(ctr) ^ e
+      // AL (index_base a multiple of 8, e0 a multiple of P): ctr + e, e < P, only fills ctr's
+      // zero low bits, so it is ctr ^ e with the same upper half: mix16(ctr + e) = mix16(ctr) ^ e
       const uint32_t m0 = mix16(ctr) ^ a.key_mix;
       float big = 0.0f;
 #pragma unroll
