@@ -154,6 +154,60 @@ def test_full_size_norm_and_fused_sampled(orc, name):
     torch.cuda.empty_cache()
 
 
+# expected E[x^2] per element of the workloads' distributions (their generator's recipe), for
+# the scales the wire test below chooses itself
+_SECOND_MOMENT = {"normal-outliers": 1e-6 * (0.99 + 0.01 * 1e4), "t3": 1e-6 * 3.0}
+
+
+@pytest.mark.parametrize("name", ["gpt2s-148t-bf16-K16-uniform7", "flat-1.3G-f32-K8-uniform127"])
+def test_full_size_wire_sampled(orc, name):
+    """The summable wire payload at full size, in the launch configuration bench.py times: every
+    worker's gq_quantize_wire over its whole buffer, with a scale per segment chosen here from
+    the distribution's expected second moment (an input both sides take), the payloads added
+    word by word as a uint32 Allreduce-SUM adds them, and gq_dequantize_wire of the sum.  On
+    the sampled runs, the first and last workers' payload bytes and the decoded mean equal the
+    oracle's bit for bit."""
+    w = W.get(name)
+    g = gq()
+    lens = np.diff(w.offsets).astype(np.float64)
+    S = np.sqrt(lens * _SECOND_MOMENT[w.dist]).astype(np.float32)
+    wb = g.wire_lane_bytes(w.grid, w.levels, w.K)
+    say("full-size wire", name, "K", w.K, "lane bytes", wb)
+    xs = W.gradients(w, "cuda")
+    Sd = torch.from_numpy(S).to("cuda")
+    acc = None
+    pays = {}
+    for k in range(w.K):
+        p = g.quantize_wire(xs[k], Sd, w.grid, w.levels, SEED, k, w.K, 0, w.offsets)
+        words = p.view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+        acc = words if acc is None else acc + words
+        if k in (0, w.K - 1):
+            pays[k] = p
+        del p, words
+    acc &= 0xFFFFFFFF
+    summed = torch.where(acc >= 2 ** 31, acc - 2 ** 32, acc).to(torch.int32).view(torch.uint8)
+    del acc
+    out_dtype = 1 if w.out_dtype == "bf16" else 0
+    out = g.dequantize_wire(summed, w.n, Sd, w.grid, w.levels, w.K, out_dtype, w.offsets)
+    torch.cuda.synchronize()
+    say("full-size wire: kernels done", name)
+    for a, b, seg in _runs(w):
+        xs_run = [W.to_numpy(x[a:b]) for x in xs]
+        for k, p in pays.items():
+            q = orc.quantize(xs_run[k], S[seg:seg + 1], w.grid, w.levels, SEED, k, index_base=a)
+            want = orc.wire_encode(q, w.grid, w.levels, w.K)[:(b - a) * wb]
+            got = host(p[a * wb:b * wb])
+            assert np.array_equal(got, want), "worker %d run [%d, %d): %s" % (
+                k, a, b, first_diff(got, want))
+        ref = orc.allreduce_mean(xs_run, w.grid, w.levels, w.bits, w.acc_bits, SEED,
+                                 index_base=a, out_dtype=out_dtype, scale=S[seg:seg + 1])
+        got = host(out[a:b])
+        assert np.array_equal(got, ref["mean"]), "run [%d, %d) seg %d: %s" % (
+            a, b, seg, first_diff(got, ref["mean"]))
+    del xs, pays, summed, out
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype,grid,levels,bits,acc_bits,K,n", [
     ("f32", 0, 127, 8, 16, 2, (1 << 31) + 3 * TILE + 5),
     ("bf16", 0, 7, 4, 16, 2, (1 << 31) + 3 * TILE + 5),
