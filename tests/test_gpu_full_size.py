@@ -115,8 +115,13 @@ def test_full_size_norm_and_fused_sampled(orc, name):
     scale = torch.from_numpy(S_ref).to("cuda")
     out = g.fused_mean(xs, scale, w.grid, w.levels, w.bits, SEED, w.acc_bits, out_dtype,
                        offsets=w.offsets)
+    # the same step unfused: every worker's codes, their integer sum, the decode
+    codes = [g.quantize_pack(xs[k], scale, w.grid, w.levels, w.bits, SEED, k, 0, w.offsets)
+             for k in range(w.K)]
+    sums = g.accumulate_codes(codes, w.n, w.grid, w.levels, w.bits, w.acc_bits)
+    mean2 = g.dequantize(sums, scale, w.grid, w.levels, w.K, out_dtype, w.offsets)
     torch.cuda.synchronize()
-    say("fused done", name)
+    say("fused and unfused steps done", name)
 
     runs = _runs(w)
     assert len(runs) >= 20
@@ -124,10 +129,19 @@ def test_full_size_norm_and_fused_sampled(orc, name):
         xs_run = [W.to_numpy(x[a:b]) for x in xs]
         ref = orc.allreduce_mean(xs_run, w.grid, w.levels, w.bits, w.acc_bits, SEED,
                                  index_base=a, out_dtype=out_dtype, scale=S_ref[seg:seg + 1])
-        got = host(out[a:b])
-        assert np.array_equal(got, ref["mean"]), "run [%d, %d) seg %d: %s" % (
-            a, b, seg, first_diff(got, ref["mean"]))
-    del out
+        for what, o in (("fused", out), ("unfused", mean2)):
+            got = host(o[a:b])
+            assert np.array_equal(got, ref["mean"]), "%s run [%d, %d) seg %d: %s" % (
+                what, a, b, seg, first_diff(got, ref["mean"]))
+        got = host(sums[a:b])
+        assert np.array_equal(got, ref["sums"]), "sums run [%d, %d): %s" % (
+            a, b, first_diff(got, ref["sums"]))
+        if w.bits == 8 or (a % 2 == 0 and (b - a) % 2 == 0):
+            cb = (lambda i: i) if w.bits == 8 else (lambda i: i // 2)
+            got = host(codes[0][cb(a):cb(b)])
+            assert np.array_equal(got, ref["codes"][0]), "codes run [%d, %d): %s" % (
+                a, b, first_diff(got, ref["codes"][0]))
+    del out, codes, sums, mean2
 
     # the per-worker-scale baseline on the same buffers: each worker's own L2 scale (the
     # oracle's norms rounded once to fp32), the one-pass mean and the receiver's decode of
