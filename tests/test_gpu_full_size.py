@@ -120,6 +120,11 @@ def test_full_size_norm_and_fused_sampled(orc, name):
              for k in range(w.K)]
     sums = g.accumulate_codes(codes, w.n, w.grid, w.levels, w.bits, w.acc_bits)
     mean2 = g.dequantize(sums, scale, w.grid, w.levels, w.K, out_dtype, w.offsets)
+    # the exponential workload also runs the literal 9-level grid (E = 8, 8-bit codes), as timed
+    out8 = None
+    if w.grid == W.EXP:
+        out8 = g.fused_mean(xs, scale, w.grid, w.levels + 1, 8, SEED, w.acc_bits, out_dtype,
+                            offsets=w.offsets)
     torch.cuda.synchronize()
     say("fused and unfused steps done", name)
 
@@ -136,12 +141,19 @@ def test_full_size_norm_and_fused_sampled(orc, name):
         got = host(sums[a:b])
         assert np.array_equal(got, ref["sums"]), "sums run [%d, %d): %s" % (
             a, b, first_diff(got, ref["sums"]))
+        if out8 is not None:
+            ref8 = orc.allreduce_mean(xs_run, w.grid, w.levels + 1, 8, w.acc_bits, SEED,
+                                      index_base=a, out_dtype=out_dtype,
+                                      scale=S_ref[seg:seg + 1])
+            got = host(out8[a:b])
+            assert np.array_equal(got, ref8["mean"]), "E+1 run [%d, %d): %s" % (
+                a, b, first_diff(got, ref8["mean"]))
         if w.bits == 8 or (a % 2 == 0 and (b - a) % 2 == 0):
             cb = (lambda i: i) if w.bits == 8 else (lambda i: i // 2)
             got = host(codes[0][cb(a):cb(b)])
             assert np.array_equal(got, ref["codes"][0]), "codes run [%d, %d): %s" % (
                 a, b, first_diff(got, ref["codes"][0]))
-    del out, codes, sums, mean2
+    del out, out8, codes, sums, mean2
 
     # the per-worker-scale baseline on the same buffers: each worker's own L2 scale (the
     # oracle's norms rounded once to fp32), the one-pass mean and the receiver's decode of
