@@ -1565,10 +1565,12 @@ void k_worker_mean(WorkerMeanArgs a) {
 
 // The receiver's side after an allgather of per-worker-scaled codes: each worker's packed
 // codes decoded with its own factor (lane k of `fl`), accumulated by fused multiply-add in
-// worker order.  P = 8 elements per part: 8 (8-bit) or 4 (4-bit) code bytes per worker.
-template <int GRID, int BITS>
+// worker order.  P elements per part: 8 for bf16 output, 4 for fp32, so that every store
+// instruction of a wave writes one contiguous 1 KB block (with 8 fp32 per lane, each 16-byte
+// store would cover only every other 16 bytes of the wave's span, and the half-written lines
+// reach memory as partial writes).
+template <int GRID, int BITS, int P>
 __global__ __launch_bounds__(kBlock) void k_decode_workers(DecodeWorkersArgs a) {
-  constexpr int P = 8;
   constexpr int NP = kChunk / (64 * P);
   constexpr int KB = 4;  // workers whose code loads are issued together
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -1843,6 +1845,15 @@ hipError_t launch_worker_mean(const WorkerMeanArgs &a, const float *scales, int 
   return hipGetLastError();
 }
 
+template <int P>
+static void launch_dw(const DecodeWorkersArgs &a, int grid, dim3 g, hipStream_t s) {
+  const bool b8 = a.bits == 8;
+  if (grid == 0 && b8) hipLaunchKernelGGL((k_decode_workers<0, 8, P>), g, dim3(kBlock), 0, s, a);
+  if (grid == 0 && !b8) hipLaunchKernelGGL((k_decode_workers<0, 4, P>), g, dim3(kBlock), 0, s, a);
+  if (grid == 1 && b8) hipLaunchKernelGGL((k_decode_workers<1, 8, P>), g, dim3(kBlock), 0, s, a);
+  if (grid == 1 && !b8) hipLaunchKernelGGL((k_decode_workers<1, 4, P>), g, dim3(kBlock), 0, s, a);
+}
+
 hipError_t launch_decode_workers(const DecodeWorkersArgs &a, const float *scales, int grid,
                                  int levels, double denom, hipStream_t s) {
   const int64_t count = (int64_t)a.K * a.tv.nseg;
@@ -1855,11 +1866,10 @@ hipError_t launch_decode_workers(const DecodeWorkersArgs &a, const float *scales
                        scales, count, levels, denom, fac);
   if (a.tv.ntiles > 0) {
     dim3 g(grid_for(a.tv.ntiles, kGridAll));
-    const bool b8 = a.bits == 8;
-    if (grid == 0 && b8) hipLaunchKernelGGL((k_decode_workers<0, 8>), g, dim3(kBlock), 0, s, a);
-    if (grid == 0 && !b8) hipLaunchKernelGGL((k_decode_workers<0, 4>), g, dim3(kBlock), 0, s, a);
-    if (grid == 1 && b8) hipLaunchKernelGGL((k_decode_workers<1, 8>), g, dim3(kBlock), 0, s, a);
-    if (grid == 1 && !b8) hipLaunchKernelGGL((k_decode_workers<1, 4>), g, dim3(kBlock), 0, s, a);
+    if (a.out_dtype == 1)
+      launch_dw<8>(a, grid, g, s);
+    else
+      launch_dw<4>(a, grid, g, s);
   }
   return hipGetLastError();
 }
