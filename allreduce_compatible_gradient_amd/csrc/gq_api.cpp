@@ -130,6 +130,20 @@ gq_status check_segments(gq_ctx *c, int64_t n, const int64_t *offsets, int32_t n
   return GQ_OK;
 }
 
+// Whether every wave store of a quantiser's output lands on whole 128-byte lines: a wave
+// stores 64 lanes' parts of P >= 4 elements (at least 128 bytes) at a multiple of its own size
+// from a tile's start, and tiles start at segment starts plus multiples of the tile, so it does
+// when the output's base and each segment's first byte (offsets[g] elements of bits_per_elem
+// bits) sit on line boundaries.
+static bool stores_on_lines(const void *out, const int64_t *offsets, int32_t nseg,
+                            int bits_per_elem) {
+  if ((reinterpret_cast<uintptr_t>(out) & 127) != 0) return false;
+  if (offsets != nullptr)
+    for (int32_t g = 0; g < nseg; ++g)
+      if (((offsets[g] * bits_per_elem) & 1023) != 0) return false;
+  return true;
+}
+
 // Validate the segment description and build the tile view (cached per layout).
 gq_status resolve_segments(gq_ctx *c, int64_t n, const int64_t *offsets, int32_t nseg,
                            hipStream_t s, TileView *tv, int tile = gq::kTile) {
@@ -511,7 +525,8 @@ GQ_EXPORT gq_status gq_quantize_pack(gq_ctx *c, const void *grad, int32_t dtype,
   a.bits = bits;
   a.key_mix = key_mix(worker_key(seed, worker));
   a.index_base = index_base;
-  hipError_t e = gq::launch_quantize_pack(a, dtype, grid, s);
+  hipError_t e = gq::launch_quantize_pack(a, dtype, grid,
+                                         stores_on_lines(codes, offsets, nseg, bits), s);
   return e == hipSuccess ? GQ_OK : hip_fail(c, e, "quantize launch");
 }
 
@@ -616,7 +631,8 @@ GQ_EXPORT gq_status gq_quantize_wire(gq_ctx *c, const void *grad, int32_t dtype,
   a.offset = (int32_t)wire_offset(grid, levels);
   a.key_mix = key_mix(worker_key(seed, worker));
   a.index_base = index_base;
-  hipError_t e = gq::launch_quantize_wire(a, dtype, grid, wb, s);
+  hipError_t e = gq::launch_quantize_wire(
+      a, dtype, grid, wb, stores_on_lines(payload, offsets, nseg, 8 * wb), s);
   return e == hipSuccess ? GQ_OK : hip_fail(c, e, "quantize_wire launch");
 }
 

@@ -180,11 +180,14 @@ struct DecodeWorkersArgs {
 
 // Kernel launchers (gq_stream.hip).  Each returns the launch error, if any.
 hipError_t launch_global_norm(const NormArgs &a, int dtype, hipStream_t s);
-hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, hipStream_t s);
+// nt: every wave store of the output lands on whole 128-byte lines (stores_on_lines), so the
+// quantisers store non-temporally; otherwise they store through L2.
+hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, bool nt,
+                                hipStream_t s);
 hipError_t launch_accumulate(const AccArgs &a, int grid, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
 hipError_t launch_fused(const FusedArgs &a, int dtype, int grid, hipStream_t s);
-hipError_t launch_quantize_wire(const WireQuantArgs &a, int dtype, int grid, int wb,
+hipError_t launch_quantize_wire(const WireQuantArgs &a, int dtype, int grid, int wb, bool nt,
                                 hipStream_t s);
 hipError_t launch_dequantize_wire(const WireDequantArgs &a, int wb, hipStream_t s);
 // Per-worker scales: a.partial holds K * ntiles fp64 sums (norm 0) or uint32 maxima (norm 1).

@@ -187,8 +187,24 @@ struct PartBuf<1, P> {
   }
 };
 
+// Store kind of the quantisers' code and lane stores (NT: non-temporal).  A non-temporal
+// store goes to HBM without waiting for the rest of its 128-byte line; where a wave's store
+// begins inside a line (segments that start off a line, as most of ResNet-50's tensors do for
+// 4-bit codes), the neighbouring wave writes the rest of each line and the two parts reach HBM
+// separately, 26% more write traffic than the codes' bytes.  Plain stores go through L2, which
+// merges the parts.  The host picks the kind per launch (whole lines: non-temporal, which
+// measured 3-5% faster there than plain stores); a run-time choice per tile inside one kernel
+// changed the kernels' code enough to cost bf16 input 3-70%.
+template <bool NT, typename T>
+__device__ __forceinline__ void put(T v, T *p) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
 // Codes: c[e] holds the code field (bits wide) of element e0 + e.
-template <int P>
+template <int P, bool NT>
 __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t e0, int cnt, int bits,
                                             const uint32_t (&c)[P]) {
   if (bits == 8) {
@@ -198,10 +214,10 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t e0, int cnt,
       w[i] = c[4 * i] | (c[4 * i + 1] << 8) | (c[4 * i + 2] << 16) | (c[4 * i + 3] << 24);
     if (cnt == P) {
       if constexpr (P == 4) {
-        __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t *>(codes + e0));
+        put<NT>(w[0], reinterpret_cast<uint32_t *>(codes + e0));
       } else {
         u32x2 v = {w[0], w[1]};
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(codes + e0));
+        put<NT>(v, reinterpret_cast<u32x2 *>(codes + e0));
       }
     } else {
       for (int e = 0; e < cnt; ++e) codes[e0 + e] = (uint8_t)c[e];
@@ -212,9 +228,9 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t e0, int cnt,
     for (int e = 0; e < P; ++e) w |= c[e] << (4 * e);
     if (cnt == P) {
       if constexpr (P == 4)
-        __builtin_nontemporal_store((uint16_t)w, reinterpret_cast<uint16_t *>(codes + e0 / 2));
+        put<NT>((uint16_t)w, reinterpret_cast<uint16_t *>(codes + e0 / 2));
       else
-        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t *>(codes + e0 / 2));
+        put<NT>(w, reinterpret_cast<uint32_t *>(codes + e0 / 2));
     } else {
       for (int b = 0; b < (cnt + 1) / 2; ++b) codes[e0 / 2 + b] = (uint8_t)(w >> (8 * b));
     }
@@ -636,7 +652,7 @@ __global__ __launch_bounds__(kBlock) void k_norm_finish(NormArgs a) {
 // threshold) has levels 0 and +-1 only, and it rounds up when fp32(h) < fl(|x| * inv) * 2^32
 // (uniform) or fl(|x| * inv) * 2^(E+31) (exponential): bit for bit the general path's codes
 // without its clamp, floor, fraction and exponent split.
-template <int DT, int GRID, bool AL>
+template <int DT, int GRID, bool AL, bool NT>
 __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
   constexpr int P = DT == 0 ? 4 : 8;
   constexpr int NP = kChunk / (64 * P);
@@ -688,13 +704,13 @@ __global__ __launch_bounds__(kBlock) void k_quantize_pack(QuantArgs a) {
             c[e] = exp_code(quant_exp_index(x[e], q.inv, a.levels, lo_scale, h), x[e], a.bits);
         }
       }
-      store_codes<P>(a.codes, e0, cnt, a.bits, c);
+      store_codes<P, NT>(a.codes, e0, cnt, a.bits, c);
     };
     auto zero_part = [&](int64_t e0, int cnt) {
       uint32_t c[P];
 #pragma unroll
       for (int e = 0; e < P; ++e) c[e] = 0;
-      store_codes<P>(a.codes, e0, cnt, a.bits, c);
+      store_codes<P, NT>(a.codes, e0, cnt, a.bits, c);
     };
     if (len == quant_tile(DT)) {
       // a full tile: each wave issues the loads of GR chunks before it uses the first
@@ -843,7 +859,7 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(DequantArgs a) {
 // Element e travels as the unsigned lane lin_e + o of WB bytes at byte e*WB (little-endian),
 // o = s or 2^(E-1), WB wide enough that `world` payloads added as unsigned 32-bit words never
 // carry between lanes.  A part is P lanes at byte e0*WB (aligned: e0 is a multiple of P).
-template <int P, int WB>
+template <int P, int WB, bool NT>
 __device__ __forceinline__ void store_lanes(uint8_t *payload, int64_t e0, int cnt, int64_t n,
                                             const uint32_t (&v)[P]) {
   if (cnt == P) {
@@ -853,24 +869,22 @@ __device__ __forceinline__ void store_lanes(uint8_t *payload, int64_t e0, int cn
       for (int i = 0; i < P / 4; ++i)
         w[i] = v[4 * i] | (v[4 * i + 1] << 8) | (v[4 * i + 2] << 16) | (v[4 * i + 3] << 24);
       if constexpr (P == 4)
-        __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t *>(payload + e0));
+        put<NT>(w[0], reinterpret_cast<uint32_t *>(payload + e0));
       else
-        __builtin_nontemporal_store((u32x2){w[0], w[1]}, reinterpret_cast<u32x2 *>(payload + e0));
+        put<NT>((u32x2){w[0], w[1]}, reinterpret_cast<u32x2 *>(payload + e0));
     } else if constexpr (WB == 2) {
       uint32_t w[P / 2];
 #pragma unroll
       for (int i = 0; i < P / 2; ++i) w[i] = v[2 * i] | (v[2 * i + 1] << 16);
       if constexpr (P == 4)
-        __builtin_nontemporal_store((u32x2){w[0], w[1]},
-                                    reinterpret_cast<u32x2 *>(payload + 2 * e0));
+        put<NT>((u32x2){w[0], w[1]}, reinterpret_cast<u32x2 *>(payload + 2 * e0));
       else
-        __builtin_nontemporal_store((u32x4){w[0], w[1], w[2], w[3]},
-                                    reinterpret_cast<u32x4 *>(payload + 2 * e0));
+        put<NT>((u32x4){w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(payload + 2 * e0));
     } else {
 #pragma unroll
       for (int i = 0; i < P / 4; ++i)
-        __builtin_nontemporal_store((u32x4){v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]},
-                                    reinterpret_cast<u32x4 *>(payload + 4 * (e0 + 4 * i)));
+        put<NT>((u32x4){v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]},
+                reinterpret_cast<u32x4 *>(payload + 4 * (e0 + 4 * i)));
     }
   } else {
     // the buffer's last part: its lanes byte by byte, then the zero padding to 4 bytes
@@ -933,7 +947,7 @@ __device__ __forceinline__ void load_lanes(const uint8_t *payload, int64_t e0, i
 }
 
 // One worker's quantisation (identical to k_quantize_pack) written as wire lanes.
-template <int DT, int GRID, int WB, bool AL>
+template <int DT, int GRID, int WB, bool AL, bool NT>
 __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
   constexpr int P = DT == 0 ? 4 : 8;
   constexpr int NP = kChunk / (64 * P);
@@ -991,13 +1005,13 @@ __global__ __launch_bounds__(kBlock) void k_quantize_wire(WireQuantArgs a) {
           v[e] = (uint32_t)(lin + a.offset);
         }
       }
-      store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
+      store_lanes<P, WB, NT>(a.payload, e0, cnt, a.tv.n, v);
     };
     auto offset_part = [&](int64_t e0, int cnt) {
       uint32_t v[P];
 #pragma unroll
       for (int e = 0; e < P; ++e) v[e] = (uint32_t)a.offset;
-      store_lanes<P, WB>(a.payload, e0, cnt, a.tv.n, v);
+      store_lanes<P, WB, NT>(a.payload, e0, cnt, a.tv.n, v);
     };
     if (len == quant_tile(DT)) {
       // a full tile: each wave issues the loads of GR chunks before it uses the first
@@ -1212,7 +1226,7 @@ __device__ __forceinline__ void fused_compute(const FusedArgs &a, int k0, int kn
         }
       }
       if constexpr (STORE)
-        if (cnt[j] > 0) store_codes<P>(a.codes[k0 + kb], e0[j], cnt[j], a.bits, c);
+        if (cnt[j] > 0) store_codes<P, true>(a.codes[k0 + kb], e0[j], cnt[j], a.bits, c);
     }
   }
 }
@@ -1323,7 +1337,7 @@ void k_fused(FusedArgs a) {
         for (int k = 0; k < K; ++k)
 #pragma unroll
           for (int j = 0; j < NP; ++j)
-            if (cnt[j] > 0) store_codes<P>(a.codes[k], e0[j], cnt[j], a.bits, z);
+            if (cnt[j] > 0) store_codes<P, true>(a.codes[k], e0[j], cnt[j], a.bits, z);
       }
 #pragma unroll
       for (int j = 0; j < NP; ++j) {
@@ -1643,26 +1657,28 @@ hipError_t launch_global_norm(const NormArgs &a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool AL>
+template <bool AL, bool NT>
 static void launch_qp(const QuantArgs &a, int dtype, int grid, dim3 g, hipStream_t s) {
   if (dtype == 0 && grid == 0)
-    hipLaunchKernelGGL((k_quantize_pack<0, 0, AL>), g, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_quantize_pack<0, 0, AL, NT>), g, dim3(kBlock), 0, s, a);
   if (dtype == 0 && grid == 1)
-    hipLaunchKernelGGL((k_quantize_pack<0, 1, AL>), g, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_quantize_pack<0, 1, AL, NT>), g, dim3(kBlock), 0, s, a);
   if (dtype == 1 && grid == 0)
-    hipLaunchKernelGGL((k_quantize_pack<1, 0, AL>), g, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_quantize_pack<1, 0, AL, NT>), g, dim3(kBlock), 0, s, a);
   if (dtype == 1 && grid == 1)
-    hipLaunchKernelGGL((k_quantize_pack<1, 1, AL>), g, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_quantize_pack<1, 1, AL, NT>), g, dim3(kBlock), 0, s, a);
 }
 
-hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, hipStream_t s) {
+hipError_t launch_quantize_pack(const QuantArgs &a, int dtype, int grid, bool nt,
+                                hipStream_t s) {
   if (a.tv.ntiles == 0) return hipSuccess;
   dim3 g(grid_for(a.tv.ntiles, kGridAll));
   // counters that start on a multiple of 8 are mixed once per part
-  if ((a.index_base & 7u) == 0)
-    launch_qp<true>(a, dtype, grid, g, s);
-  else
-    launch_qp<false>(a, dtype, grid, g, s);
+  const bool al = (a.index_base & 7u) == 0;
+  if (al && nt) launch_qp<true, true>(a, dtype, grid, g, s);
+  if (al && !nt) launch_qp<true, false>(a, dtype, grid, g, s);
+  if (!al && nt) launch_qp<false, true>(a, dtype, grid, g, s);
+  if (!al && !nt) launch_qp<false, false>(a, dtype, grid, g, s);
   return hipGetLastError();
 }
 
@@ -1698,30 +1714,34 @@ hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DT, int GRID, bool AL>
+template <int DT, int GRID, bool AL, bool NT>
 static void launch_qw(const WireQuantArgs &a, int wb, dim3 g, hipStream_t s) {
-  if (wb == 1) hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 1, AL>), g, dim3(kBlock), 0, s, a);
-  if (wb == 2) hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 2, AL>), g, dim3(kBlock), 0, s, a);
-  if (wb == 4) hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 4, AL>), g, dim3(kBlock), 0, s, a);
+  if (wb == 1)
+    hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 1, AL, NT>), g, dim3(kBlock), 0, s, a);
+  if (wb == 2)
+    hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 2, AL, NT>), g, dim3(kBlock), 0, s, a);
+  if (wb == 4)
+    hipLaunchKernelGGL((k_quantize_wire<DT, GRID, 4, AL, NT>), g, dim3(kBlock), 0, s, a);
 }
 
 template <int DT, int GRID>
-static void launch_qw(const WireQuantArgs &a, int wb, dim3 g, hipStream_t s) {
+static void launch_qw(const WireQuantArgs &a, int wb, bool nt, dim3 g, hipStream_t s) {
   // counters that start on a multiple of 8 are mixed once per part
-  if ((a.index_base & 7u) == 0)
-    launch_qw<DT, GRID, true>(a, wb, g, s);
-  else
-    launch_qw<DT, GRID, false>(a, wb, g, s);
+  const bool al = (a.index_base & 7u) == 0;
+  if (al && nt) launch_qw<DT, GRID, true, true>(a, wb, g, s);
+  if (al && !nt) launch_qw<DT, GRID, true, false>(a, wb, g, s);
+  if (!al && nt) launch_qw<DT, GRID, false, true>(a, wb, g, s);
+  if (!al && !nt) launch_qw<DT, GRID, false, false>(a, wb, g, s);
 }
 
-hipError_t launch_quantize_wire(const WireQuantArgs &a, int dtype, int grid, int wb,
+hipError_t launch_quantize_wire(const WireQuantArgs &a, int dtype, int grid, int wb, bool nt,
                                 hipStream_t s) {
   if (a.tv.ntiles == 0) return hipSuccess;
   const dim3 g(grid_for(a.tv.ntiles, kGridAll));
-  if (dtype == 0 && grid == 0) launch_qw<0, 0>(a, wb, g, s);
-  if (dtype == 0 && grid == 1) launch_qw<0, 1>(a, wb, g, s);
-  if (dtype == 1 && grid == 0) launch_qw<1, 0>(a, wb, g, s);
-  if (dtype == 1 && grid == 1) launch_qw<1, 1>(a, wb, g, s);
+  if (dtype == 0 && grid == 0) launch_qw<0, 0>(a, wb, nt, g, s);
+  if (dtype == 0 && grid == 1) launch_qw<0, 1>(a, wb, nt, g, s);
+  if (dtype == 1 && grid == 0) launch_qw<1, 0>(a, wb, nt, g, s);
+  if (dtype == 1 && grid == 1) launch_qw<1, 1>(a, wb, nt, g, s);
   return hipGetLastError();
 }
 

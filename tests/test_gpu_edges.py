@@ -170,6 +170,51 @@ def test_index_base_alignment(orc, dt, base):
         assert np.any(q != 0)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_store_kinds_write_the_same_bytes(orc, dt):
+    """The quantisers store non-temporally when every wave store lands on whole 128-byte lines
+    (line-aligned output, segments that start on lines) and through L2 otherwise.  Outputs 16
+    bytes past a line and segments that start off a line take the second kind: codes and wire
+    payloads equal the oracle's either way, over full tiles and ragged tails, and the bytes
+    around an output are left alone."""
+    g = gq()
+    tile = 8192 if dt == "f32" else 16384
+    n = 3 * tile + 1003
+    say("store kinds", dt)
+    rng = np.random.default_rng(91 + (dt == "bf16"))
+    x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 0, n)).astype(np.float32)
+    if dt == "bf16":
+        x = (x.view(np.uint32) >> 16).astype(np.uint16)
+    xd = dev(x)
+    xf = x if dt == "f32" else (x.astype(np.uint32) << 16).view(np.float32)
+    # one segment (on lines); segments on lines for 8-bit codes only; segments off every line
+    layouts = (None, np.array([0, 2 * tile + 128, n], np.int64),
+               np.array([0, 8, tile + 72, 2 * tile + 64, n], np.int64))
+    for offsets, (grid, levels, bits, world) in itertools.product(
+            layouts, ((U, 7, 4, 16), (X, 7, 4, 8), (U, 127, 8, 300))):
+        bounds = [0, n] if offsets is None else list(offsets)
+        S = np.array([np.max(np.abs(xf[b:e])) for b, e in zip(bounds[:-1], bounds[1:])],
+                     np.float32)
+        q = orc.quantize(x, S, grid, levels, 5, 3, offsets=offsets)
+        assert np.any(q != 0)
+        want = {"codes": orc.pack(q, grid, bits), "wire": orc.wire_encode(q, grid, levels, world)}
+        for what, ref in want.items():
+            for shift in (0, 16):
+                buf = torch.full((ref.size + 256,), 0xA5, dtype=torch.uint8, device="cuda")
+                base = (-buf.data_ptr()) % 128 + shift
+                out = buf[base:base + ref.size]
+                if what == "codes":
+                    g.quantize_pack(xd, dev(S), grid, levels, bits, 5, 3, offsets=offsets,
+                                    codes=out)
+                else:
+                    g.quantize_wire(xd, dev(S), grid, levels, 5, 3, world, offsets=offsets,
+                                    payload=out)
+                got = host(buf)
+                assert np.array_equal(got[base:base + ref.size], ref), (
+                    what, shift, first_diff(got[base:base + ref.size], ref))
+                assert np.all(got[:base] == 0xA5) and np.all(got[base + ref.size:] == 0xA5)
+
+
 def test_one_hot_at_scale_hits_top_level(orc):
     say("one-hot")
     n = 1000
