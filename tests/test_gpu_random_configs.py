@@ -1,7 +1,8 @@
 """Seeded random configurations through every Global-QSGD and baseline entry point, each
 compared with the oracle: lengths (ragged, tile-crossing), segment layouts (empty and tiny
 segments), worker counts (compiled and generic paths), grids, level counts, code widths,
-accumulator widths, element and output types, seeds and counter bases drawn at random.
+accumulator widths, element and output types, seeds and counter bases drawn at random, and
+code outputs placed at random 16-byte offsets from a 128-byte line.
 Codes, sums, payloads and means must be bit-exact; the norm within 1e-6 relative."""
 import numpy as np
 import pytest
@@ -80,6 +81,19 @@ def _run(orc, i, c):
     for k in range(K):
         assert np.array_equal(host(codes[k]), ref["codes"][k]), first_diff(host(codes[k]),
                                                                           ref["codes"][k])
+    # the same codes written at a random multiple of 16 bytes past a 128-byte line (the
+    # quantiser then stores through L2 unless the shift is 0), the bytes around them untouched
+    shift = 16 * int(np.random.default_rng(i).integers(0, 8))
+    for k in range(K):
+        nb = codes[k].numel()
+        buf = torch.full((nb + 256,), 0x5A, dtype=torch.uint8, device="cuda")
+        base = (-buf.data_ptr()) % 128 + shift
+        g.quantize_pack(xd[k], S, grid, levels, bits, c["seed"], k, c["index_base"], off,
+                        codes=buf[base:base + nb])
+        got = host(buf)
+        assert np.array_equal(got[base:base + nb], ref["codes"][k]), (
+            shift, first_diff(got[base:base + nb], ref["codes"][k]))
+        assert np.all(got[:base] == 0x5A) and np.all(got[base + nb:] == 0x5A)
     sums = g.accumulate_codes(codes, n, grid, levels, bits, c["acc_bits"])
     assert np.array_equal(host(sums), ref["sums"]), first_diff(host(sums), ref["sums"])
     mean = g.dequantize(sums, S, grid, levels, K, c["out_dtype"], off)
