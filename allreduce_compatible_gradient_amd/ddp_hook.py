@@ -16,10 +16,12 @@ Allreduce):
      exactly as the unsigned sum the payload is defined on);
   5. the decode of the mean into the bucket (gq_dequantize_wire, world = ranks).
 
-Every step of the computation runs in libgq's kernels or in the collectives; the hook only
-marshals.  A rank whose bucket norm is not finite makes the all-reduced norm infinite, and
-every rank then uses scale 0 for the bucket (all-zero codes, a zero mean), as a non-finite
-segment does in gq_global_norm.
+The norm, the quantisation and the decode run in libgq's kernels, the exchange in the
+collectives.  Between the two all-reduces the hook does the one-element bookkeeping of the
+scale with torch ops on the device: a NaN norm becomes +inf before the MAX (so that it wins,
+as an infinite one does), a non-finite maximum becomes 0, and the fp64 maximum is rounded
+once to fp32.  A rank whose bucket norm is not finite therefore makes every rank use scale 0
+for the bucket (all-zero codes, a zero mean), as a non-finite segment does in gq_global_norm.
 """
 import dataclasses
 from typing import List, Optional
