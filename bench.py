@@ -119,7 +119,7 @@ def time_calls(torch, fn, iters, warmup=1, median=True):
 
 
 ROW_GROUPS = ("flat-1M", "flat-1.3G-steps", "resnet50", "gpt2", "lq-4096x4096",
-              "lq-4096x11008", "lq-workers", "baselines")
+              "lq-4096x11008", "lq-workers", "baselines", "graphs")
 FLAT_GROUPS = ("flat-1.3G-steps", "baselines")  # groups timed on the resident 1.3e9 buffers
 
 
@@ -152,6 +152,8 @@ def rows_breakdown(torch, gq, W, grads, S, w, args, groups=ROW_GROUPS):
         rows_lq_workers(torch, gq, W, row)
     if "baselines" in groups:
         rows_baselines(torch, gq, W, grads, w, row, it)
+    if "graphs" in groups:
+        rows_graphs(torch, gq, W, row)
     torch.cuda.empty_cache()
     return rows
 
@@ -378,6 +380,55 @@ def rows_lq_workers(torch, gq, W, row):
         row("lq_workers_K%d_%dx%d_r%d" % (K, n5, m5, r5), ms, (6 * K + 1) * n5 * m5 * 4,
             "per worker: G read, E read+write, E read, E read+write; G_hat written once")
         del Gs, Es, Qs, o5
+
+
+def time_graph(torch, step, iters):
+    """The median time of replaying ``step`` captured as one HIP graph (after one eager call
+    that sizes the context's scratch), timed like time_calls; and that of the eager call."""
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    ms_graph = time_calls(torch, graph.replay, iters)
+    ms_eager = time_calls(torch, step, iters)
+    del graph
+    return ms_graph, ms_eager
+
+
+def rows_graphs(torch, gq, W, row):
+    """The launch-bound steps (several kernels of a few microseconds each) replayed as one
+    captured HIP graph, beside the same calls launched one by one: the 2^20 x 4 step and the
+    single-worker LQ-SGD step at 4096 x 4096."""
+    w1 = W.get("flat-1M-f32-K4-uniform31")
+    g1 = W.gradients(w1, "cuda")
+    n, K = w1.n, w1.K
+    ctx = gq.Context()
+    S1 = torch.empty(1, dtype=torch.float32, device="cuda")
+    o1 = torch.empty(n, dtype=torch.float32, device="cuda")
+
+    def step1():
+        gq.global_norm(g1, scale_out=S1, ctx=ctx)
+        gq.fused_mean(g1, S1, w1.grid, w1.levels, w1.bits, 1, 32, 0, out=o1, ctx=ctx)
+    ms_g, ms_e = time_graph(torch, step1, 21)
+    nb = 2 * K * n * 4 + n * 4
+    row("graph_step_1M_K4_norm_plus_fused", ms_g, nb,
+        "the whole 2^20 x 4 step replayed as a graph", eager_ms=round(ms_e, 4))
+    del g1, o1
+    n5, m5 = 4096, 4096
+    for r5 in W.LQ_RANKS:
+        G, Q0 = W.lq_problem(n5, m5, r5, 0, "cuda")
+        E = torch.zeros_like(G)
+        Q = Q0.clone()
+        lctx = gq.Context()
+        o5 = {"p_hat": torch.empty(n5, r5, dtype=torch.float32, device="cuda")}
+        o5 = gq.powersgd_logquant(G, E, Q, W.LQ_ALPHA, W.LQ_BITS, out=o5, ctx=lctx)
+        ms_g, ms_e = time_graph(torch, lambda: gq.powersgd_logquant(
+            G, E, Q, W.LQ_ALPHA, W.LQ_BITS, out=o5, ctx=lctx), 11)
+        row("graph_lq_step_%dx%d_r%d" % (n5, m5, r5), ms_g, 6 * n5 * m5 * 4,
+            "one LQ-SGD step replayed as a graph", eager_ms=round(ms_e, 4))
+        del G, E, Q, o5
 
 
 def rows_baselines(torch, gq, W, grads, w, row, it):
