@@ -22,8 +22,26 @@
  *          Q_t computed from the orthonormalised P_t); referee minor comment on
  *          Section III-A (Ghat_t is the approximate global gradient).
  *
- * Parity status of each function is given beside it; "parity unpinned" marks the parts
- * that only a second implementation of the same definition can check.
+ * Every function below is pinned to something other than itself by the CPU tests; none
+ * is parity unpinned.  Where each is pinned:
+ *   splitmix64_next, fmix32, worker_key: published known answers (tests/golden/rng_kat.json);
+ *   uniform, hash_fill: the zero draw at counter = key, the fp32 rounding of hashes built
+ *     through the inverse finaliser, uniformity and independence statistics (test_oracle_rng);
+ *   load, sumsq, norm_finish, global_norm: closed forms and exact math.fsum sums;
+ *   quant_one, quantize, quantize_list, lin: exact levels, unbiasedness, the two-point
+ *     variance, QSGD's variance bound, brute force over small inputs (test_oracle_quant);
+ *   pack, unpack_one: hand-worked byte layouts (tests/golden/pack_layout.json);
+ *   accumulate, decode_factor, dequantize, f32_to_bf16: the allreduce-compatibility identity,
+ *     exact rationals, bf16 rounding against torch;
+ *   wire_*: hand-worked lane layouts (tests/golden/wire_layout.json), no carry between lanes;
+ *   worker_scales, worker_mean, decode_workers: numpy norms and maxima, Fraction sums
+ *     (test_oracle_baselines);
+ *   logq_index, logq_level, logquant: every bin boundary against 60-digit decimal arithmetic
+ *     (test_oracle_lq);
+ *   mgs_rho, mgs, powersgd_logquant, lq_step_workers: LAPACK QR, the exact rank-one case,
+ *     error-feedback identities and telescoping (test_oracle_lq, test_oracle_lq_workers).
+ * The test_oracle_mutations suite plants one-line mistakes in a copy of this oracle and
+ * checks that these pins catch every one.
  */
 #ifndef GQ_ORACLE_H
 #define GQ_ORACLE_H
